@@ -1,0 +1,23 @@
+"""CPU oracle for the BitLinear forward pass (test infrastructure only).
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg may use
+this package; the product path never imports it.
+"""
+
+from .bitlinear_oracle import (  # noqa: F401
+    absmean_exact,
+    act_quant,
+    bf16_to_f32,
+    contract,
+    contract_loops,
+    dequant,
+    f32_to_bf16,
+    forward,
+    forward_acc,
+    pack,
+    pack_weights,
+    ternarize,
+    unpack,
+    weight_quant,
+    weight_scale,
+)
