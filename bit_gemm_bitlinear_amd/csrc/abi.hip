@@ -1,0 +1,324 @@
+// extern "C" entry points of libbitlinear.so (declared in include/bitlinear.h):
+// host-side argument validation, workspace layout and kernel dispatch.  No
+// entry point allocates, frees or synchronizes; every argument is checked
+// before anything is enqueued.
+#include "../../include/bitlinear.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+
+#include "internal.hpp"
+
+using namespace bl;
+
+namespace {
+
+constexpr int64_t kMaxK = int64_t(1) << 22;
+constexpr int64_t kMaxN = int64_t(1) << 30;
+constexpr int64_t kMaxM = int64_t(1) << 24;
+constexpr int64_t kMaxElems = int64_t(1) << 40;
+constexpr size_t kPackWorkspace = 256 * sizeof(unsigned long long);
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bl_status check_ptr(const void* p) {
+  if (!p) return BL_EINVAL;
+  if (!aligned16(p)) return BL_EALIGN;
+  return BL_OK;
+}
+
+bl_status check_shape(int64_t m, int64_t n, int64_t k) {
+  if (m < 1 || n < 1 || k < 1) return BL_ESHAPE;
+  if (k % 4 != 0 || k > kMaxK || n > kMaxN || m > kMaxM) return BL_ESHAPE;
+  if (m * k >= kMaxElems || n * (k / 4) >= kMaxElems || m * n >= kMaxElems) return BL_ESHAPE;
+  return BL_OK;
+}
+
+int load_mode_for(int64_t k) { return (k % 64 == 0) ? 0 : (k % 16 == 0) ? 1 : 2; }
+
+// Workspace layout of a forward call (shared by the size query and the call).
+struct Layout {
+  bool decode;
+  int load_mode;
+  int32_t m_pad;
+  size_t q_off[kMaxProj], xs_off[kMaxProj], qs_off[kMaxProj];
+  size_t part_off[kMaxProj], cnt_off[kMaxProj];
+  DecodePlan plan[kMaxProj];
+  size_t zero_off, zero_bytes;
+  size_t total;
+};
+
+int load_mode_for(int32_t count, const int64_t* ks) {
+  int mode = 0;
+  for (int i = 0; i < count; ++i) mode = std::max(mode, load_mode_for(ks[i]));
+  return mode;
+}
+
+void make_layout(int32_t count, const int64_t* ns, const int64_t* ks, int64_t m, Layout& L) {
+  L.decode = m <= kDecodeMaxM;
+  L.load_mode = load_mode_for(count, ks);
+  L.m_pad = L.decode ? (int32_t)m : (int32_t)round_up(m, kPrefillBM);
+  size_t off = 0;
+  for (int i = 0; i < count; ++i) {
+    const int64_t ldq = round_up(ks[i], kKPad);
+    L.q_off[i] = off;
+    off = align256(off + (size_t)L.m_pad * (size_t)ldq);
+    L.xs_off[i] = off;
+    off = align256(off + sizeof(float) * (size_t)m);
+    L.qs_off[i] = off;
+    off = align256(off + sizeof(int32_t) * (size_t)m);
+  }
+  L.zero_off = off;
+  for (int i = 0; i < count; ++i) {
+    L.part_off[i] = L.cnt_off[i] = 0;
+    if (!L.decode) continue;
+    L.plan[i] = plan_decode(m, ns[i], ks[i], L.load_mode);
+    if (L.plan[i].ksplit > 1) {
+      L.part_off[i] = off;
+      off = align256(off + sizeof(int32_t) * (size_t)(m * ns[i]));
+      L.cnt_off[i] = off;
+      off = align256(off + sizeof(uint32_t) * (size_t)L.plan[i].ngroups);
+    }
+  }
+  L.zero_bytes = off - L.zero_off;
+  L.total = off;
+}
+
+struct ProjIO {
+  const uint16_t* x;
+  const int8_t* q_in;
+  const uint8_t* packed;
+  const float* w_scale;
+  uint16_t* y;
+  int32_t* acc;
+  int64_t n, k;
+};
+
+bl_status run_forward(int32_t count, const ProjIO* io, int64_t m, void* workspace,
+                      size_t ws_bytes, hipStream_t stream) {
+  int64_t ns[kMaxProj], ks[kMaxProj];
+  for (int i = 0; i < count; ++i) {
+    ns[i] = io[i].n;
+    ks[i] = io[i].k;
+  }
+  Layout L;
+  make_layout(count, ns, ks, m, L);
+  if (!workspace) return BL_EWORKSPACE;
+  if (!aligned16(workspace)) return BL_EALIGN;
+  if (ws_bytes < L.total) return BL_EWORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+
+  const int load_mode = L.load_mode;
+
+  // 1. activation codes (+ scales, code sums), and clearing of split-K partials
+  ActQuantArgs qa = {};
+  qa.count = count;
+  int rows = 0;
+  for (int i = 0; i < count; ++i) {
+    ActQuantJob& J = qa.j[i];
+    J.x = io[i].x;
+    J.q_in = io[i].q_in;
+    J.q = reinterpret_cast<int8_t*>(ws + L.q_off[i]);
+    J.x_scale = reinterpret_cast<float*>(ws + L.xs_off[i]);
+    J.qsum = reinterpret_cast<int32_t*>(ws + L.qs_off[i]);
+    J.k = (int32_t)ks[i];
+    J.ldq = (int32_t)round_up(ks[i], kKPad);
+    J.m = (int32_t)m;
+    J.m_pad = L.m_pad;
+    J.row_begin = rows;
+    rows += L.m_pad;
+  }
+  qa.zero = reinterpret_cast<int32_t*>(ws + L.zero_off);
+  qa.zero_words = (int64_t)(L.zero_bytes / sizeof(int32_t));
+  if (launch_act_quant_internal(qa, rows, stream) != hipSuccess) return BL_EHIP;
+
+  // 2. contraction + dequantization
+  if (L.decode) {
+    DecodeArgs da = {};
+    da.count = count;
+    da.m = (int32_t)m;
+    da.load_mode = load_mode;
+    int wgs = 0, lds_row = 0;
+    size_t red = 0;
+    for (int i = 0; i < count; ++i) {
+      DecodeProj& P = da.p[i];
+      const DecodePlan& pl = L.plan[i];
+      P.packed = io[i].packed;
+      P.w_scale = io[i].w_scale;
+      P.y = io[i].y;
+      P.acc_out = io[i].acc;
+      P.q = qa.j[i].q;
+      P.x_scale = qa.j[i].x_scale;
+      P.qsum = qa.j[i].qsum;
+      P.part = pl.ksplit > 1 ? reinterpret_cast<int32_t*>(ws + L.part_off[i]) : nullptr;
+      P.count = pl.ksplit > 1 ? reinterpret_cast<uint32_t*>(ws + L.cnt_off[i]) : nullptr;
+      P.n = (int32_t)ns[i];
+      P.k = (int32_t)ks[i];
+      P.ldq = qa.j[i].ldq;
+      P.tw = pl.tw;
+      P.kspw = pl.kspw;
+      P.ksplit = pl.ksplit;
+      P.ngroups = pl.ngroups;
+      P.wg_begin = wgs;
+      wgs += pl.ngroups * pl.ksplit;
+      lds_row = std::max(lds_row, pl.kspw * 256 + 16);
+      red = std::max(red, (size_t)4 * pl.tw * m * 16 * 4);
+    }
+    da.lds_row = lds_row;
+    const size_t lds = std::max((size_t)m * lds_row, red);
+    if (launch_decode(da, wgs, lds, stream) != hipSuccess) return BL_EHIP;
+  } else {
+    PrefillArgs pa = {};
+    pa.count = count;
+    pa.m = (int32_t)m;
+    pa.tiles_m = L.m_pad / kPrefillBM;
+    pa.load_mode = load_mode;
+    int64_t tiles = 0;
+    for (int i = 0; i < count; ++i) {
+      PrefillProj& P = pa.p[i];
+      P.packed = io[i].packed;
+      P.w_scale = io[i].w_scale;
+      P.y = io[i].y;
+      P.acc_out = io[i].acc;
+      P.q = qa.j[i].q;
+      P.x_scale = qa.j[i].x_scale;
+      P.qsum = qa.j[i].qsum;
+      P.n = (int32_t)ns[i];
+      P.k = (int32_t)ks[i];
+      P.ldq = qa.j[i].ldq;
+      P.tiles_n = (int32_t)((ns[i] + kPrefillBN - 1) / kPrefillBN);
+      P.tile_begin = (int32_t)tiles;
+      tiles += (int64_t)pa.tiles_m * P.tiles_n;
+    }
+    if (tiles >= (int64_t(1) << 31)) return BL_ESHAPE;
+    if (launch_prefill(pa, (int)tiles, stream) != hipSuccess) return BL_EHIP;
+  }
+  return BL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* bitlinear_status_string(bl_status s) {
+  switch (s) {
+    case BL_OK: return "ok";
+    case BL_EINVAL: return "invalid argument (null pointer or count out of range)";
+    case BL_ESHAPE: return "unsupported shape (M, N, K >= 1, K % 4 == 0, K <= 2^22)";
+    case BL_EALIGN: return "pointer not 16-byte aligned";
+    case BL_EWORKSPACE: return "workspace missing or too small";
+    case BL_EHIP: return "HIP kernel launch failed";
+  }
+  return "unknown status";
+}
+
+int bitlinear_abi_version(void) { return 1; }
+
+size_t bitlinear_pack_workspace_bytes(int64_t n, int64_t k) {
+  (void)n;
+  (void)k;
+  return kPackWorkspace;
+}
+
+bl_status bitlinear_pack_weights(const float* w, int64_t n, int64_t k, uint8_t* packed,
+                                 float* w_scale, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  bl_status st;
+  if ((st = check_shape(1, n, k)) != BL_OK) return st;
+  if (n * k >= kMaxElems) return BL_ESHAPE;
+  if ((st = check_ptr(w)) != BL_OK || (st = check_ptr(packed)) != BL_OK) return st;
+  if ((st = check_ptr(w_scale)) != BL_OK) return st;
+  if (!workspace || workspace_bytes < kPackWorkspace) return BL_EWORKSPACE;
+  if (!aligned16(workspace)) return BL_EALIGN;
+  if (launch_pack(w, n, k, packed, w_scale, static_cast<unsigned long long*>(workspace),
+                  static_cast<hipStream_t>(stream)) != hipSuccess)
+    return BL_EHIP;
+  return BL_OK;
+}
+
+bl_status bitlinear_unpack_weights(const uint8_t* packed, int64_t n, int64_t k, int8_t* u,
+                                   void* stream) {
+  bl_status st;
+  if ((st = check_shape(1, n, k)) != BL_OK) return st;
+  if ((st = check_ptr(packed)) != BL_OK || (st = check_ptr(u)) != BL_OK) return st;
+  if (launch_unpack(packed, n, k, u, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return BL_EHIP;
+  return BL_OK;
+}
+
+bl_status bitlinear_act_quant(const uint16_t* x, int64_t m, int64_t k, int8_t* q,
+                              float* x_scale, void* stream) {
+  bl_status st;
+  if ((st = check_shape(m, 1, k)) != BL_OK) return st;
+  if ((st = check_ptr(x)) != BL_OK || (st = check_ptr(q)) != BL_OK ||
+      (st = check_ptr(x_scale)) != BL_OK)
+    return st;
+  if (launch_act_quant_public(x, m, k, q, x_scale, static_cast<hipStream_t>(stream)) !=
+      hipSuccess)
+    return BL_EHIP;
+  return BL_OK;
+}
+
+size_t bitlinear_forward_workspace_bytes(int64_t m, int64_t n, int64_t k) {
+  if (check_shape(m, n, k) != BL_OK) return 0;
+  Layout L;
+  make_layout(1, &n, &k, m, L);
+  return L.total;
+}
+
+bl_status bitlinear_forward(int64_t m, int64_t n, int64_t k, const uint16_t* x,
+                            const uint8_t* packed, const float* w_scale, uint16_t* y,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  bl_status st;
+  if ((st = check_shape(m, n, k)) != BL_OK) return st;
+  if ((st = check_ptr(x)) != BL_OK || (st = check_ptr(packed)) != BL_OK ||
+      (st = check_ptr(w_scale)) != BL_OK || (st = check_ptr(y)) != BL_OK)
+    return st;
+  ProjIO io = {x, nullptr, packed, w_scale, y, nullptr, n, k};
+  return run_forward(1, &io, m, workspace, workspace_bytes, static_cast<hipStream_t>(stream));
+}
+
+size_t bitlinear_forward_grouped_workspace_bytes(int32_t count, const bl_projection* projs,
+                                                 int64_t m) {
+  if (count < 1 || count > kMaxProj || !projs) return 0;
+  int64_t ns[kMaxProj], ks[kMaxProj];
+  for (int i = 0; i < count; ++i) {
+    if (check_shape(m, projs[i].n, projs[i].k) != BL_OK) return 0;
+    ns[i] = projs[i].n;
+    ks[i] = projs[i].k;
+  }
+  Layout L;
+  make_layout(count, ns, ks, m, L);
+  return L.total;
+}
+
+bl_status bitlinear_forward_grouped(int32_t count, const bl_projection* projs, int64_t m,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+  if (count < 1 || count > kMaxProj || !projs) return BL_EINVAL;
+  ProjIO io[kMaxProj];
+  for (int i = 0; i < count; ++i) {
+    const bl_projection& p = projs[i];
+    bl_status st;
+    if ((st = check_shape(m, p.n, p.k)) != BL_OK) return st;
+    if ((st = check_ptr(p.x)) != BL_OK || (st = check_ptr(p.packed)) != BL_OK ||
+        (st = check_ptr(p.w_scale)) != BL_OK || (st = check_ptr(p.y)) != BL_OK)
+      return st;
+    io[i] = ProjIO{p.x, nullptr, p.packed, p.w_scale, p.y, nullptr, p.n, p.k};
+  }
+  return run_forward(count, io, m, workspace, workspace_bytes, static_cast<hipStream_t>(stream));
+}
+
+bl_status bitlinear_forward_acc(int64_t m, int64_t n, int64_t k, const int8_t* q,
+                                const uint8_t* packed, int32_t* acc, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  bl_status st;
+  if ((st = check_shape(m, n, k)) != BL_OK) return st;
+  if ((st = check_ptr(q)) != BL_OK || (st = check_ptr(packed)) != BL_OK ||
+      (st = check_ptr(acc)) != BL_OK)
+    return st;
+  ProjIO io = {nullptr, q, packed, nullptr, nullptr, acc, n, k};
+  return run_forward(1, &io, m, workspace, workspace_bytes, static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,183 @@
+// Per-token activation quantization: the Falcon-Edge blog's
+// activation_norm_quant ("A series of powerful, universal and fine-tunable
+// 1.58-bit language models", section "Falcon-Edge, a series of universal
+// models"):  scale = 127 / max(max_k |x|, 1e-5);  q = clamp(round(x*scale),
+// -128, 127).  One workgroup per row: an integer max over the bf16 magnitude
+// bits (exact), then one fp32 division and one multiply + round per code.
+//
+// Two outputs: the public natural layout [M][K], and the internal layout the
+// contraction kernels read (rows padded with zero codes to a multiple of 256,
+// each group of 16 codes stored 4x4-transposed to match the weight decode in
+// common.hpp, plus the per-row code sum used to turn unsigned weight codes
+// c = u + 1 back into u: sum q*u = sum q*c - sum q).
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace bl {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t* red) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o));
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return max(max(red[0], red[1]), max(red[2], red[3]));
+}
+
+__device__ __forceinline__ int32_t block_sum_i32(int32_t v, int32_t* red) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return red[0] + red[1] + red[2] + red[3];
+}
+
+// Row absmax scale of one bf16 row of length k (k % 4 == 0).
+__device__ __forceinline__ float row_scale(const uint16_t* __restrict__ xr, int k,
+                                           uint32_t* red) {
+  const uint2* x4 = reinterpret_cast<const uint2*>(xr);
+  uint32_t a = 0;
+  for (int g = threadIdx.x; g < (k >> 2); g += kThreads) {
+    uint2 v = x4[g];
+    a = max(a, absmax_bits4(v.x, v.y));
+  }
+  a = block_max_u32(a, red);
+  return act_scale(bf16_to_f32(a));
+}
+
+// 16 codes starting at k0 (codes at k >= k are zero).
+__device__ __forceinline__ void quant16(const uint16_t* __restrict__ xr, int k, int k0, float s,
+                                        int32_t (&q)[16]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if (k0 + 4 * j < k) {
+      uint2 v = *reinterpret_cast<const uint2*>(xr + k0 + 4 * j);
+      q[4 * j + 0] = quant_i8(bf16_to_f32(v.x & 0xFFFFu), s);
+      q[4 * j + 1] = quant_i8(bf16_to_f32(v.x >> 16), s);
+      q[4 * j + 2] = quant_i8(bf16_to_f32(v.y & 0xFFFFu), s);
+      q[4 * j + 3] = quant_i8(bf16_to_f32(v.y >> 16), s);
+    } else {
+      q[4 * j + 0] = q[4 * j + 1] = q[4 * j + 2] = q[4 * j + 3] = 0;
+    }
+  }
+}
+
+__device__ __forceinline__ void load16_codes(const int8_t* __restrict__ qr, int k, int k0,
+                                             int32_t (&q)[16]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    uint32_t v = (k0 + 4 * j < k) ? *reinterpret_cast<const uint32_t*>(qr + k0 + 4 * j) : 0u;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) q[4 * j + b] = (int32_t)(int8_t)(v >> (8 * b));
+  }
+}
+
+// Internal layout of 16 codes: dword a, byte b = code 4b + a.
+__device__ __forceinline__ v4i transpose16(const int32_t (&q)[16]) {
+  v4i o;
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    uint32_t d = ((uint32_t)q[a] & 0xFFu) | (((uint32_t)q[4 + a] & 0xFFu) << 8) |
+                 (((uint32_t)q[8 + a] & 0xFFu) << 16) | (((uint32_t)q[12 + a] & 0xFFu) << 24);
+    o[a] = (int32_t)d;
+  }
+  return o;
+}
+
+__global__ __launch_bounds__(kThreads) void act_quant_public_kernel(
+    const uint16_t* __restrict__ x, int k, int8_t* __restrict__ q, float* __restrict__ x_scale) {
+  __shared__ uint32_t red[4];
+  const int64_t m = blockIdx.x;
+  const uint16_t* xr = x + m * k;
+  const float s = row_scale(xr, k, red);
+  int8_t* qr = q + m * k;
+  for (int g = threadIdx.x; g < (k + 15) / 16; g += kThreads) {
+    int32_t c[16];
+    quant16(xr, k, 16 * g, s, c);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (16 * g + 4 * j < k) {
+        uint32_t d = ((uint32_t)c[4 * j] & 0xFFu) | (((uint32_t)c[4 * j + 1] & 0xFFu) << 8) |
+                     (((uint32_t)c[4 * j + 2] & 0xFFu) << 16) |
+                     (((uint32_t)c[4 * j + 3] & 0xFFu) << 24);
+        *reinterpret_cast<uint32_t*>(qr + 16 * g + 4 * j) = d;
+      }
+    }
+  }
+  if (threadIdx.x == 0) x_scale[m] = s;
+}
+
+__global__ __launch_bounds__(kThreads) void act_quant_internal_kernel(const ActQuantArgs a) {
+  __shared__ uint32_t red[4];
+  const int b = blockIdx.x;
+  if (b >= a.zero_blocks_begin) {
+    const int64_t nzb = (int64_t)(gridDim.x - a.zero_blocks_begin);
+    for (int64_t i = (int64_t)(b - a.zero_blocks_begin) * kThreads + threadIdx.x; i < a.zero_words;
+         i += nzb * kThreads)
+      a.zero[i] = 0;
+    return;
+  }
+  int ji = 0;
+  while (ji + 1 < a.count && b >= a.j[ji + 1].row_begin) ++ji;
+  const ActQuantJob& J = a.j[ji];
+  const int m = b - J.row_begin;
+  int8_t* qr = J.q + (int64_t)m * J.ldq;
+  if (m >= J.m) {  // padding row: zero codes
+    for (int g = threadIdx.x; g < J.ldq / 16; g += kThreads)
+      reinterpret_cast<v4i*>(qr)[g] = v4i{0, 0, 0, 0};
+    return;
+  }
+  float s = 0.0f;
+  const uint16_t* xr = nullptr;
+  const int8_t* qin = nullptr;
+  if (J.x) {
+    xr = J.x + (int64_t)m * J.k;
+    s = row_scale(xr, J.k, red);
+  } else {
+    qin = J.q_in + (int64_t)m * J.k;
+  }
+  int32_t sum = 0;
+  for (int g = threadIdx.x; g < J.ldq / 16; g += kThreads) {
+    int32_t c[16];
+    if (xr)
+      quant16(xr, J.k, 16 * g, s, c);
+    else
+      load16_codes(qin, J.k, 16 * g, c);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sum += c[i];
+    reinterpret_cast<v4i*>(qr)[g] = transpose16(c);
+  }
+  sum = block_sum_i32(sum, reinterpret_cast<int32_t*>(red));
+  if (threadIdx.x == 0) {
+    J.qsum[m] = sum;
+    if (xr) J.x_scale[m] = s;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_act_quant_public(const uint16_t* x, int64_t m, int64_t k, int8_t* q,
+                                   float* x_scale, hipStream_t s) {
+  act_quant_public_kernel<<<(unsigned)m, kThreads, 0, s>>>(x, (int)k, q, x_scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_act_quant_internal(const ActQuantArgs& a, int total_rows, hipStream_t s) {
+  ActQuantArgs args = a;
+  int zero_blocks = 0;
+  if (args.zero_words > 0) {
+    int64_t per = (int64_t)kThreads * 16;
+    int64_t zb = (args.zero_words + per - 1) / per;
+    zero_blocks = (int)(zb > 1024 ? 1024 : zb);
+  }
+  args.zero_blocks_begin = total_rows;
+  act_quant_internal_kernel<<<(unsigned)(total_rows + zero_blocks), kThreads, 0, s>>>(args);
+  return hipGetLastError();
+}
+
+}  // namespace bl

@@ -1,0 +1,86 @@
+// Device helpers shared by the BitLinear kernels (gfx950).
+//
+// Formulas follow the Falcon-Edge blog ("A series of powerful, universal and
+// fine-tunable 1.58-bit language models", section "Falcon-Edge, a series of
+// universal models"): activation_norm_quant, _weight_quant and
+// BitLinear.post_quant_process.  All float arithmetic is single IEEE fp32
+// operations with round-to-nearest-even (no contraction into FMAs, correctly
+// rounded division), so results are bit-identical to a plain fp32 evaluation.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bl {
+
+typedef int32_t v4i __attribute__((ext_vector_type(4)));
+
+// fp32(1e-5): the lower clamp of the absmax / absmean denominators.
+constexpr float kEps = 1e-5f;
+
+// 2-bit codes of 16 packed weights -> 4 dwords of int8 codes (0..3).
+// Byte b of the packed dword holds weights 4b..4b+3 (2 bits each, least
+// significant first).  Output dword a, byte b, holds the code of weight
+// 4b + a: a 4x4 transpose of the natural order that costs one shift and
+// one mask per dword.  Activations are stored in the same transposed order
+// (see act_quant.hip), so the pairing of codes with activations is exact.
+__device__ __forceinline__ v4i decode16(uint32_t p) {
+  v4i r;
+  r.x = (int32_t)(p & 0x03030303u);
+  r.y = (int32_t)((p >> 2) & 0x03030303u);
+  r.z = (int32_t)((p >> 4) & 0x03030303u);
+  r.w = (int32_t)((p >> 6) & 0x03030303u);
+  return r;
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// fp32 -> bf16, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// Per-token scale from the row's absmax: 127 / max(amax, 1e-5).
+__device__ __forceinline__ float act_scale(float amax) {
+  return 127.0f / fmaxf(amax, kEps);
+}
+
+// One int8 code: clamp(round_half_even(x * s), -128, 127).
+__device__ __forceinline__ int32_t quant_i8(float x, float s) {
+  float t = rintf(x * s);
+  t = fminf(fmaxf(t, -128.0f), 127.0f);
+  return (int32_t)t;
+}
+
+// One ternary code c = u + 1 with u = clamp(round_half_even(w * s), -1, 1).
+__device__ __forceinline__ uint32_t ternary_code(float w, float s) {
+  float t = rintf(w * s);
+  t = fminf(fmaxf(t, -1.0f), 1.0f);
+  return (uint32_t)(int32_t)(t + 1.0f);
+}
+
+// Output: bf16(acc / (x_scale * w_scale)), one fp32 product, one division.
+__device__ __forceinline__ uint16_t dequant_bf16(int32_t acc, float xs, float ws) {
+  float d = xs * ws;
+  float yf = (float)acc / d;
+  return f32_to_bf16(yf);
+}
+
+// Largest magnitude pattern of four bf16 values held in two dwords; the
+// bit pattern of |x| orders like |x| for finite values.
+__device__ __forceinline__ uint32_t absmax_bits4(uint32_t lo, uint32_t hi) {
+  uint32_t a = max(lo & 0x7FFFu, (lo >> 16) & 0x7FFFu);
+  uint32_t b = max(hi & 0x7FFFu, (hi >> 16) & 0x7FFFu);
+  return max(a, b);
+}
+
+__device__ __forceinline__ v4i mfma_16x16x64_i8(v4i a, v4i b, v4i c) {
+  return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
+}
+
+}  // namespace bl

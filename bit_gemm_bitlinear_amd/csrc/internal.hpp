@@ -1,0 +1,117 @@
+// Internal launch interface between the C ABI (abi.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace bl {
+
+constexpr int kMaxProj = 16;
+
+// Decode path (M <= 16) limits.
+constexpr int kDecodeMaxM = 16;
+constexpr int kDecodeMaxTw = 8;       // 16-row tiles per WG
+// 16-byte weight chunks a lane holds in registers, by row alignment (load
+// mode 0: 16-byte rows, 1: 4-byte rows, 2: unaligned rows, byte loads).
+constexpr int decode_max_items(int mode) { return mode == 0 ? 16 : mode == 1 ? 8 : 4; }
+constexpr int kDecodeLdsA = 48 * 1024;
+
+// Activation codes for the contraction kernels are kept in an internal
+// layout: rows padded to a multiple of 256 codes (zero filled), and inside
+// every group of 16 codes the 4x4 byte transpose described in common.hpp.
+constexpr int kKPad = 256;
+
+inline int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
+inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+// ---- activation quantization (act_quant.hip) ----
+struct ActQuantJob {
+  const uint16_t* x;   // [m][k] bf16 (nullptr: take codes from q_in)
+  const int8_t* q_in;  // [m][k] int8 natural layout (used when x == nullptr)
+  int8_t* q;           // [m_pad][ldq] internal layout (written)
+  float* x_scale;      // [m] (written when x != nullptr)
+  int32_t* qsum;       // [m] row sums of the codes (written)
+  int32_t k, ldq, m, m_pad;
+  int32_t row_begin;   // first block of this job in the launch
+};
+
+struct ActQuantArgs {
+  ActQuantJob j[kMaxProj];
+  int32_t count;
+  int32_t zero_blocks_begin;  // blocks from here on only zero `zero`
+  int32_t* zero;              // region cleared by the same launch (split-K partials)
+  int64_t zero_words;         // its size in int32 words
+};
+
+hipError_t launch_act_quant_internal(const ActQuantArgs& a, int total_rows, hipStream_t s);
+hipError_t launch_act_quant_public(const uint16_t* x, int64_t m, int64_t k, int8_t* q,
+                                   float* x_scale, hipStream_t s);
+
+// ---- decode contraction (decode.hip) ----
+struct DecodeProj {
+  const uint8_t* packed;
+  const float* w_scale;
+  uint16_t* y;         // bf16 output, or nullptr
+  int32_t* acc_out;    // int32 output when y == nullptr
+  const int8_t* q;     // internal-layout codes, [16][ldq]
+  const float* x_scale;
+  const int32_t* qsum;
+  int32_t* part;       // [m][n] int32 split-K partials (zeroed beforehand)
+  uint32_t* count;     // [ngroups] split-K arrival counters (zeroed beforehand)
+  int32_t n, k, ldq;
+  int32_t tw;          // 16-row tiles per WG
+  int32_t kspw;        // K slabs (256 codes) per WG
+  int32_t ksplit;      // WGs sharing one row group along K
+  int32_t ngroups;     // row groups
+  int32_t wg_begin;    // first WG of this projection in the launch
+};
+
+struct DecodeArgs {
+  DecodeProj p[kMaxProj];
+  int32_t count;
+  int32_t m;
+  int32_t load_mode;  // 0: 16-byte rows, 1: 4-byte rows, 2: byte rows
+  int32_t lds_row;    // LDS row stride of the staged codes (bytes)
+};
+
+struct DecodePlan {
+  int32_t tw, kspw, ksplit, ngroups;
+};
+DecodePlan plan_decode(int64_t m, int64_t n, int64_t k, int mode);
+size_t decode_lds_bytes(int64_t m, const DecodePlan& p);
+hipError_t launch_decode(const DecodeArgs& a, int total_wgs, size_t lds_bytes, hipStream_t s);
+
+// ---- prefill contraction (prefill.hip) ----
+constexpr int kPrefillBM = 128;
+constexpr int kPrefillBN = 128;
+
+struct PrefillProj {
+  const uint8_t* packed;
+  const float* w_scale;
+  uint16_t* y;
+  int32_t* acc_out;
+  const int8_t* q;      // internal layout [m_pad][ldq]
+  const float* x_scale;
+  const int32_t* qsum;
+  int32_t n, k, ldq;
+  int32_t tiles_n;      // ceil(n / BN)
+  int32_t tile_begin;   // first tile of this projection in the launch
+};
+
+struct PrefillArgs {
+  PrefillProj p[kMaxProj];
+  int32_t count;
+  int32_t m;
+  int32_t tiles_m;
+  int32_t load_mode;
+};
+
+hipError_t launch_prefill(const PrefillArgs& a, int total_tiles, hipStream_t s);
+
+// ---- weight preparation (pack.hip) ----
+hipError_t launch_pack(const float* w, int64_t n, int64_t k, uint8_t* packed, float* w_scale,
+                       unsigned long long* buckets, hipStream_t s);
+hipError_t launch_unpack(const uint8_t* packed, int64_t n, int64_t k, int8_t* u, hipStream_t s);
+
+}  // namespace bl

@@ -1,0 +1,157 @@
+/*
+ * bitlinear.h -- C ABI of libbitlinear.so, the BitNet b1.58 BitLinear forward
+ * pass on AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (sources: the Falcon-Edge blog, rendered in Arabic on
+ * n77n.net as "A series of powerful, universal and fine-tunable 1.58-bit
+ * language models", section "Falcon-Edge, a series of universal models",
+ * functions activation_norm_quant, _weight_quant, BitLinear.forward and
+ * BitLinear.post_quant_process; and the GeekNews page "BitNet: an inference
+ * framework for 1-bit LLMs", section "Hacker News comments", on 2-bit
+ * storage):
+ *
+ *   weights   : w_scale = 1 / max(mean|w|, 1e-5)            (per tensor)
+ *               u = clamp(round(w * w_scale), -1, 1)        (ternary)
+ *   activations: x_scale[m] = 127 / max(max_k |x[m,k]|, 1e-5) (per token)
+ *               q = clamp(round(x * x_scale), -128, 127)    (int8)
+ *   contraction: acc[m,n] = sum_k q[m,k] * u[n,k]          (exact int32)
+ *   output    : y[m,n] = bf16(acc[m,n] / (x_scale[m] * w_scale))
+ *
+ * Arithmetic: IEEE fp32, round-to-nearest-even for the multiplies, the
+ * correctly rounded divisions and round(); 1e-5 is fp32(1e-5); mean|w| is
+ * the exact sum of |w| over the element count, rounded once to fp32 (so it
+ * does not depend on summation order); the output is rounded to bf16 with
+ * round-to-nearest-even.  Every result is deterministic and bit-identical
+ * from run to run.
+ *
+ * Packed weight format: row-major [N][K/4] bytes.  Byte k/4 of row n holds
+ * weight k at bits 2*(k%4)..2*(k%4)+1 as the code c = u + 1 (0, 1 or 2).
+ * Code 3 is never written; if present in caller data it decodes as +2.
+ *
+ * Conventions for every entry point:
+ *  - All tensor pointers are DEVICE pointers to contiguous row-major data,
+ *    owned by the caller.  The library never allocates, frees, or
+ *    synchronizes, and keeps no state between calls; calls are thread-safe.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Work is only
+ *    enqueued; results are ready once the stream has reached that point.
+ *  - Arguments are validated on the host before anything is enqueued.  On
+ *    any error nothing is enqueued and the status says why.  A failed
+ *    launch returns BL_EHIP.  Faults inside kernels surface at the caller's
+ *    next synchronization, as with any HIP work.
+ *  - Shapes: M, N, K >= 1; K % 4 == 0; K <= 2^22; N <= 2^30; M <= 2^24;
+ *    M*K, N*K/4 and M*N each below 2^40.
+ *  - Alignment: every pointer 16-byte aligned (what hipMalloc and the
+ *    PyTorch caching allocator return for a tensor's storage).
+ *  - Inputs must be finite; non-finite inputs give unspecified outputs.
+ */
+#ifndef BITLINEAR_H
+#define BITLINEAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  BL_OK = 0,
+  BL_EINVAL = 1,     /* null pointer, or count/argument out of range */
+  BL_ESHAPE = 2,     /* M, N or K out of the supported range, K % 4 != 0 */
+  BL_EALIGN = 3,     /* a pointer is not 16-byte aligned */
+  BL_EWORKSPACE = 4, /* workspace pointer null or smaller than required */
+  BL_EHIP = 5        /* a kernel launch failed */
+} bl_status;
+
+/* One projection of a grouped forward call (host-side descriptor). */
+typedef struct {
+  const uint16_t *x;      /* [M][K] bf16 activations (device) */
+  const uint8_t *packed;  /* [N][K/4] packed ternary weights (device) */
+  const float *w_scale;   /* 1 float, the weight scale (device) */
+  uint16_t *y;            /* [M][N] bf16 output (device) */
+  int64_t n;              /* N, output features */
+  int64_t k;              /* K, input features */
+} bl_projection;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *bitlinear_status_string(bl_status s);
+
+/* Interface version of this header; bumped on any ABI change. */
+int bitlinear_abi_version(void);
+
+/* --- weight preparation (offline) ------------------------------------- */
+
+/* Bytes of workspace bitlinear_pack_weights needs (independent of sizes:
+ * 256 64-bit exponent buckets). */
+size_t bitlinear_pack_workspace_bytes(int64_t n, int64_t k);
+
+/* Ternarize and pack latent weights: the blog's _weight_quant followed by
+ * 2-bit storage.  w: [N][K] fp32.  packed: [N][K/4] bytes (written).
+ * w_scale: 1 float (written) = 1 / max(mean|w|, 1e-5).  The mean is exact
+ * (order independent).  workspace: at least
+ * bitlinear_pack_workspace_bytes(n, k) bytes of device memory; its contents
+ * on entry do not matter and are clobbered.  Enqueues four kernels. */
+bl_status bitlinear_pack_weights(const float *w, int64_t n, int64_t k,
+                                 uint8_t *packed, float *w_scale,
+                                 void *workspace, size_t workspace_bytes,
+                                 void *stream);
+
+/* Expand packed weights to int8 values c - 1: [N][K/4] -> [N][K].
+ * (The blog's unpack_weights; used to inspect stored weights.) */
+bl_status bitlinear_unpack_weights(const uint8_t *packed, int64_t n,
+                                   int64_t k, int8_t *u, void *stream);
+
+/* --- activation quantization ------------------------------------------ */
+
+/* The blog's activation_norm_quant on bf16 input.  x: [M][K] bf16.
+ * q: [M][K] int8 (written).  x_scale: [M] fp32 (written). */
+bl_status bitlinear_act_quant(const uint16_t *x, int64_t m, int64_t k,
+                              int8_t *q, float *x_scale, void *stream);
+
+/* --- forward ----------------------------------------------------------- */
+
+/* Bytes of workspace bitlinear_forward needs for this shape. */
+size_t bitlinear_forward_workspace_bytes(int64_t m, int64_t n, int64_t k);
+
+/* BitLinear.forward without bias: y = bf16(q(x) . u^T / (x_scale*w_scale)).
+ * x: [M][K] bf16; packed: [N][K/4]; w_scale: 1 float (device); y: [M][N]
+ * bf16 (written).  workspace: at least
+ * bitlinear_forward_workspace_bytes(m, n, k) bytes; contents on entry do
+ * not matter.  M <= 16 runs the decode GEMV path, larger M the int8
+ * matrix-core GEMM path; both give identical results.  Enqueues two
+ * kernels (activation quantization, then the contraction). */
+bl_status bitlinear_forward(int64_t m, int64_t n, int64_t k,
+                            const uint16_t *x, const uint8_t *packed,
+                            const float *w_scale, uint16_t *y,
+                            void *workspace, size_t workspace_bytes,
+                            void *stream);
+
+/* Bytes of workspace bitlinear_forward_grouped needs. */
+size_t bitlinear_forward_grouped_workspace_bytes(int32_t count,
+                                                 const bl_projection *projs,
+                                                 int64_t m);
+
+/* Several independent BitLinear forwards with the same token count M (for
+ * instance the projections of one decoder layer) in one pass: one
+ * activation-quantization launch and one contraction launch for all of
+ * them.  projs: HOST array of `count` descriptors (1 <= count <= 16);
+ * results are identical to calling bitlinear_forward on each. */
+bl_status bitlinear_forward_grouped(int32_t count, const bl_projection *projs,
+                                    int64_t m, void *workspace,
+                                    size_t workspace_bytes, void *stream);
+
+/* Integer accumulators of caller-supplied int8 codes: acc = q . u^T.
+ * q: [M][K] int8 (any values); packed: [N][K/4]; acc: [M][N] int32
+ * (written).  Runs the same contraction kernels as bitlinear_forward (the
+ * path chosen by M) with an int32 epilogue; exposes the exact accumulators
+ * for inspection.  workspace: bitlinear_forward_workspace_bytes(m, n, k). */
+bl_status bitlinear_forward_acc(int64_t m, int64_t n, int64_t k,
+                                const int8_t *q, const uint8_t *packed,
+                                int32_t *acc, void *workspace,
+                                size_t workspace_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BITLINEAR_H */

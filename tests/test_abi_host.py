@@ -1,0 +1,219 @@
+"""Host-side checks of libbitlinear.so that need no GPU.
+
+* the library loads and exports every function include/bitlinear.h declares;
+* argument validation rejects bad calls before anything is enqueued (every
+  call below fails validation, so no kernel is ever launched);
+* the exact-mean rounding code the finalize kernel runs
+  (csrc/absmean_round.hpp) is compiled for the host and compared with the
+  oracle's mean on exponent-bucket sums, including subnormal and tie cases.
+"""
+
+import ctypes
+import os
+import random
+import re
+import subprocess
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle.bitlinear_oracle import _round_to_f32
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bitlinear.h")
+CSRC = os.path.join(ROOT, "bit_gemm_bitlinear_amd", "csrc")
+
+
+@pytest.fixture(scope="module")
+def bl():
+    from bit_gemm_bitlinear_amd import build as b
+
+    if not os.path.exists(b.LIB):
+        b.build()
+    from bit_gemm_bitlinear_amd import bitlinear
+
+    return bitlinear
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bitlinear_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_function(bl):
+    names = declared_functions()
+    assert len(names) == 11
+    lib = bl.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", bl.LIB_PATH], capture_output=True,
+                         text=True).stdout
+    exported = set(re.findall(r"\bT (bitlinear_\w+)", out))
+    assert set(names) <= exported
+
+
+def test_status_strings_and_version(bl):
+    lib = bl.lib()
+    assert lib.bitlinear_abi_version() == 1
+    for s in range(6):
+        assert lib.bitlinear_status_string(s)
+    assert lib.bitlinear_status_string(99) == b"unknown status"
+
+
+P = ctypes.c_void_p
+A16 = [P(0x10000 * (i + 1)) for i in range(8)]  # aligned, never dereferenced
+
+
+def test_forward_validation(bl):
+    lib = bl.lib()
+    x, pk, ws_, y, w = A16[:5]
+    big = ctypes.c_size_t(1 << 40)
+    assert lib.bitlinear_forward(1, 16, 64, None, pk, ws_, y, w, big, None) == 1
+    assert lib.bitlinear_forward(1, 16, 64, x, None, ws_, y, w, big, None) == 1
+    assert lib.bitlinear_forward(1, 16, 64, x, pk, None, y, w, big, None) == 1
+    assert lib.bitlinear_forward(1, 16, 64, x, pk, ws_, None, w, big, None) == 1
+    for m, n, k in [(0, 16, 64), (1, 0, 64), (1, 16, 0), (1, 16, 62), (1, 16, 2 ** 22 + 4),
+                    (-1, 16, 64), (2 ** 24 + 1, 16, 64), (1, 2 ** 30 + 1, 64)]:
+        assert lib.bitlinear_forward(m, n, k, x, pk, ws_, y, w, big, None) == 2, (m, n, k)
+    assert lib.bitlinear_forward(1, 16, 64, P(0x10008), pk, ws_, y, w, big, None) == 3
+    assert lib.bitlinear_forward(1, 16, 64, x, pk, ws_, P(0x10002), w, big, None) == 3
+    need = lib.bitlinear_forward_workspace_bytes(1, 16, 64)
+    assert need > 0
+    assert lib.bitlinear_forward(1, 16, 64, x, pk, ws_, y, None, big, None) == 4
+    assert lib.bitlinear_forward(1, 16, 64, x, pk, ws_, y, w, need - 1, None) == 4
+    assert lib.bitlinear_forward(1, 16, 64, x, pk, ws_, y, P(0x10004), need, None) == 3
+
+
+def test_other_entry_points_validation(bl):
+    lib = bl.lib()
+    a, b, c, d = A16[:4]
+    assert lib.bitlinear_act_quant(None, 1, 64, b, c, None) == 1
+    assert lib.bitlinear_act_quant(a, 1, 66, b, c, None) == 2
+    assert lib.bitlinear_act_quant(a, 1, 64, b, P(0x10001), None) == 3
+    pw = lib.bitlinear_pack_workspace_bytes(16, 64)
+    assert pw == 2048
+    assert lib.bitlinear_pack_weights(a, 16, 64, b, c, d, pw - 1, None) == 4
+    assert lib.bitlinear_pack_weights(a, 16, 64, b, c, None, pw, None) == 4
+    assert lib.bitlinear_pack_weights(a, 16, 6, b, c, d, pw, None) == 2
+    assert lib.bitlinear_pack_weights(None, 16, 64, b, c, d, pw, None) == 1
+    assert lib.bitlinear_unpack_weights(a, 16, 10, b, None) == 2
+    assert lib.bitlinear_unpack_weights(a, 16, 64, None, None) == 1
+    assert lib.bitlinear_forward_acc(1, 16, 64, a, b, c, None, 1 << 30, None) == 4
+    assert lib.bitlinear_forward_acc(1, 16, 60, None, b, c, d, 1 << 30, None) == 1
+
+
+def test_grouped_validation_and_sizes(bl):
+    lib = bl.lib()
+    Proj = bl.Projection
+    arr = (Proj * 17)()
+    for i in range(17):
+        arr[i] = Proj(0x10000, 0x20000, 0x30000, 0x40000, 64, 128)
+    assert lib.bitlinear_forward_grouped(0, arr, 1, A16[0], 1 << 30, None) == 1
+    assert lib.bitlinear_forward_grouped(17, arr, 1, A16[0], 1 << 30, None) == 1
+    assert lib.bitlinear_forward_grouped(2, None, 1, A16[0], 1 << 30, None) == 1
+    arr[1].k = 130
+    assert lib.bitlinear_forward_grouped(2, arr, 1, A16[0], 1 << 30, None) == 2
+    arr[1].k = 128
+    arr[1].y = 0
+    assert lib.bitlinear_forward_grouped(2, arr, 1, A16[0], 1 << 30, None) == 1
+    arr[1].y = 0x40000
+    need = lib.bitlinear_forward_grouped_workspace_bytes(2, arr, 1)
+    assert need >= 2 * lib.bitlinear_forward_workspace_bytes(1, 64, 128) - 512
+    assert lib.bitlinear_forward_grouped(2, arr, 1, A16[0], need - 1, None) == 4
+    assert lib.bitlinear_forward_grouped_workspace_bytes(0, arr, 1) == 0
+
+
+def test_workspace_sizes_cover_codes(bl):
+    lib = bl.lib()
+    for m, n, k in [(1, 2048, 2048), (16, 3072, 9216), (17, 100, 68), (2048, 6912, 2560),
+                    (512, 14336, 4096)]:
+        need = lib.bitlinear_forward_workspace_bytes(m, n, k)
+        m_pad = m if m <= 16 else -(-m // 128) * 128
+        assert need >= m_pad * (-(-k // 256) * 256) + 8 * m
+    assert lib.bitlinear_forward_workspace_bytes(1, 16, 63) == 0
+
+
+# ------------------------------------------------- exact mean, host build
+
+@pytest.fixture(scope="module")
+def absmean_exe(tmp_path_factory):
+    src = tmp_path_factory.mktemp("absmean") / "absmean_host.cpp"
+    exe = src.with_suffix("")
+    src.write_text(
+        '#include "absmean_round.hpp"\n#include <cstdio>\n'
+        "int main() {\n"
+        "  unsigned long long b[256]; unsigned long long count; int cases;\n"
+        '  if (scanf("%d", &cases) != 1) return 1;\n'
+        "  for (int c = 0; c < cases; ++c) {\n"
+        '    if (scanf("%llu", &count) != 1) return 1;\n'
+        '    for (int i = 0; i < 256; ++i) if (scanf("%llu", &b[i]) != 1) return 1;\n'
+        '    printf("%u\\n", bl::absmean_bits_from_buckets(b, count));\n'
+        "  }\n  return 0;\n}\n")
+    subprocess.run(["g++", "-O2", "-std=c++17", "-I", CSRC, str(src), "-o", str(exe)],
+                   check=True)
+    return str(exe)
+
+
+def oracle_mean_bits(buckets, count):
+    total = sum(int(v) << (max(e, 1) - 1) for e, v in enumerate(buckets))
+    f = _round_to_f32(Fraction(total, count) / Fraction(2) ** 149)
+    return int(np.float32(f).view(np.uint32))
+
+
+def buckets_of(w):
+    bits = np.abs(np.asarray(w, np.float32)).view(np.uint32)
+    e = bits >> 23
+    m = (bits & 0x7FFFFF) | ((e > 0).astype(np.uint32) << 23)
+    b = [0] * 256
+    for ei, mi in zip(e.tolist(), m.tolist()):
+        b[ei] += mi
+    return b
+
+
+def test_host_absmean_rounding_matches_oracle(absmean_exe):
+    rng = random.Random(7)
+    cases = []
+    # real tensors (through the oracle's own exact mean as a cross-check)
+    nrng = np.random.default_rng(8)
+    tensors = [nrng.standard_normal(1000).astype(np.float32) * 0.02,
+               np.full(37, 0.3, np.float32),
+               np.array([1.401298464324817e-45] * 5 + [0.0] * 3, np.float32),
+               np.array([3e38, 3e38, 1e-40], np.float32),
+               np.zeros(9, np.float32)]
+    for w in tensors:
+        cases.append((buckets_of(w), w.size, w))
+    # random bucket patterns a tensor can produce: n_e elements of exponent e
+    # contribute between n_e * 2^23 and n_e * (2^24 - 1) (e > 0), or up to
+    # n_e * (2^23 - 1) for subnormals; zeros fill the rest of the count
+    for _ in range(300):
+        count = rng.choice([1, 2, 3, 7, 10, 1000, 2 ** 20 + 1, rng.randint(1, 2 ** 39)])
+        b = [0] * 256
+        left = count
+        for _ in range(rng.randint(1, 6)):
+            if left == 0:
+                break
+            e = rng.choice([0, 1, 2, rng.randint(0, 254), rng.randint(100, 140), 254])
+            ne = rng.randint(1, left)
+            left -= ne
+            lo, hi = (ne, ne * (2 ** 23 - 1)) if e == 0 else (ne * 2 ** 23, ne * (2 ** 24 - 1))
+            b[e] += rng.randint(lo, hi)
+        cases.append((b, count, None))
+    # exact ties: total = (2j+1) * 2^-150 * count patterns
+    for j in range(40):
+        b = [0] * 256
+        b[0] = 2 * j + 1  # subnormal units of 2^-149 summed; mean = that / 2
+        cases.append((b, 2, None))
+    inp = [str(len(cases))]
+    for b, count, _ in cases:
+        inp.append(str(count))
+        inp.append(" ".join(str(v) for v in b))
+    out = subprocess.run([absmean_exe], input="\n".join(inp), capture_output=True, text=True,
+                         check=True).stdout.split()
+    assert len(out) == len(cases)
+    for (b, count, w), got in zip(cases, out):
+        assert int(got) == oracle_mean_bits(b, count), (count, [(i, v) for i, v in enumerate(b) if v])
+        if w is not None:
+            assert int(got) == int(np.float32(oracle.absmean_exact(w)).view(np.uint32))
