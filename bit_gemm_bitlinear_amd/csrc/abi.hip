@@ -55,12 +55,22 @@ int load_mode_for(int32_t count, const int64_t* ks) {
   return mode;
 }
 
-void make_layout(int32_t count, const int64_t* ns, const int64_t* ks, int64_t m, Layout& L) {
+// `have_x`: the activations are bf16 (not caller-supplied codes), so small
+// decode projections may quantize inside the contraction kernel and need no
+// workspace for codes.
+void make_layout(int32_t count, const int64_t* ns, const int64_t* ks, int64_t m, bool have_x,
+                 Layout& L) {
   L.decode = m <= kDecodeMaxM;
   L.load_mode = load_mode_for(count, ks);
   L.m_pad = L.decode ? (int32_t)m : (int32_t)round_up(m, kPrefillBM);
   size_t off = 0;
   for (int i = 0; i < count; ++i) {
+    L.q_off[i] = L.xs_off[i] = L.qs_off[i] = 0;
+    if (L.decode) {
+      L.plan[i] = plan_decode(m, ns[i], ks[i], L.load_mode);
+      L.plan[i].fused = L.plan[i].fused && have_x;
+      if (L.plan[i].fused) continue;
+    }
     const int64_t ldq = round_up(ks[i], kKPad);
     L.q_off[i] = off;
     off = align256(off + (size_t)L.m_pad * (size_t)ldq);
@@ -73,7 +83,6 @@ void make_layout(int32_t count, const int64_t* ns, const int64_t* ks, int64_t m,
   for (int i = 0; i < count; ++i) {
     L.part_off[i] = L.cnt_off[i] = 0;
     if (!L.decode) continue;
-    L.plan[i] = plan_decode(m, ns[i], ks[i], L.load_mode);
     if (L.plan[i].ksplit > 1) {
       L.part_off[i] = off;
       off = align256(off + sizeof(int32_t) * (size_t)(m * ns[i]));
@@ -82,7 +91,7 @@ void make_layout(int32_t count, const int64_t* ns, const int64_t* ks, int64_t m,
     }
   }
   L.zero_bytes = off - L.zero_off;
-  L.total = off;
+  L.total = off > 0 ? off : 256;
 }
 
 struct ProjIO {
@@ -102,26 +111,37 @@ bl_status run_forward(int32_t count, const ProjIO* io, int64_t m, void* workspac
     ns[i] = io[i].n;
     ks[i] = io[i].k;
   }
+  // The documented requirement (the size queries) is the layout with a code
+  // region for every projection; a call that quantizes inside the
+  // contraction kernel uses less of it.
   Layout L;
-  make_layout(count, ns, ks, m, L);
+  make_layout(count, ns, ks, m, false, L);
   if (!workspace) return BL_EWORKSPACE;
   if (!aligned16(workspace)) return BL_EALIGN;
   if (ws_bytes < L.total) return BL_EWORKSPACE;
+  if (io[0].x != nullptr) make_layout(count, ns, ks, m, true, L);
   char* ws = static_cast<char*>(workspace);
 
   const int load_mode = L.load_mode;
 
-  // 1. activation codes (+ scales, code sums), and clearing of split-K partials
+  // 1. activation codes (+ scales, code sums) of the projections that do not
+  //    quantize inside the contraction kernel, and clearing of split-K partials
   ActQuantArgs qa = {};
-  qa.count = count;
-  int rows = 0;
+  int8_t* qptr[kMaxProj];
+  float* xsptr[kMaxProj];
+  int32_t* qsptr[kMaxProj];
+  int rows = 0, jobs = 0;
   for (int i = 0; i < count; ++i) {
-    ActQuantJob& J = qa.j[i];
+    qptr[i] = reinterpret_cast<int8_t*>(ws + L.q_off[i]);
+    xsptr[i] = reinterpret_cast<float*>(ws + L.xs_off[i]);
+    qsptr[i] = reinterpret_cast<int32_t*>(ws + L.qs_off[i]);
+    if (L.decode && L.plan[i].fused) continue;
+    ActQuantJob& J = qa.j[jobs++];
     J.x = io[i].x;
     J.q_in = io[i].q_in;
-    J.q = reinterpret_cast<int8_t*>(ws + L.q_off[i]);
-    J.x_scale = reinterpret_cast<float*>(ws + L.xs_off[i]);
-    J.qsum = reinterpret_cast<int32_t*>(ws + L.qs_off[i]);
+    J.q = qptr[i];
+    J.x_scale = xsptr[i];
+    J.qsum = qsptr[i];
     J.k = (int32_t)ks[i];
     J.ldq = (int32_t)round_up(ks[i], kKPad);
     J.m = (int32_t)m;
@@ -129,9 +149,11 @@ bl_status run_forward(int32_t count, const ProjIO* io, int64_t m, void* workspac
     J.row_begin = rows;
     rows += L.m_pad;
   }
+  qa.count = jobs;
   qa.zero = reinterpret_cast<int32_t*>(ws + L.zero_off);
   qa.zero_words = (int64_t)(L.zero_bytes / sizeof(int32_t));
-  if (launch_act_quant_internal(qa, rows, stream) != hipSuccess) return BL_EHIP;
+  if (jobs > 0 || qa.zero_words > 0)
+    if (launch_act_quant_internal(qa, rows, stream) != hipSuccess) return BL_EHIP;
 
   // 2. contraction + dequantization
   if (L.decode) {
@@ -140,7 +162,6 @@ bl_status run_forward(int32_t count, const ProjIO* io, int64_t m, void* workspac
     da.m = (int32_t)m;
     da.load_mode = load_mode;
     int wgs = 0, lds_row = 0;
-    size_t red = 0;
     for (int i = 0; i < count; ++i) {
       DecodeProj& P = da.p[i];
       const DecodePlan& pl = L.plan[i];
@@ -148,25 +169,27 @@ bl_status run_forward(int32_t count, const ProjIO* io, int64_t m, void* workspac
       P.w_scale = io[i].w_scale;
       P.y = io[i].y;
       P.acc_out = io[i].acc;
-      P.q = qa.j[i].q;
-      P.x_scale = qa.j[i].x_scale;
-      P.qsum = qa.j[i].qsum;
+      P.x = pl.fused ? io[i].x : nullptr;
+      P.q = qptr[i];
+      P.x_scale = xsptr[i];
+      P.qsum = qsptr[i];
       P.part = pl.ksplit > 1 ? reinterpret_cast<int32_t*>(ws + L.part_off[i]) : nullptr;
       P.count = pl.ksplit > 1 ? reinterpret_cast<uint32_t*>(ws + L.cnt_off[i]) : nullptr;
       P.n = (int32_t)ns[i];
       P.k = (int32_t)ks[i];
-      P.ldq = qa.j[i].ldq;
-      P.tw = pl.tw;
+      P.ldq = (int32_t)round_up(ks[i], kKPad);
+      P.wk = pl.wk;
+      P.tww = pl.tww;
       P.kspw = pl.kspw;
       P.ksplit = pl.ksplit;
       P.ngroups = pl.ngroups;
-      P.wg_begin = wgs;
+      da.wg_begin[i] = wgs;
       wgs += pl.ngroups * pl.ksplit;
       lds_row = std::max(lds_row, pl.kspw * 256 + 16);
-      red = std::max(red, (size_t)4 * pl.tw * m * 16 * 4);
     }
+    for (int i = count; i < kMaxProj; ++i) da.wg_begin[i] = wgs;
     da.lds_row = lds_row;
-    const size_t lds = std::max((size_t)m * lds_row, red);
+    const size_t lds = decode_lds_bytes(m, lds_row);
     if (launch_decode(da, wgs, lds, stream) != hipSuccess) return BL_EHIP;
   } else {
     PrefillArgs pa = {};
@@ -181,12 +204,12 @@ bl_status run_forward(int32_t count, const ProjIO* io, int64_t m, void* workspac
       P.w_scale = io[i].w_scale;
       P.y = io[i].y;
       P.acc_out = io[i].acc;
-      P.q = qa.j[i].q;
-      P.x_scale = qa.j[i].x_scale;
-      P.qsum = qa.j[i].qsum;
+      P.q = qptr[i];
+      P.x_scale = xsptr[i];
+      P.qsum = qsptr[i];
       P.n = (int32_t)ns[i];
       P.k = (int32_t)ks[i];
-      P.ldq = qa.j[i].ldq;
+      P.ldq = (int32_t)round_up(ks[i], kKPad);
       P.tiles_n = (int32_t)((ns[i] + kPrefillBN - 1) / kPrefillBN);
       P.tile_begin = (int32_t)tiles;
       tiles += (int64_t)pa.tiles_m * P.tiles_n;
@@ -263,7 +286,7 @@ bl_status bitlinear_act_quant(const uint16_t* x, int64_t m, int64_t k, int8_t* q
 size_t bitlinear_forward_workspace_bytes(int64_t m, int64_t n, int64_t k) {
   if (check_shape(m, n, k) != BL_OK) return 0;
   Layout L;
-  make_layout(1, &n, &k, m, L);
+  make_layout(1, &n, &k, m, false, L);  // also covers bitlinear_forward_acc
   return L.total;
 }
 
@@ -289,7 +312,7 @@ size_t bitlinear_forward_grouped_workspace_bytes(int32_t count, const bl_project
     ks[i] = projs[i].k;
   }
   Layout L;
-  make_layout(count, ns, ks, m, L);
+  make_layout(count, ns, ks, m, false, L);
   return L.total;
 }
 

@@ -37,34 +37,93 @@ __device__ __forceinline__ int32_t block_sum_i32(int32_t v, int32_t* red) {
   return red[0] + red[1] + red[2] + red[3];
 }
 
-// Row absmax scale of one bf16 row of length k (k % 4 == 0).
-__device__ __forceinline__ float row_scale(const uint16_t* __restrict__ xr, int k,
-                                           uint32_t* red) {
-  const uint2* x4 = reinterpret_cast<const uint2*>(xr);
-  uint32_t a = 0;
-  for (int g = threadIdx.x; g < (k >> 2); g += kThreads) {
-    uint2 v = x4[g];
-    a = max(a, absmax_bits4(v.x, v.y));
-  }
-  a = block_max_u32(a, red);
-  return act_scale(bf16_to_f32(a));
-}
+// A thread handles groups of 16 codes: group g covers k in [16g, 16g+16).
+// Loads of one batch (kBatch groups per thread, 4 x 8 bytes each) are all
+// issued before any is used; addresses past the row end are clamped and the
+// values replaced by zeros (K % 4 == 0, so 4-value pieces never straddle).
+constexpr int kBatch = 4;
+constexpr int kOneBatchK = 16 * kBatch * kThreads;  // rows up to this stay in registers
 
-// 16 codes starting at k0 (codes at k >= k are zero).
-__device__ __forceinline__ void quant16(const uint16_t* __restrict__ xr, int k, int k0, float s,
-                                        int32_t (&q)[16]) {
+struct Group {
+  uint2 v[4];
+};
+
+__device__ __forceinline__ void load_group(const uint16_t* __restrict__ xr, int k, int g,
+                                           Group& o) {
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    if (k0 + 4 * j < k) {
-      uint2 v = *reinterpret_cast<const uint2*>(xr + k0 + 4 * j);
-      q[4 * j + 0] = quant_i8(bf16_to_f32(v.x & 0xFFFFu), s);
-      q[4 * j + 1] = quant_i8(bf16_to_f32(v.x >> 16), s);
-      q[4 * j + 2] = quant_i8(bf16_to_f32(v.y & 0xFFFFu), s);
-      q[4 * j + 3] = quant_i8(bf16_to_f32(v.y >> 16), s);
-    } else {
-      q[4 * j + 0] = q[4 * j + 1] = q[4 * j + 2] = q[4 * j + 3] = 0;
+    const int e = 16 * g + 4 * j;
+    const uint2 v = *reinterpret_cast<const uint2*>(xr + min(e, k - 4));
+    o.v[j] = (e < k) ? v : make_uint2(0u, 0u);
+  }
+}
+
+__device__ __forceinline__ uint32_t group_absmax(const Group& G) {
+  uint32_t a = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) a = max(a, absmax_bits4(G.v[j].x, G.v[j].y));
+  return a;
+}
+
+__device__ __forceinline__ void quant_group(const Group& G, float s, int32_t (&q)[16]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    q[4 * j + 0] = quant_i8(bf16_to_f32(G.v[j].x & 0xFFFFu), s);
+    q[4 * j + 1] = quant_i8(bf16_to_f32(G.v[j].x >> 16), s);
+    q[4 * j + 2] = quant_i8(bf16_to_f32(G.v[j].y & 0xFFFFu), s);
+    q[4 * j + 3] = quant_i8(bf16_to_f32(G.v[j].y >> 16), s);
+  }
+}
+
+// Quantizes one bf16 row of length k; `emit(g, codes)` stores group g for
+// every g < ngroups (groups past the row end carry zero codes).
+template <typename Emit>
+__device__ __forceinline__ float quant_row(const uint16_t* __restrict__ xr, int k, int ngroups,
+                                           uint32_t* red, Emit emit) {
+  const int tid = threadIdx.x;
+  if (ngroups * 16 <= kOneBatchK) {
+    Group G[kBatch];
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) load_group(xr, k, tid + kThreads * b, G[b]);
+    uint32_t a = 0;
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) a = max(a, group_absmax(G[b]));
+    const float s = act_scale(bf16_to_f32(block_max_u32(a, red)));
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) {
+      const int g = tid + kThreads * b;
+      if (g < ngroups) {
+        int32_t q[16];
+        quant_group(G[b], s, q);
+        emit(g, q);
+      }
+    }
+    return s;
+  }
+  uint32_t a = 0;
+  for (int g0 = 0; g0 < ngroups; g0 += kThreads * kBatch) {
+    Group G[kBatch];
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) load_group(xr, k, g0 + tid + kThreads * b, G[b]);
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) a = max(a, group_absmax(G[b]));
+  }
+  const float s = act_scale(bf16_to_f32(block_max_u32(a, red)));
+  for (int g0 = 0; g0 < ngroups; g0 += kThreads * kBatch) {
+    Group G[kBatch];
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) load_group(xr, k, g0 + tid + kThreads * b, G[b]);
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) {
+      const int g = g0 + tid + kThreads * b;
+      if (g < ngroups) {
+        int32_t q[16];
+        quant_group(G[b], s, q);
+        emit(g, q);
+      }
     }
   }
+  return s;
 }
 
 __device__ __forceinline__ void load16_codes(const int8_t* __restrict__ qr, int k, int k0,
@@ -93,12 +152,8 @@ __global__ __launch_bounds__(kThreads) void act_quant_public_kernel(
     const uint16_t* __restrict__ x, int k, int8_t* __restrict__ q, float* __restrict__ x_scale) {
   __shared__ uint32_t red[4];
   const int64_t m = blockIdx.x;
-  const uint16_t* xr = x + m * k;
-  const float s = row_scale(xr, k, red);
   int8_t* qr = q + m * k;
-  for (int g = threadIdx.x; g < (k + 15) / 16; g += kThreads) {
-    int32_t c[16];
-    quant16(xr, k, 16 * g, s, c);
+  const float s = quant_row(x + m * k, k, (k + 15) / 16, red, [&](int g, const int32_t(&c)[16]) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       if (16 * g + 4 * j < k) {
@@ -108,7 +163,7 @@ __global__ __launch_bounds__(kThreads) void act_quant_public_kernel(
         *reinterpret_cast<uint32_t*>(qr + 16 * g + 4 * j) = d;
       }
     }
-  }
+  });
   if (threadIdx.x == 0) x_scale[m] = s;
 }
 
@@ -132,30 +187,30 @@ __global__ __launch_bounds__(kThreads) void act_quant_internal_kernel(const ActQ
       reinterpret_cast<v4i*>(qr)[g] = v4i{0, 0, 0, 0};
     return;
   }
-  float s = 0.0f;
-  const uint16_t* xr = nullptr;
-  const int8_t* qin = nullptr;
-  if (J.x) {
-    xr = J.x + (int64_t)m * J.k;
-    s = row_scale(xr, J.k, red);
-  } else {
-    qin = J.q_in + (int64_t)m * J.k;
-  }
   int32_t sum = 0;
-  for (int g = threadIdx.x; g < J.ldq / 16; g += kThreads) {
-    int32_t c[16];
-    if (xr)
-      quant16(xr, J.k, 16 * g, s, c);
-    else
+  v4i* qv = reinterpret_cast<v4i*>(qr);
+  float s = 0.0f;
+  if (J.x) {
+    s = quant_row(J.x + (int64_t)m * J.k, J.k, J.ldq / 16, red,
+                  [&](int g, const int32_t(&c)[16]) {
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) sum += c[i];
+                    qv[g] = transpose16(c);
+                  });
+  } else {
+    const int8_t* qin = J.q_in + (int64_t)m * J.k;
+    for (int g = threadIdx.x; g < J.ldq / 16; g += kThreads) {
+      int32_t c[16];
       load16_codes(qin, J.k, 16 * g, c);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) sum += c[i];
-    reinterpret_cast<v4i*>(qr)[g] = transpose16(c);
+      for (int i = 0; i < 16; ++i) sum += c[i];
+      qv[g] = transpose16(c);
+    }
   }
   sum = block_sum_i32(sum, reinterpret_cast<int32_t*>(red));
   if (threadIdx.x == 0) {
     J.qsum[m] = sum;
-    if (xr) J.x_scale[m] = s;
+    if (J.x) J.x_scale[m] = s;
   }
 }
 

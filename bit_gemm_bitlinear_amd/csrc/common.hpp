@@ -15,6 +15,22 @@ namespace bl {
 
 typedef int32_t v4i __attribute__((ext_vector_type(4)));
 
+// Address-space casts.  Pointers rebuilt from broadcast lane values lose the
+// compiler's knowledge that they point to global memory, which would turn
+// every access into a flat access (slower, and counted by both the vector
+// and the scalar/LDS memory counters).  G() marks global memory, C() marks
+// read-only data that may be read with scalar loads.
+#define BL_GLOBAL __attribute__((address_space(1)))
+#define BL_CONST __attribute__((address_space(4)))
+template <typename T>
+__device__ __forceinline__ BL_GLOBAL T* G(T* p) {
+  return (BL_GLOBAL T*)p;
+}
+template <typename T>
+__device__ __forceinline__ const BL_CONST T* C(const T* p) {
+  return (const BL_CONST T*)p;
+}
+
 // fp32(1e-5): the lower clamp of the absmax / absmean denominators.
 constexpr float kEps = 1e-5f;
 

@@ -8,10 +8,14 @@
 // so the kernel is organised around streaming them once:
 //  * work unit: a workgroup (4 waves) owns 16*TW consecutive weight rows and
 //    a range of K (all of it unless K is split for LDS space); every lane
-//    issues all of its 16-byte weight loads before touching anything else,
-//    so a whole decoder layer is in flight at once;
-//  * the activation codes (int8, prepared by act_quant.hip) are staged once
-//    per workgroup in LDS;
+//    issues all of its 16-byte weight loads up front, so a whole decoder
+//    layer is in flight at once;
+//  * activations: for small M*K the workgroup quantizes the bf16 rows itself
+//    (activation_norm_quant: exact integer absmax over the bf16 magnitude
+//    bits, one fp32 division, one multiply and round per code) straight into
+//    LDS -- no separate launch; otherwise it stages codes prepared by
+//    act_quant.hip.  Either way activation loads are issued before the weight
+//    loads, because the memory counter retires loads in order;
 //  * each 16 packed bytes hold 64 weights = four K-steps of one row for the
 //    16x16x64 int8 matrix-core op; they are expanded in registers to codes
 //    c = u + 1 with one shift and one mask per dword (common.hpp), and
@@ -24,12 +28,21 @@
 #include "common.hpp"
 #include "internal.hpp"
 
+#include <type_traits>
+
 namespace bl {
 
 namespace {
 
+#ifndef BL_DECODE_WINDOW
+#define BL_DECODE_WINDOW 8
+#endif
+
 constexpr int kThreads = 256;
-constexpr int kStageUnits = kDecodeLdsA / 16 / kThreads;  // 16-byte A units per thread
+constexpr int kWindow = BL_DECODE_WINDOW;  // 16-byte weight chunks in flight per lane
+constexpr int kWaveChunks = 16;            // target chunks streamed per wave
+constexpr int kWaveMaxChunks = 24;         // most chunks one wave streams
+constexpr int kStageUnits = kDecodeLdsA / 16 / kThreads;  // 16-byte code units per thread
 
 // 16 bytes of a packed row at byte offset `off` (a multiple of 16).  Parts
 // past `rowbytes` read the row's last bytes instead (multiplied by zero).
@@ -39,215 +52,427 @@ template <int MODE>
 __device__ __forceinline__ v4i load_w16(const uint8_t* __restrict__ row, int off, int rowbytes) {
   v4i r;
   if constexpr (MODE == 0) {
-    r = *reinterpret_cast<const v4i*>(row + min(off, rowbytes - 16));
+    r = __builtin_nontemporal_load(G(reinterpret_cast<const v4i*>(row + min(off, rowbytes - 16))));
   } else if constexpr (MODE == 1) {
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      r[j] = *reinterpret_cast<const int32_t*>(row + min(off + 4 * j, rowbytes - 4));
+      r[j] = __builtin_nontemporal_load(
+          G(reinterpret_cast<const int32_t*>(row + min(off + 4 * j, rowbytes - 4))));
   } else {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       uint32_t d = 0;
 #pragma unroll
-      for (int b = 0; b < 4; ++b) d |= (uint32_t)row[min(off + 4 * j + b, rowbytes - 1)] << (8 * b);
+      for (int b = 0; b < 4; ++b)
+        d |= (uint32_t)__builtin_nontemporal_load(G(row + min(off + 4 * j + b, rowbytes - 1)))
+             << (8 * b);
       r[j] = (int32_t)d;
     }
   }
   return r;
 }
 
-template <int TW, int MODE>
+// The workgroup's projection, found in one round trip to the kernel-argument
+// segment: lane j (of each 16) reads projection j's first WG index and
+// descriptor, a ballot picks the projection containing this WG, and its
+// descriptor words are broadcast with readlane.  (Indexing the argument
+// struct by a computed projection index would cost a second, dependent
+// round trip before any weight load could be issued.)
+__device__ __forceinline__ DecodeProj select_proj(int count, int* wl) {
+  const char* kp = (const char*)__builtin_amdgcn_kernarg_segment_ptr();
+  const DecodeArgs* ka = reinterpret_cast<const DecodeArgs*>(kp);
+  const int j = threadIdx.x & 15;
+  const int beg = ka->wg_begin[j];
+  const int nxt = ka->wg_begin[j < kMaxProj - 1 ? j + 1 : j];
+  constexpr int kWords = sizeof(DecodeProj) / 16;
+  static_assert(sizeof(DecodeProj) % 16 == 0, "descriptor is read as 16-byte words");
+  v4i words[kWords];
+  const v4i* src = reinterpret_cast<const v4i*>(&ka->p[j]);
+#pragma unroll
+  for (int i = 0; i < kWords; ++i) words[i] = src[i];
+  __builtin_amdgcn_sched_barrier(0);
+  const int end = (j + 1 < count) ? nxt : 0x7FFFFFFF;
+  const int b = (int)blockIdx.x;
+  const unsigned long long hit = __ballot(j < count && b >= beg && b < end);
+  const int pi = __builtin_ctzll(hit) & 15;
+  DecodeProj P;
+  int32_t* dst = reinterpret_cast<int32_t*>(&P);
+#pragma unroll
+  for (int i = 0; i < kWords; ++i)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) dst[4 * i + c] = __builtin_amdgcn_readlane(words[i][c], pi);
+  *wl = b - __builtin_amdgcn_readlane(beg, pi);
+  return P;
+}
+
+__device__ __forceinline__ uint32_t wave_max(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o));
+  return v;
+}
+
+__device__ __forceinline__ int32_t wave_sum(int32_t v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// Calls f(integral_constant<int, i>) for i = 0 .. N-1 (a compile-time loop).
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for_impl(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for_impl<I + 1, N>(f);
+  }
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl<0, N>(f);
+}
+
+// Per-WG scalars shared by the prologue and the epilogue.
+struct Shared {
+  float xs[kDecodeMaxM];      // activation scales
+  int32_t qs[kDecodeMaxM];    // code sums
+  uint32_t part[4][kFusedMaxM];
+  int32_t flag;
+};
+
+// Writes one output (bf16, or the int32 accumulator for inspection).
+__device__ __forceinline__ void store_out(const DecodeProj& P, int m, int n, int32_t acc,
+                                          const Shared& sh, float ws) {
+  if (P.y)
+    *G(P.y + (int64_t)m * P.n + n) = dequant_bf16(acc - sh.qs[m], sh.xs[m], ws);
+  else
+    *G(P.acc_out + (int64_t)m * P.n + n) = acc - sh.qs[m];
+}
+
+template <int TWW, int MODE, bool FUSED>
 __device__ __forceinline__ void decode_body(const DecodeArgs& A, const DecodeProj& P, int wl,
-                                            int8_t* __restrict__ lds, int* __restrict__ flag) {
-  constexpr int MAXS = decode_max_items(MODE) / TW;  // slabs per wave held in registers
+                                            int8_t* __restrict__ lds, Shared& sh) {
   const int M = A.m;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
   const int ln = lane & 15, lg = lane >> 4;
+  // WG -> (row group, K part); wave -> (row wave wr, K wave wk_i)
   const int group = wl / P.ksplit, kpart = wl - group * P.ksplit;
-  const int row0 = group * 16 * TW;
+  const int wr = wave / P.wk, wki = wave - wr * P.wk;
+  const int rows_wg = (4 / P.wk) * TWW * 16;
+  const int row0 = group * rows_wg + wr * TWW * 16;
   const int S = (P.k + 255) >> 8;
   const int sb = kpart * P.kspw;
   const int ns = min(S, sb + P.kspw) - sb;  // slabs of this WG
-  const int nsw = (ns + 3) >> 2;            // slabs per wave
-  const int ws0 = min(ns, wave * nsw);
+  const int nsw = (ns + P.wk - 1) / P.wk;   // slabs per wave
+  const int ws0 = min(ns, wki * nsw);       // first slab of this wave (relative)
   const int nw = min(ns, ws0 + nsw) - ws0;  // slabs of this wave (may be 0)
   const int rowbytes = P.k >> 2;
   const int lrow = A.lds_row;
 
-  // 1. activation codes of this WG -> registers (issued first: L2 hits)
-  const int upr = ns * 16;  // 16-byte units per token row
-  const int units = M * upr;
-  v4i stage[kStageUnits];
+  // 1. activations (bf16 rows, or codes staged by act_quant.hip)
+  constexpr int NX = FUSED ? kFusedChunks : kStageUnits;
+  v4i xin[NX];
+  int units;
+  if constexpr (FUSED) {
+    units = M * P.k / 8;  // 16-byte chunks of 8 bf16, row-contiguous (k % 16 == 0)
 #pragma unroll
-  for (int i = 0; i < kStageUnits; ++i) {
-    int u = min((int)threadIdx.x + kThreads * i, units - 1);
-    int m = u / upr, c = u - m * upr;
-    stage[i] = *reinterpret_cast<const v4i*>(P.q + (int64_t)m * P.ldq + sb * 256 + c * 16);
-  }
-  __builtin_amdgcn_sched_barrier(0);
-
-  // 2. every weight load of this lane, in consumption order
-  v4i breg[MAXS][TW];
-  const int lsmax = max(nw - 1, 0);
+    for (int i = 0; i < NX; ++i)
+      xin[i] = *G(reinterpret_cast<const v4i*>(P.x + 8 * (int64_t)min(tid + kThreads * i, units - 1)));
+  } else {
+    units = M * ns * 16;  // 16-byte code units of the staged K range
+    const int upr = ns * 16;
 #pragma unroll
-  for (int ls = 0; ls < MAXS; ++ls) {
-#pragma unroll
-    for (int t = 0; t < TW; ++t) {
-      const int row = min(row0 + 16 * t + ln, P.n - 1);
-      const int slab = sb + ws0 + min(ls, lsmax);
-      breg[ls][t] = load_w16<MODE>(P.packed + (int64_t)row * rowbytes, slab * 64 + 16 * lg,
-                                   rowbytes);
+    for (int i = 0; i < NX; ++i) {
+      const int u = min(tid + kThreads * i, units - 1);
+      const int m = u / upr, c = u - m * upr;
+      xin[i] = *G(reinterpret_cast<const v4i*>(P.q + (int64_t)m * P.ldq + sb * 256 + c * 16));
+    }
+    if (tid < M) {
+      sh.qs[tid] = *G(P.qsum + tid);
+      if (P.y) sh.xs[tid] = *G(P.x_scale + tid);
     }
   }
-  __builtin_amdgcn_sched_barrier(0);
+  const float ws = P.y ? *C(P.w_scale) : 0.0f;
 
-  // 3. staged codes -> LDS
+  // 2. activation codes -> LDS, before any weight request: under a full HBM
+  //    load every request through the fabric waits about as long as the whole
+  //    weight stream, while an idle fabric answers in one round trip.
+  if constexpr (FUSED) {
+    // per-row absmax over the bf16 magnitude bits (exact)
+    uint32_t mx[kFusedMaxM] = {0, 0, 0, 0};
 #pragma unroll
-  for (int i = 0; i < kStageUnits; ++i) {
-    int u = (int)threadIdx.x + kThreads * i;
-    if (u < units) {
-      int m = u / upr, c = u - m * upr;
-      *reinterpret_cast<v4i*>(lds + m * lrow + c * 16) = stage[i];
-    }
-  }
-  __syncthreads();
-
-  // 4. contraction: per slab, the four A fragments feed TW row tiles
-  v4i acc[TW];
+    for (int i = 0; i < NX; ++i) {
+      const int c = tid + kThreads * i;
+      if (c < units) {
+        const int m = (8 * c) / P.k;
+        const uint32_t a = max(absmax_bits4((uint32_t)xin[i].x, (uint32_t)xin[i].y),
+                               absmax_bits4((uint32_t)xin[i].z, (uint32_t)xin[i].w));
 #pragma unroll
-  for (int t = 0; t < TW; ++t) acc[t] = v4i{0, 0, 0, 0};
-  const bool live = ln < M;
-  const int8_t* abase = lds + (live ? ln : 0) * lrow + 64 * lg;
-#pragma unroll
-  for (int ls = 0; ls < MAXS; ++ls) {
-    if (ls < nw) {
-      v4i a[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        v4i v = *reinterpret_cast<const v4i*>(abase + (ws0 + ls) * 256 + 16 * j);
-        a[j] = live ? v : v4i{0, 0, 0, 0};
+        for (int r = 0; r < kFusedMaxM; ++r) mx[r] = (m == r) ? max(mx[r], a) : mx[r];
       }
+    }
 #pragma unroll
-      for (int t = 0; t < TW; ++t) {
+    for (int r = 0; r < kFusedMaxM; ++r) {
+      if (r < M) {
+        const uint32_t v = wave_max(mx[r]);
+        if (lane == 0) sh.part[wave][r] = v;
+      }
+    }
+    // zero the padding codes [k, 256*S) of every row meanwhile
+    const int pad0 = P.k, padg = (S * 256 - P.k) / 16;  // k % 16 == 0
+    for (int i = tid; i < M * padg; i += kThreads) {
+      const int m = i / padg, c = i - m * padg;
+      *reinterpret_cast<v4i*>(lds + m * lrow + pad0 + 16 * c) = v4i{0, 0, 0, 0};
+    }
+    __syncthreads();
+    float s[kFusedMaxM];
+#pragma unroll
+    for (int r = 0; r < kFusedMaxM; ++r) {
+      const uint32_t a = max(max(sh.part[0][r], sh.part[1][r]), max(sh.part[2][r], sh.part[3][r]));
+      s[r] = act_scale(bf16_to_f32(a));
+    }
+    __syncthreads();  // sh.part is reused for the code sums
+    // quantize: chunk c holds codes 8c..8c+7 of the flattened rows; inside
+    // the 16-group g = k/16, element 4b + a goes to byte 4a + b
+    int32_t sum[kFusedMaxM] = {0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < NX; ++i) {
+      const int c = tid + kThreads * i;
+      if (c < units) {
+        const int m = (8 * c) / P.k;
+        const int k0 = 8 * c - m * P.k;
+        float sc = s[0];
+#pragma unroll
+        for (int r = 1; r < kFusedMaxM; ++r) sc = (m == r) ? s[r] : sc;
+        int32_t code[8];
+        const uint32_t w4[4] = {(uint32_t)xin[i].x, (uint32_t)xin[i].y, (uint32_t)xin[i].z,
+                                (uint32_t)xin[i].w};
+        int32_t part = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t b16 = (e & 1) ? (w4[e >> 1] >> 16) : (w4[e >> 1] & 0xFFFFu);
+          code[e] = quant_i8(bf16_to_f32(b16), sc);
+          part += code[e];
+        }
+#pragma unroll
+        for (int r = 0; r < kFusedMaxM; ++r) sum[r] += (m == r) ? part : 0;
+        // k0 = 16g + 8h: element e of the chunk is 4(2h + e/4) + e%4 of the group
+        int8_t* dst = lds + m * lrow + (k0 & ~15) + 2 * ((k0 >> 3) & 1);
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const uint32_t pair = ((uint32_t)code[a] & 0xFFu) | (((uint32_t)code[4 + a] & 0xFFu) << 8);
+          *reinterpret_cast<uint16_t*>(dst + 4 * a) = (uint16_t)pair;
+        }
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < kFusedMaxM; ++r) {
+      if (r < M) {
+        const int32_t v = wave_sum(sum[r]);
+        if (lane == 0) sh.part[wave][r] = (uint32_t)v;
+      }
+      if (tid == r && r < M) sh.xs[r] = s[r];
+    }
+    __syncthreads();
+    if (tid < M)
+      sh.qs[tid] = (int32_t)(sh.part[0][tid] + sh.part[1][tid] + sh.part[2][tid] + sh.part[3][tid]);
+  } else {
+    const int upr = ns * 16;
+#pragma unroll
+    for (int i = 0; i < NX; ++i) {
+      const int u = tid + kThreads * i;
+      if (u < units) {
+        const int m = u / upr, c = u - m * upr;
+        *reinterpret_cast<v4i*>(lds + m * lrow + c * 16) = xin[i];
+      }
+    }
+    __syncthreads();
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // 3. weights: this wave streams its TWW row tiles over its K slabs through a
+  //    ring of kWindow 16-byte chunks per lane (chunk = 64 weights of one row
+  //    = four K-steps), slab-major so each A fragment feeds TWW tiles.  Every
+  //    load is unconditional (past the end it repeats the last chunk, a cache
+  //    hit that is never used), so the memory-counter waits are exact.
+  constexpr int W = kWindow;
+  static_assert(W % TWW == 0, "a ring slot always holds the same row tile");
+  const int NI = TWW * nw;
+  const int last = max(NI - 1, 0);
+  auto wload = [&](int it) {
+    const int c = min(it, last);
+    const int ls = c / TWW, t = c - ls * TWW;
+    const int row = min(row0 + 16 * t + ln, P.n - 1);
+    return load_w16<MODE>(P.packed + (int64_t)row * rowbytes, (sb + ws0 + ls) * 64 + 16 * lg,
+                          rowbytes);
+  };
+  v4i ring[W];
+#pragma unroll
+  for (int d = 0; d < W; ++d) ring[d] = wload(d);
+
+  v4i acc[TWW];
+#pragma unroll
+  for (int t = 0; t < TWW; ++t) acc[t] = v4i{0, 0, 0, 0};
+  const bool live = ln < M;
+  const int8_t* abase = lds + (live ? ln : 0) * lrow + 64 * lg + ws0 * 256;
+  v4i a[4];
+  // One round consumes ring slots 0..W-1 (items base..base+W-1); with
+  // REFILL each slot is reloaded with the item one round ahead right after
+  // it is read.  Rounds are nested so every executed path is straight-line
+  // code: the memory-counter waits stay exact and no load is wasted.
+  auto round = [&](int base, auto refill) {
+    static_for<W>([&](auto dc) {
+      constexpr int d = decltype(dc)::value;
+      const int it = base + d;
+      const v4i b = ring[d];
+      if constexpr (decltype(refill)::value) ring[d] = wload(it + W);
+      if (it < NI) {
+        constexpr int t = d % TWW;  // base is a multiple of W, W of TWW
+        if constexpr (t == 0) {
+          const int ls = base / TWW + d / TWW;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const v4i v = *reinterpret_cast<const v4i*>(abase + ls * 256 + 16 * j);
+            a[j] = live ? v : v4i{0, 0, 0, 0};
+          }
+        }
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          acc[t] = mfma_16x16x64_i8(a[j], decode16((uint32_t)breg[ls][t][j]), acc[t]);
+          acc[t] = mfma_16x16x64_i8(a[j], decode16((uint32_t)b[j]), acc[t]);
       }
+    });
+  };
+  using Yes = std::true_type;
+  using No = std::false_type;
+  static_assert(kWaveMaxChunks <= 3 * W, "at most three rounds");
+  if (NI <= W) {
+    round(0, No{});
+  } else {
+    round(0, Yes{});
+    if (NI <= 2 * W) {
+      round(W, No{});
+    } else {
+      round(W, Yes{});
+      round(2 * W, No{});
     }
   }
-  __syncthreads();  // LDS is reused below
 
-  // 5. cross-wave reduction: red[wave][t][m][16]; lane holds rows 4*lg+r, column ln
-  int32_t* red = reinterpret_cast<int32_t*>(lds);
+  // 4. epilogue.  Lane (ln, lg) holds rows m = 4*lg + r of output column
+  //    row0 + 16*t + ln.
+  if (P.wk == 1 && P.ksplit == 1) {
 #pragma unroll
-  for (int t = 0; t < TW; ++t) {
+    for (int t = 0; t < TWW; ++t) {
+      const int n = row0 + 16 * t + ln;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int m = 4 * lg + r;
-      if (m < M) red[((wave * TW + t) * M + m) * 16 + ln] = acc[t][r];
-    }
-  }
-  __syncthreads();
-
-  const int nout = TW * M * 16;
-  const int wstride = TW * M * 16;
-  if (P.ksplit == 1) {
-    const float ws = P.y ? P.w_scale[0] : 0.0f;
-    for (int idx = threadIdx.x; idx < nout; idx += kThreads) {
-      const int t = idx / (M * 16), rem = idx - t * M * 16, m = rem >> 4, c = rem & 15;
-      const int n = row0 + 16 * t + c;
-      if (n >= P.n) continue;
-      const int32_t v = red[idx] + red[idx + wstride] + red[idx + 2 * wstride] +
-                        red[idx + 3 * wstride] - P.qsum[m];
-      if (P.y)
-        P.y[(int64_t)m * P.n + n] = dequant_bf16(v, P.x_scale[m], ws);
-      else
-        P.acc_out[(int64_t)m * P.n + n] = v;
+      for (int r = 0; r < 4; ++r) {
+        const int m = 4 * lg + r;
+        if (m < M && n < P.n) store_out(P, m, n, acc[t][r], sh, ws);
+      }
     }
     return;
   }
-
-  // K split across WGs: add partials in L2, the last WG of the row group
-  // finishes (integer addition, so the arrival order does not matter).
-  for (int idx = threadIdx.x; idx < nout; idx += kThreads) {
-    const int t = idx / (M * 16), rem = idx - t * M * 16, m = rem >> 4, c = rem & 15;
-    const int n = row0 + 16 * t + c;
-    if (n >= P.n) continue;
-    atomicAdd(&P.part[(int64_t)m * P.n + n],
-              red[idx] + red[idx + wstride] + red[idx + 2 * wstride] + red[idx + 3 * wstride]);
+  // K split across the waves of a row group: partial sums meet in LDS
+  // (a region after the staged codes, so no barrier is needed before writing)
+  int32_t* red = reinterpret_cast<int32_t*>(lds + M * lrow);
+#pragma unroll
+  for (int t = 0; t < TWW; ++t) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int m = 4 * lg + r;
+      if (m < M) red[((wave * TWW + t) * M + m) * 16 + ln] = acc[t][r];
+    }
   }
-  __threadfence();
   __syncthreads();
-  if (threadIdx.x == 0) *flag = (atomicAdd(&P.count[group], 1u) == (uint32_t)(P.ksplit - 1));
-  __syncthreads();
-  if (!*flag) return;
-  __threadfence();
-  const float ws = P.y ? P.w_scale[0] : 0.0f;
-  for (int idx = threadIdx.x; idx < nout; idx += kThreads) {
-    const int t = idx / (M * 16), rem = idx - t * M * 16, m = rem >> 4, c = rem & 15;
-    const int n = row0 + 16 * t + c;
+  const int nout = (4 / P.wk) * TWW * M * 16;  // outputs of this WG
+  const int grp = TWW * M * 16;                 // outputs per row wave
+  for (int idx = tid; idx < nout; idx += kThreads) {
+    const int g = idx / grp, rem = idx - g * grp;  // g = row wave
+    const int t = rem / (M * 16), rem2 = rem - t * M * 16, m = rem2 >> 4, c = rem2 & 15;
+    const int n = group * rows_wg + g * TWW * 16 + 16 * t + c;
+    int32_t v = 0;
+    for (int q = 0; q < P.wk; ++q) v += red[(((g * P.wk + q) * TWW + t) * M + m) * 16 + c];
     if (n >= P.n) continue;
-    const int32_t v = atomicAdd(&P.part[(int64_t)m * P.n + n], 0) - P.qsum[m];
-    if (P.y)
-      P.y[(int64_t)m * P.n + n] = dequant_bf16(v, P.x_scale[m], ws);
+    if (P.ksplit == 1)
+      store_out(P, m, n, v, sh, ws);
     else
-      P.acc_out[(int64_t)m * P.n + n] = v;
+      atomicAdd(P.part + (int64_t)m * P.n + n, v);
   }
+  if (P.ksplit == 1) return;
+
+  // K split across WGs (never with fused quantization): the last WG of the
+  // row group finishes (integer addition, so the arrival order does not matter).
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) sh.flag = (atomicAdd(P.count + group, 1u) == (uint32_t)(P.ksplit - 1));
+  __syncthreads();
+  if (!sh.flag) return;
+  __threadfence();
+  for (int idx = tid; idx < nout; idx += kThreads) {
+    const int g = idx / grp, rem = idx - g * grp;
+    const int t = rem / (M * 16), rem2 = rem - t * M * 16, m = rem2 >> 4, c = rem2 & 15;
+    const int n = group * rows_wg + g * TWW * 16 + 16 * t + c;
+    if (n >= P.n) continue;
+    store_out(P, m, n, atomicAdd(P.part + (int64_t)m * P.n + n, 0), sh, ws);
+  }
+}
+
+template <int TWW, int MODE>
+__device__ __forceinline__ void decode_tw(const DecodeArgs& A, const DecodeProj& P, int wl,
+                                          int8_t* lds, Shared& sh) {
+  if constexpr (MODE == 0) {
+    if (P.x) {
+      decode_body<TWW, MODE, true>(A, P, wl, lds, sh);
+      return;
+    }
+  }
+  decode_body<TWW, MODE, false>(A, P, wl, lds, sh);
 }
 
 template <int MODE>
 __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs A) {
   extern __shared__ __align__(16) int8_t lds[];
-  __shared__ int flag;
-  int pi = 0;
-  while (pi + 1 < A.count && (int)blockIdx.x >= A.p[pi + 1].wg_begin) ++pi;
-  const DecodeProj& P = A.p[pi];
-  const int wl = (int)blockIdx.x - P.wg_begin;
-  constexpr int kMaxTw = decode_max_items(MODE) < kDecodeMaxTw ? decode_max_items(MODE)
-                                                                : kDecodeMaxTw;
-  switch (P.tw) {
-    case 1: decode_body<1, MODE>(A, P, wl, lds, &flag); break;
-    case 2: decode_body<2, MODE>(A, P, wl, lds, &flag); break;
-    case 3: if constexpr (kMaxTw >= 3) decode_body<3, MODE>(A, P, wl, lds, &flag); break;
-    case 4: if constexpr (kMaxTw >= 4) decode_body<4, MODE>(A, P, wl, lds, &flag); break;
-    case 5: if constexpr (kMaxTw >= 5) decode_body<5, MODE>(A, P, wl, lds, &flag); break;
-    case 6: if constexpr (kMaxTw >= 6) decode_body<6, MODE>(A, P, wl, lds, &flag); break;
-    case 7: if constexpr (kMaxTw >= 7) decode_body<7, MODE>(A, P, wl, lds, &flag); break;
-    case 8: if constexpr (kMaxTw >= 8) decode_body<8, MODE>(A, P, wl, lds, &flag); break;
-    default: break;
+  __shared__ Shared sh;
+  int wl;
+  const DecodeProj P = select_proj(A.count, &wl);
+  switch (P.tww) {
+    case 1: decode_tw<1, MODE>(A, P, wl, lds, sh); break;
+    case 2: decode_tw<2, MODE>(A, P, wl, lds, sh); break;
+    default: decode_tw<4, MODE>(A, P, wl, lds, sh); break;
   }
 }
 
 }  // namespace
 
-// Choose the work split of one projection: K per WG limited by the LDS
-// budget for staged codes and by the register budget (16 loads per lane),
-// then as many 16-row tiles per WG as fill the register budget (so every
-// lane issues about 16 loads of 16 bytes and a WG moves about 64 KB).
+// Work split of one projection.  The K range of a WG is limited by the LDS
+// budget for staged codes (beyond it WGs split K and add partial sums in
+// L2).  Waves of a WG split K as well when its range is long (1, 2 or 4
+// ways, partial sums meet in LDS); otherwise each wave owns its own row
+// tiles.  Tiles per wave bring a wave's stream to about kWaveChunks 16-byte
+// chunks, so a WG moves about 64 KB.  Small M*K with 16-aligned rows takes
+// the fused path (the WG quantizes the bf16 rows itself), which never
+// splits K across WGs.
 DecodePlan plan_decode(int64_t m, int64_t n, int64_t k, int mode) {
   DecodePlan p;
-  const int items = decode_max_items(mode);
   const int S = (int)((k + 255) / 256);
-  int cap_lds = (int)((kDecodeLdsA / m - 16) / 256);
-  if (cap_lds < 1) cap_lds = 1;
-  const int cap = cap_lds < 4 * items ? cap_lds : 4 * items;
+  int cap = (int)((kDecodeLdsA / m - 16) / 256);
+  if (cap < 1) cap = 1;
+  if (cap > 4 * kWaveMaxChunks) cap = 4 * kWaveMaxChunks;
   p.ksplit = (S + cap - 1) / cap;
   p.kspw = (S + p.ksplit - 1) / p.ksplit;
-  const int nsw = (p.kspw + 3) / 4;
-  int tw = items / nsw;
-  if (tw > kDecodeMaxTw) tw = kDecodeMaxTw;
-  if (tw < 1) tw = 1;
-  const int tiles = (int)((n + 15) / 16);
-  if (tw > tiles) tw = tiles;
-  p.tw = tw;
-  p.ngroups = (int)((n + 16 * tw - 1) / (16 * tw));
+  p.wk = p.kspw <= kWaveChunks ? 1 : (p.kspw <= 2 * kWaveMaxChunks ? 2 : 4);
+  if (p.wk == 2 && (p.kspw + 1) / 2 > kWaveChunks && p.kspw > 2 * kWaveChunks) p.wk = 4;
+  const int nsw = (p.kspw + p.wk - 1) / p.wk;  // <= kWaveMaxChunks
+  int tww = 1;
+  while (tww < kDecodeMaxTww && 2 * tww * nsw <= kWaveChunks) tww *= 2;  // 1, 2 or 4
+  const int rows_wg = (4 / p.wk) * tww * 16;
+  p.tww = tww;
+  p.ngroups = (int)((n + rows_wg - 1) / rows_wg);
+  p.fused = mode == 0 && m <= kFusedMaxM && k % 16 == 0 && m * k <= kFusedMaxElems &&
+            p.ksplit == 1;
   return p;
 }
 
-size_t decode_lds_bytes(int64_t m, const DecodePlan& p) {
-  size_t a = (size_t)m * ((size_t)p.kspw * 256 + 16);
-  size_t r = (size_t)4 * p.tw * m * 16 * 4;
-  return a > r ? a : r;
+size_t decode_lds_bytes(int64_t m, int lds_row) {
+  return (size_t)m * lds_row + (size_t)4 * kDecodeMaxTww * m * 16 * 4;
 }
 
 hipError_t launch_decode(const DecodeArgs& a, int total_wgs, size_t lds_bytes, hipStream_t s) {

@@ -11,10 +11,7 @@ constexpr int kMaxProj = 16;
 
 // Decode path (M <= 16) limits.
 constexpr int kDecodeMaxM = 16;
-constexpr int kDecodeMaxTw = 8;       // 16-row tiles per WG
-// 16-byte weight chunks a lane holds in registers, by row alignment (load
-// mode 0: 16-byte rows, 1: 4-byte rows, 2: unaligned rows, byte loads).
-constexpr int decode_max_items(int mode) { return mode == 0 ? 16 : mode == 1 ? 8 : 4; }
+constexpr int kDecodeMaxTww = 4;      // 16-row tiles per wave
 constexpr int kDecodeLdsA = 48 * 1024;
 
 // Activation codes for the contraction kernels are kept in an internal
@@ -49,25 +46,34 @@ hipError_t launch_act_quant_public(const uint16_t* x, int64_t m, int64_t k, int8
                                    float* x_scale, hipStream_t s);
 
 // ---- decode contraction (decode.hip) ----
+// Fused activation quantization inside the decode kernel: each workgroup
+// reads the whole bf16 rows (at most kFusedMaxElems values, 16-byte chunks
+// held in registers) and quantizes them itself.
+constexpr int kFusedMaxM = 4;
+constexpr int kFusedChunks = 8;  // 16-byte chunks of x per thread
+constexpr int64_t kFusedMaxElems = (int64_t)kFusedChunks * 8 * 256;
+
 struct DecodeProj {
   const uint8_t* packed;
   const float* w_scale;
   uint16_t* y;         // bf16 output, or nullptr
   int32_t* acc_out;    // int32 output when y == nullptr
-  const int8_t* q;     // internal-layout codes, [16][ldq]
+  const uint16_t* x;   // fused: bf16 activations [m][k]; nullptr otherwise
+  const int8_t* q;     // not fused: internal-layout codes [m][ldq]
   const float* x_scale;
   const int32_t* qsum;
   int32_t* part;       // [m][n] int32 split-K partials (zeroed beforehand)
   uint32_t* count;     // [ngroups] split-K arrival counters (zeroed beforehand)
   int32_t n, k, ldq;
-  int32_t tw;          // 16-row tiles per WG
+  int32_t wk;          // waves sharing one row tile along K (1, 2 or 4)
+  int32_t tww;         // 16-row tiles per wave
   int32_t kspw;        // K slabs (256 codes) per WG
   int32_t ksplit;      // WGs sharing one row group along K
-  int32_t ngroups;     // row groups
-  int32_t wg_begin;    // first WG of this projection in the launch
+  int32_t ngroups;     // row groups of (4 / wk) * tww * 16 rows
 };
 
 struct DecodeArgs {
+  int32_t wg_begin[kMaxProj];  // first WG of each projection
   DecodeProj p[kMaxProj];
   int32_t count;
   int32_t m;
@@ -76,10 +82,11 @@ struct DecodeArgs {
 };
 
 struct DecodePlan {
-  int32_t tw, kspw, ksplit, ngroups;
+  int32_t wk, tww, kspw, ksplit, ngroups;
+  bool fused;
 };
 DecodePlan plan_decode(int64_t m, int64_t n, int64_t k, int mode);
-size_t decode_lds_bytes(int64_t m, const DecodePlan& p);
+size_t decode_lds_bytes(int64_t m, int lds_row);
 hipError_t launch_decode(const DecodeArgs& a, int total_wgs, size_t lds_bytes, hipStream_t s);
 
 // ---- prefill contraction (prefill.hip) ----
