@@ -197,9 +197,15 @@ bl_status run_forward(int32_t count, const ProjIO* io, int64_t m, void* workspac
     pa.m = (int32_t)m;
     pa.tiles_m = L.m_pad / kPrefillBM;
     pa.load_mode = load_mode;
+    // Longest K first: the dispatcher hands out workgroups in launch order,
+    // so the costliest tiles start first and the short ones fill in.
+    int order[kMaxProj];
+    for (int i = 0; i < count; ++i) order[i] = i;
+    std::stable_sort(order, order + count, [&](int a, int b) { return ks[a] > ks[b]; });
     int64_t tiles = 0;
-    for (int i = 0; i < count; ++i) {
-      PrefillProj& P = pa.p[i];
+    for (int o = 0; o < count; ++o) {
+      const int i = order[o];
+      PrefillProj& P = pa.p[o];
       P.packed = io[i].packed;
       P.w_scale = io[i].w_scale;
       P.y = io[i].y;
@@ -210,10 +216,11 @@ bl_status run_forward(int32_t count, const ProjIO* io, int64_t m, void* workspac
       P.n = (int32_t)ns[i];
       P.k = (int32_t)ks[i];
       P.ldq = (int32_t)round_up(ks[i], kKPad);
-      P.tiles_n = (int32_t)((ns[i] + kPrefillBN - 1) / kPrefillBN);
-      P.tile_begin = (int32_t)tiles;
-      tiles += (int64_t)pa.tiles_m * P.tiles_n;
+      P.tiles_n = (int32_t)((ns[i] + prefill_bn(load_mode) - 1) / prefill_bn(load_mode));
+      pa.tile_begin[o] = (int32_t)tiles;
+      tiles += round_up((int64_t)pa.tiles_m * P.tiles_n, 8);  // XCD-aligned ranges
     }
+    for (int o = count; o < kMaxProj; ++o) pa.tile_begin[o] = (int32_t)tiles;
     if (tiles >= (int64_t(1) << 31)) return BL_ESHAPE;
     if (launch_prefill(pa, (int)tiles, stream) != hipSuccess) return BL_EHIP;
   }

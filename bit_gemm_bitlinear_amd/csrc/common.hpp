@@ -53,12 +53,13 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
   return __uint_as_float(bits16 << 16);
 }
 
-// fp32 -> bf16, round to nearest even; NaN stays a quiet NaN.
+// fp32 -> bf16, round to nearest even; NaN stays a quiet NaN (a select,
+// not a branch).
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t rounded = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+  const uint32_t quiet = (u >> 16) | 0x40u;
+  return (uint16_t)(((u & 0x7FFFFFFFu) > 0x7F800000u) ? quiet : rounded);
 }
 
 // Per-token scale from the row's absmax: 127 / max(amax, 1e-5).
@@ -85,6 +86,23 @@ __device__ __forceinline__ uint16_t dequant_bf16(int32_t acc, float xs, float ws
   float d = xs * ws;
   float yf = (float)acc / d;
   return f32_to_bf16(yf);
+}
+
+}  // namespace bl
+
+#include "row_div.hpp"
+
+namespace bl {
+
+// Same result as dequant_bf16 for a row whose divisor was prepared once.
+__device__ __forceinline__ uint16_t dequant_bf16_row(int32_t acc, const RowDiv& r) {
+  return f32_to_bf16(row_div((float)acc, r));
+}
+
+// The same when the divisor is known to be in the range of the fast step
+// (row_div_setup's `fast`), without the per-value check.
+__device__ __forceinline__ uint16_t dequant_bf16_fast(int32_t acc, float d, float y) {
+  return f32_to_bf16(row_div_fast((float)acc, d, y));
 }
 
 // Largest magnitude pattern of four bf16 values held in two dwords; the

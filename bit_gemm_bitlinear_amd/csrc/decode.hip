@@ -132,7 +132,7 @@ __device__ __forceinline__ void static_for(F&& f) {
 
 // Per-WG scalars shared by the prologue and the epilogue.
 struct Shared {
-  float xs[kDecodeMaxM];      // activation scales
+  RowDiv rd[kDecodeMaxM];     // per-row divisors x_scale * w_scale
   int32_t qs[kDecodeMaxM];    // code sums
   uint32_t part[4][kFusedMaxM];
   int32_t flag;
@@ -141,8 +141,9 @@ struct Shared {
 // Writes one output (bf16, or the int32 accumulator for inspection).
 __device__ __forceinline__ void store_out(const DecodeProj& P, int m, int n, int32_t acc,
                                           const Shared& sh, float ws) {
+  (void)ws;
   if (P.y)
-    *G(P.y + (int64_t)m * P.n + n) = dequant_bf16(acc - sh.qs[m], sh.xs[m], ws);
+    *G(P.y + (int64_t)m * P.n + n) = dequant_bf16_row(acc - sh.qs[m], sh.rd[m]);
   else
     *G(P.acc_out + (int64_t)m * P.n + n) = acc - sh.qs[m];
 }
@@ -186,12 +187,14 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& A, const DecodePro
       const int m = u / upr, c = u - m * upr;
       xin[i] = *G(reinterpret_cast<const v4i*>(P.q + (int64_t)m * P.ldq + sb * 256 + c * 16));
     }
-    if (tid < M) {
-      sh.qs[tid] = *G(P.qsum + tid);
-      if (P.y) sh.xs[tid] = *G(P.x_scale + tid);
-    }
   }
   const float ws = P.y ? *C(P.w_scale) : 0.0f;
+  if constexpr (!FUSED) {
+    if (tid < M) {
+      sh.qs[tid] = *G(P.qsum + tid);
+      if (P.y) sh.rd[tid] = row_div_setup(*G(P.x_scale + tid) * ws);
+    }
+  }
 
   // 2. activation codes -> LDS, before any weight request: under a full HBM
   //    load every request through the fabric waits about as long as the whole
@@ -270,7 +273,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& A, const DecodePro
         const int32_t v = wave_sum(sum[r]);
         if (lane == 0) sh.part[wave][r] = (uint32_t)v;
       }
-      if (tid == r && r < M) sh.xs[r] = s[r];
+      if (tid == r && r < M && P.y) sh.rd[r] = row_div_setup(s[r] * ws);
     }
     __syncthreads();
     if (tid < M)

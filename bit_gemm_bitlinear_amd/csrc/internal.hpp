@@ -90,8 +90,13 @@ size_t decode_lds_bytes(int64_t m, int lds_row);
 hipError_t launch_decode(const DecodeArgs& a, int total_wgs, size_t lds_bytes, hipStream_t s);
 
 // ---- prefill contraction (prefill.hip) ----
-constexpr int kPrefillBM = 128;
-constexpr int kPrefillBN = 128;
+constexpr int kPrefillBM = 128;  // token rows per tile
+#ifndef BL_PREFILL_BN
+#define BL_PREFILL_BN 128
+#endif
+constexpr int kPrefillBN = BL_PREFILL_BN;  // output columns per tile, 16-byte aligned weight rows
+constexpr int kPrefillRegBN = 256;  // output columns per tile, other weight rows
+inline int prefill_bn(int load_mode) { return load_mode == 0 ? kPrefillBN : kPrefillRegBN; }
 
 struct PrefillProj {
   const uint8_t* packed;
@@ -103,10 +108,10 @@ struct PrefillProj {
   const int32_t* qsum;
   int32_t n, k, ldq;
   int32_t tiles_n;      // ceil(n / BN)
-  int32_t tile_begin;   // first tile of this projection in the launch
 };
 
 struct PrefillArgs {
+  int32_t tile_begin[kMaxProj];  // first tile of each projection in the launch
   PrefillProj p[kMaxProj];
   int32_t count;
   int32_t m;

@@ -4,142 +4,470 @@
 // Falcon-Edge blog ("A series of powerful, universal and fine-tunable 1.58-bit
 // language models", section "Falcon-Edge, a series of universal models").
 //
-// A dense contraction, so it runs on v_mfma_i32_16x16x64_i8.  A workgroup
-// computes a 128x128 output tile with four waves (2x2, 64x64 each).  Per
-// 256-wide K slab a lane loads, for each of its four 16-column weight tiles,
-// 16 packed bytes (64 weights = four K-steps of one row) and expands them in
-// registers (common.hpp); the activation codes come from the internal layout
-// written by act_quant.hip (rows padded to the tile, K padded to 256 with
-// zero codes), so no operand load needs a bounds check.  Out-of-range weight
-// rows and columns are clamped to valid addresses: they only reach output
-// entries that are not stored, or meet zero activation codes.
+// A dense contraction, so it runs on v_mfma_i32_32x32x32_i8 (half the
+// operand bytes and half the weight-expansion work per multiply of the
+// 16x16x64 form).  A workgroup computes a 128 (tokens) x 256 (outputs) tile
+// with four waves of 64 x 128 (2 x 4 matrix-core tiles of 32 x 32).
+//
+//  * K advances by slabs of 256 codes.  The activation-code tile of a slab
+//    (128 rows x 256 B, internal layout from act_quant.hip) is staged in LDS,
+//    double-buffered: slab s+1 is fetched into registers while slab s is
+//    consumed, then written to the other buffer.  16-byte chunk c of row r is
+//    stored at chunk c ^ (r & 15), which spreads the 32 rows one A fragment
+//    reads over all banks.
+//  * Packed weights are small (2 bits each) and each wave needs its own 128
+//    columns, so they go straight from global memory to registers, one slab
+//    ahead, and are expanded there (common.hpp).  In K-step s of a slab, lane
+//    (column j, half g) supplies codes 128g + 16s .. +15, i.e. 32 contiguous
+//    packed bytes per lane per slab; the activation fragment uses the same
+//    codes (the assignment of codes to K-steps is free as long as both
+//    operands agree).
+//  * Rows of codes are zero-padded to the tile, K to 256, so activation loads
+//    need no bounds checks; weight rows and columns past the end are clamped
+//    to valid addresses (they meet zero codes or reach outputs that are not
+//    stored).
 #include "common.hpp"
 #include "internal.hpp"
+
+#include <type_traits>
 
 namespace bl {
 
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int BM = kPrefillBM;  // 128
+constexpr int BN = kPrefillRegBN;  // 256 (register-staged variant)
+constexpr int kStageChunks = BM * 16 / kThreads;  // 16-byte A chunks per thread per slab
+
+typedef int32_t v16i __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ v16i mfma_32x32x32_i8(v4i a, v4i b, v16i c) {
+  return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
+}
 
 // 16 bytes of a packed row (see decode.hip); MODE fixes the row alignment.
 template <int MODE>
 __device__ __forceinline__ v4i load_w16(const uint8_t* __restrict__ row, int off, int rowbytes) {
   v4i r;
   if constexpr (MODE == 0) {
-    r = *reinterpret_cast<const v4i*>(row + min(off, rowbytes - 16));
+    r = *G(reinterpret_cast<const v4i*>(row + min(off, rowbytes - 16)));
   } else if constexpr (MODE == 1) {
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      r[j] = *reinterpret_cast<const int32_t*>(row + min(off + 4 * j, rowbytes - 4));
+      r[j] = *G(reinterpret_cast<const int32_t*>(row + min(off + 4 * j, rowbytes - 4)));
   } else {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       uint32_t d = 0;
 #pragma unroll
-      for (int b = 0; b < 4; ++b) d |= (uint32_t)row[min(off + 4 * j + b, rowbytes - 1)] << (8 * b);
+      for (int b = 0; b < 4; ++b) d |= (uint32_t)*G(row + min(off + 4 * j + b, rowbytes - 1)) << (8 * b);
       r[j] = (int32_t)d;
     }
   }
   return r;
 }
 
-struct Frags {
-  v4i a[4][4];  // [m tile][k step]
-  v4i b[4];     // [n tile], 4 K-steps each
+struct Tile {
+  const PrefillProj* P;
+  int m0, n0;
 };
 
+// Weight fragments of one slab: 4 column tiles x 32 packed bytes per lane.
 template <int MODE>
-__device__ __forceinline__ void load_frags(Frags& f, const PrefillProj& P, int m0, int n0,
-                                           int slab, int ln, int lg) {
+__device__ __forceinline__ void load_b(v4i (&b)[4][2], const PrefillProj& P, int ncol0, int slab,
+                                       int lj, int lg) {
   const int rowbytes = P.k >> 2;
 #pragma unroll
-  for (int nf = 0; nf < 4; ++nf) {
-    const int row = min(n0 + 16 * nf + ln, P.n - 1);
-    f.b[nf] = load_w16<MODE>(P.packed + (int64_t)row * rowbytes, slab * 64 + 16 * lg, rowbytes);
-  }
-#pragma unroll
-  for (int mf = 0; mf < 4; ++mf) {
-    const int8_t* ap = P.q + (int64_t)(m0 + 16 * mf + ln) * P.ldq + slab * 256 + 64 * lg;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) f.a[mf][j] = *reinterpret_cast<const v4i*>(ap + 16 * j);
+  for (int f = 0; f < 4; ++f) {
+    const int row = min(ncol0 + 32 * f + lj, P.n - 1);
+    const uint8_t* rp = P.packed + (int64_t)row * rowbytes;
+    const int off = slab * 64 + 32 * lg;
+    b[f][0] = load_w16<MODE>(rp, off, rowbytes);
+    b[f][1] = load_w16<MODE>(rp, off + 16, rowbytes);
   }
 }
 
-__device__ __forceinline__ void mma_slab(v4i (&acc)[4][4], const Frags& f) {
+__device__ __forceinline__ void load_a(v4i (&st)[kStageChunks], const PrefillProj& P, int m0,
+                                       int slab) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int i = 0; i < kStageChunks; ++i) {
+    const int id = threadIdx.x + kThreads * i;
+    const int r = id >> 4, c = id & 15;
+    st[i] = *G(reinterpret_cast<const v4i*>(P.q + (int64_t)(m0 + r) * P.ldq + slab * 256 + 16 * c));
+  }
+}
+
+__device__ __forceinline__ void store_a(int8_t* __restrict__ buf, const v4i (&st)[kStageChunks]) {
 #pragma unroll
-    for (int nf = 0; nf < 4; ++nf) {
-      const v4i bj = decode16((uint32_t)f.b[nf][j]);
+  for (int i = 0; i < kStageChunks; ++i) {
+    const int id = threadIdx.x + kThreads * i;
+    const int r = id >> 4, c = id & 15;
+    *reinterpret_cast<v4i*>(buf + r * 256 + 16 * (c ^ (r & 15))) = st[i];
+  }
+}
+
+// Tile of workgroup `l` of a projection, by XCD.  Workgroups go to the 8
+// XCDs round-robin (l % 8, each projection's range starts at a multiple of
+// 8) and every XCD has its own L2, so each XCD gets one contiguous share of
+// the tiles: when the M-tile count is a multiple of 8, a share is whole
+// M-tiles walked N-outer (its activation rows stay in its L2 and
+// neighbouring workgroups reuse each weight tile); otherwise a share is a
+// contiguous range of N-tiles (its weights are read by no other XCD).
+// Returns false for padding workgroups.
+__device__ __forceinline__ bool tile_of(int l, int tiles_m, int tiles_n, int* tm, int* tn) {
+  const int T = tiles_m * tiles_n;
+  const int chunk = (T + 7) >> 3;
+  const int x = l & 7, w = l >> 3;
+  if (w >= chunk) return false;
+  if ((tiles_m & 7) == 0) {
+    const int mt = tiles_m >> 3;
+    *tm = x * mt + w % mt;
+    *tn = w / mt;
+    return true;
+  }
+  const int L = x * chunk + w;
+  if (L >= T) return false;
+  *tm = L % tiles_m;
+  *tn = L / tiles_m;
+  return true;
+}
+
+// Register-staged variant (weight rows not 16-byte aligned): activation codes
+// through a double-buffered LDS tile, weights straight to registers.
+template <int MODE>
+__global__ __launch_bounds__(kThreads) void prefill_reg_kernel(const PrefillArgs A) {
+  __shared__ __align__(16) int8_t abuf[2][BM * 256];
+  int pi = 0;
 #pragma unroll
-      for (int mf = 0; mf < 4; ++mf) acc[mf][nf] = mfma_16x16x64_i8(f.a[mf][j], bj, acc[mf][nf]);
+  for (int i = 1; i < kMaxProj; ++i) pi += (i < A.count && (int)blockIdx.x >= A.tile_begin[i]);
+  const PrefillProj& P = A.p[pi];
+  int tm, tn;
+  if (!tile_of((int)blockIdx.x - A.tile_begin[pi], A.tiles_m, P.tiles_n, &tm, &tn)) return;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int lj = lane & 31, lg = lane >> 5;
+  const int m0 = tm * BM;
+  const int wm0 = (wave & 1) * 64;              // wave's rows within the tile
+  const int ncol0 = tn * BN + (wave >> 1) * 128;  // wave's first output column
+  const int S = (P.k + 255) >> 8;
+  __shared__ int32_t s_qs[BM];
+  __shared__ RowDiv s_rd[BM];
+  if (tid < BM && m0 + tid < A.m) {
+    s_qs[tid] = *G(P.qsum + m0 + tid);
+    if (P.y) s_rd[tid] = row_div_setup(*G(P.x_scale + m0 + tid) * *C(P.w_scale));
+  }
+
+  v16i acc[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int f = 0; f < 4; ++f)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][f][r] = 0;
+
+  v4i st[kStageChunks];
+  v4i bcur[4][2], bnext[4][2];
+  load_a(st, P, m0, 0);
+  load_b<MODE>(bcur, P, ncol0, 0, lj, lg);
+  store_a(abuf[0], st);
+  __syncthreads();
+
+  for (int s = 0; s < S; ++s) {
+    const bool more = s + 1 < S;
+    if (more) {
+      load_a(st, P, m0, s + 1);
+      load_b<MODE>(bnext, P, ncol0, s + 1, lj, lg);
+    }
+    const int8_t* buf = abuf[s & 1];
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      // this lane's 16 codes of K-step ks: chunk 8g + ks of its rows
+      v4i a[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int r = wm0 + 32 * i + lj;
+        a[i] = *reinterpret_cast<const v4i*>(buf + r * 256 + 16 * ((8 * lg + ks) ^ (r & 15)));
+      }
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        const v4i bq = decode16((uint32_t)bcur[f][ks >> 2][ks & 3]);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) acc[i][f] = mfma_32x32x32_i8(a[i], bq, acc[i][f]);
+      }
+    }
+    if (more) store_a(abuf[(s + 1) & 1], st);
+    __syncthreads();
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      bcur[f][0] = bnext[f][0];
+      bcur[f][1] = bnext[f][1];
     }
   }
-}
 
-template <int MODE>
-__global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs A) {
-  int pi = 0;
-  while (pi + 1 < A.count && (int)blockIdx.x >= A.p[pi + 1].tile_begin) ++pi;
-  const PrefillProj& P = A.p[pi];
-  const int tl = (int)blockIdx.x - P.tile_begin;
-  const int tm = tl % A.tiles_m, tn = tl / A.tiles_m;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int ln = lane & 15, lg = lane >> 4;
-  const int m0 = tm * kPrefillBM + (wave & 1) * 64;
-  const int n0 = tn * kPrefillBN + (wave >> 1) * 64;
-  const int S = (P.k + 255) >> 8;
-
-  v4i acc[4][4];
+  // epilogue: lane holds C[8*(r/4) + 4*lg + r%4][lj] of each 32x32 tile
+  // (the loop's last barrier also published s_qs / s_rd)
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 2; ++i) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = v4i{0, 0, 0, 0};
-
-  Frags f0, f1;
-  load_frags<MODE>(f0, P, m0, n0, 0, ln, lg);
-  int s = 0;
-  for (; s + 2 <= S; s += 2) {
-    load_frags<MODE>(f1, P, m0, n0, s + 1, ln, lg);
-    mma_slab(acc, f0);
-    if (s + 2 < S) load_frags<MODE>(f0, P, m0, n0, s + 2, ln, lg);
-    mma_slab(acc, f1);
-  }
-  if (s < S) mma_slab(acc, f0);
-
-  const float ws = P.y ? P.w_scale[0] : 0.0f;
-#pragma unroll
-  for (int mf = 0; mf < 4; ++mf) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int m = m0 + 16 * mf + 4 * lg + r;
+    for (int r = 0; r < 16; ++r) {
+      const int ml = wm0 + 32 * i + 8 * (r >> 2) + 4 * lg + (r & 3);
+      const int m = m0 + ml;
       if (m >= A.m) continue;
-      const int32_t qs = P.qsum[m];
-      const float xs = P.y ? P.x_scale[m] : 0.0f;
+      const int32_t qs = s_qs[ml];
+      const RowDiv rd = s_rd[ml];
 #pragma unroll
-      for (int nf = 0; nf < 4; ++nf) {
-        const int n = n0 + 16 * nf + ln;
+      for (int f = 0; f < 4; ++f) {
+        const int n = ncol0 + 32 * f + lj;
         if (n >= P.n) continue;
-        const int32_t v = acc[mf][nf][r] - qs;
+        const int32_t v = acc[i][f][r] - qs;
         if (P.y)
-          P.y[(int64_t)m * P.n + n] = dequant_bf16(v, xs, ws);
+          *G(P.y + (int64_t)m * P.n + n) = dequant_bf16_row(v, rd);
         else
-          P.acc_out[(int64_t)m * P.n + n] = v;
+          *G(P.acc_out + (int64_t)m * P.n + n) = v;
       }
     }
   }
 }
 
+// ---------------------------------------------------------------------------
+// Main variant (16-byte aligned weight rows): both operands of a slab go
+// straight from global memory into LDS (gfx950 global_load_lds, 16 bytes
+// per lane, lane L's bytes landing at dst + 16 L), through a ring of NST
+// slab buffers: while slab s is multiplied, slabs up to s+NST-1 are in
+// flight.  No staging registers, one barrier per slab.  The tile is BM=128
+// tokens x BNT outputs; four waves of 64 x BNT/2.
+//
+// LDS image of a slab:
+//   A: 128 rows x 16 chunks of 16 B; chunk c of row r at r*16 + (c ^ (r & 15)).
+//   B: BNT columns x 4 chunks of 16 B (64 packed bytes = 256 codes); chunk c
+//      of column j at j*4 + (c ^ ((j >> 2) & 3)).
+// Both swizzles keep the lanes of one LDS read on distinct banks.
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+__device__ __forceinline__ void dma16(const void* src, int8_t* lds_dst) {
+  __builtin_amdgcn_global_load_lds((const BL_GLOBAL void*)src,
+                                   (__attribute__((address_space(3))) void*)lds_dst, 16, 0, 0);
+}
+
+template <int BNT>
+struct Cfg {
+  static constexpr int kAChunks = BM * 16;
+  static constexpr int kBChunks = BNT * 4;
+  static constexpr int kStageBytes = (kAChunks + kBChunks) * 16;
+  static constexpr int kADma = kAChunks / kThreads;
+  static constexpr int kBDma = kBChunks / kThreads;
+  static constexpr int kDma = kADma + kBDma;  // DMA instructions per thread per slab
+  static constexpr int WN = BNT / 64;         // 32-column tiles per wave
+};
+
+template <int BNT>
+__device__ __forceinline__ void issue_stage(const PrefillProj& P, int m0, int n0, int slab,
+                                            int8_t* __restrict__ st) {
+  using K = Cfg<BNT>;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int i = 0; i < K::kADma; ++i) {
+    const int blk = wave * K::kADma + i;  // 64-chunk block written by this instruction
+    const int pos = blk * 64 + lane;
+    const int r = pos >> 4, c = (pos & 15) ^ (r & 15);
+    dma16(P.q + (int64_t)(m0 + r) * P.ldq + slab * 256 + 16 * c, st + blk * 1024);
+  }
+  const int rowbytes = P.k >> 2;
+  int8_t* bst = st + K::kAChunks * 16;
+#pragma unroll
+  for (int i = 0; i < K::kBDma; ++i) {
+    const int blk = wave * K::kBDma + i;
+    const int pos = blk * 64 + lane;
+    const int j = pos >> 2, c = (pos & 3) ^ ((j >> 2) & 3);
+    const int row = min(n0 + j, P.n - 1);
+    dma16(P.packed + (int64_t)row * rowbytes + min(slab * 64 + 16 * c, rowbytes - 16),
+          bst + blk * 1024);
+  }
+}
+
+template <int BNT, int NST>
+__global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs A) {
+  using K = Cfg<BNT>;
+  constexpr int WN = K::WN;
+  extern __shared__ __align__(16) int8_t smem[];
+  int pi = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxProj; ++i) pi += (i < A.count && (int)blockIdx.x >= A.tile_begin[i]);
+  const PrefillProj& P = A.p[pi];
+  int tm, tn;
+  if (!tile_of((int)blockIdx.x - A.tile_begin[pi], A.tiles_m, P.tiles_n, &tm, &tn)) return;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int lj = lane & 31, lg = lane >> 5;
+  const int m0 = tm * BM;
+  const int n0 = tn * BNT;
+  const int wm0 = (wave & 1) * 64;             // wave's rows within the tile
+  const int wn0 = (wave >> 1) * (BNT / 2);     // wave's columns within the tile
+  const int S = (P.k + 255) >> 8;
+
+  v16i acc[2][WN];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int f = 0; f < WN; ++f)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][f][r] = 0;
+
+#pragma unroll
+  for (int p = 0; p < NST - 1; ++p)
+    if (p < S) issue_stage<BNT>(P, m0, n0, p, smem + p * K::kStageBytes);
+
+  for (int s = 0; s < S; ++s) {
+    // wait for slab s: the slabs issued after it (at most NST-2) may still fly
+    const int ahead = min(S - 1 - s, NST - 2);
+    if constexpr (NST == 3) {
+      if (ahead >= 1)
+        wait_vm<K::kDma>();
+      else
+        wait_vm<0>();
+    } else {
+      wait_vm<0>();
+    }
+    __builtin_amdgcn_s_barrier();  // every wave's slab-s data is in LDS, and
+                                   // every wave is done with slab s-1's buffer
+    if (s + NST - 1 < S)
+      issue_stage<BNT>(P, m0, n0, s + NST - 1, smem + ((s + NST - 1) % NST) * K::kStageBytes);
+    const int8_t* abuf = smem + (s % NST) * K::kStageBytes;
+    const int8_t* bbuf = abuf + K::kAChunks * 16;
+    // weight chunks of this lane: column wn0 + 32f + lj, chunks 2lg and 2lg+1
+    v4i b[WN][2];
+#pragma unroll
+    for (int f = 0; f < WN; ++f) {
+      const int j = wn0 + 32 * f + lj;
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        b[f][h] = *reinterpret_cast<const v4i*>(bbuf + 16 * (j * 4 + ((2 * lg + h) ^ ((j >> 2) & 3))));
+    }
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      v4i a[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int r = wm0 + 32 * i + lj;
+        a[i] = *reinterpret_cast<const v4i*>(abuf + 16 * (r * 16 + ((8 * lg + ks) ^ (r & 15))));
+      }
+#pragma unroll
+      for (int f = 0; f < WN; ++f) {
+        const v4i bq = decode16((uint32_t)b[f][ks >> 2][ks & 3]);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) acc[i][f] = mfma_32x32x32_i8(a[i], bq, acc[i][f]);
+      }
+    }
+  }
+
+  // epilogue: lane holds C[8*(r/4) + 4*lg + r%4][lj] of each 32x32 tile.
+  // Per-row code sums and divisors of this lane's 32 rows are fetched with
+  // all loads in flight at once; the finished values go through LDS (the
+  // stage buffers are free now) so that global stores are whole 16-byte
+  // pieces of output rows.
+  const bool bf = P.y != nullptr;
+  int32_t qs[2][4][4];
+  RowDiv rd[2][4][4];
+  int fast = 1;
+  const float ws = bf ? *C(P.w_scale) : 0.0f;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int m = min(m0 + wm0 + 32 * i + 8 * q4 + 4 * lg + e, A.m - 1);
+        qs[i][q4][e] = *G(P.qsum + m);
+        rd[i][q4][e] = row_div_setup(bf ? *G(P.x_scale + m) * ws : 1.0f);
+        fast &= rd[i][q4][e].fast;
+      }
+  const int esz = bf ? 2 : 4;
+  const int orow = BNT * esz + 16;  // LDS bytes per output row (padded)
+  // one decision per workgroup instead of one per value: every divisor in
+  // the fast range (rows past M are clamped copies of the last row)
+  const int all_fast = __syncthreads_and(fast);  // also: every wave is done with the stage buffers
+  auto put = [&](auto mode) {
+    constexpr int MODE_OUT = decltype(mode)::value;  // 0 bf16 fast, 1 bf16, 2 int32
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int ml = wm0 + 32 * i + 8 * (r >> 2) + 4 * lg + (r & 3);
+        const int32_t q = qs[i][r >> 2][r & 3];
+        const RowDiv d = rd[i][r >> 2][r & 3];
+#pragma unroll
+        for (int f = 0; f < WN; ++f) {
+          const int nl = wn0 + 32 * f + lj;
+          const int32_t v = acc[i][f][r] - q;
+          if constexpr (MODE_OUT == 0)
+            *reinterpret_cast<uint16_t*>(smem + ml * orow + 2 * nl) = dequant_bf16_fast(v, d.d, d.y);
+          else if constexpr (MODE_OUT == 1)
+            *reinterpret_cast<uint16_t*>(smem + ml * orow + 2 * nl) = dequant_bf16_row(v, d);
+          else
+            *reinterpret_cast<int32_t*>(smem + ml * orow + 4 * nl) = v;
+        }
+      }
+    }
+  };
+  if (!bf)
+    put(std::integral_constant<int, 2>{});
+  else if (all_fast)
+    put(std::integral_constant<int, 0>{});
+  else
+    put(std::integral_constant<int, 1>{});
+  __syncthreads();
+  const int chunks_row = BNT * esz / 16;  // 16-byte pieces per output row
+  const int per = 16 / esz;               // outputs per piece
+  const bool wide = (P.n % per) == 0;     // rows of the output are 16-byte aligned
+  int8_t* out = bf ? reinterpret_cast<int8_t*>(P.y) : reinterpret_cast<int8_t*>(P.acc_out);
+  for (int idx = tid; idx < BM * chunks_row; idx += kThreads) {
+    const int ml = idx / chunks_row, c = idx - ml * chunks_row;
+    const int m = m0 + ml, n = n0 + c * per;
+    if (m >= A.m || n >= P.n) continue;
+    const int8_t* src = smem + ml * orow + c * 16;
+    int8_t* dst = out + ((int64_t)m * P.n + n) * esz;
+    if (wide && n + per <= P.n) {
+      *G(reinterpret_cast<v4i*>(dst)) = *reinterpret_cast<const v4i*>(src);
+    } else {
+      for (int e = 0; e < per && n + e < P.n; ++e) {
+        if (bf)
+          *G(reinterpret_cast<uint16_t*>(dst) + e) = reinterpret_cast<const uint16_t*>(src)[e];
+        else
+          *G(reinterpret_cast<int32_t*>(dst) + e) = reinterpret_cast<const int32_t*>(src)[e];
+      }
+    }
+  }
+}
+
+// Slab buffers of the main variant.
+#ifndef BL_PREFILL_NST
+#define BL_PREFILL_NST 2
+#endif
+
 }  // namespace
 
 hipError_t launch_prefill(const PrefillArgs& a, int total_tiles, hipStream_t s) {
-  if (a.load_mode == 0)
-    prefill_kernel<0><<<(unsigned)total_tiles, kThreads, 0, s>>>(a);
-  else if (a.load_mode == 1)
-    prefill_kernel<1><<<(unsigned)total_tiles, kThreads, 0, s>>>(a);
-  else
-    prefill_kernel<2><<<(unsigned)total_tiles, kThreads, 0, s>>>(a);
+  if (a.load_mode == 0) {
+    constexpr int BNT = BL_PREFILL_BN, NST = BL_PREFILL_NST;
+    constexpr size_t stages = (size_t)NST * Cfg<BNT>::kStageBytes;
+    constexpr size_t out = (size_t)BM * (BNT * 4 + 16);  // int32 output staging
+    constexpr size_t lds = stages > out ? stages : out;
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&prefill_kernel<BNT, NST>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (attr != hipSuccess) return attr;
+    prefill_kernel<BNT, NST><<<(unsigned)total_tiles, kThreads, lds, s>>>(a);
+  } else if (a.load_mode == 1) {
+    prefill_reg_kernel<1><<<(unsigned)total_tiles, kThreads, 0, s>>>(a);
+  } else {
+    prefill_reg_kernel<2><<<(unsigned)total_tiles, kThreads, 0, s>>>(a);
+  }
   return hipGetLastError();
 }
 

@@ -217,3 +217,71 @@ def test_host_absmean_rounding_matches_oracle(absmean_exe):
         assert int(got) == oracle_mean_bits(b, count), (count, [(i, v) for i, v in enumerate(b) if v])
         if w is not None:
             assert int(got) == int(np.float32(oracle.absmean_exact(w)).view(np.uint32))
+
+
+# ------------------------------------------------- per-row division, host build
+
+ROW_DIV_SRC = r'''
+#include "row_div.hpp"
+#include <cstdio>
+#include <cstdint>
+#include <cstring>
+#include <random>
+// Compares row_div against IEEE division (correctly rounded on the host).
+static float from_bits(uint32_t u) { float f; memcpy(&f, &u, 4); return f; }
+int main() {
+  std::mt19937_64 g(12345);
+  long long checked = 0, bad = 0, corrected = 0;
+  auto check = [&](float a, const bl::RowDiv& r) {
+    float q = bl::row_div(a, r), e = a / r.d;
+    uint32_t qu, eu; memcpy(&qu, &q, 4); memcpy(&eu, &e, 4);
+    ++checked; if (qu != eu) ++bad;
+    if (a * r.y != e) ++corrected;
+  };
+  // 1. realistic divisors: activation scale 127/amax (amax from bf16) times a
+  //    weight scale 1/mean, every accumulator in [-2^16, 2^16]
+  for (int t = 0; t < 64; ++t) {
+    float amax = from_bits((uint32_t)(g() % 0x7F7Fu + 1) << 16);  // finite positive bf16
+    if (!(amax > 1e-30f && amax < 1e30f)) continue;
+    float s = 127.0f / (amax > 1e-5f ? amax : 1e-5f);
+    float mean = (float)(1e-3 + (g() % 100000) * 1e-6);
+    float ws = 1.0f / mean;
+    bl::RowDiv r = bl::row_div_setup(s * ws);
+    for (int a = -65536; a <= 65536; ++a) check((float)a, r);
+  }
+  // 2. random divisors over a wide exponent range, random accumulators < 2^24
+  for (int t = 0; t < 20000; ++t) {
+    uint32_t e = 127 - 60 + (uint32_t)(g() % 120);
+    float d = from_bits((e << 23) | (uint32_t)(g() & 0x7FFFFF));
+    bl::RowDiv r = bl::row_div_setup(d);
+    for (int j = 0; j < 1000; ++j) {
+      int32_t a = (int32_t)(g() % (1u << 25)) - (1 << 24);
+      check((float)a, r);
+    }
+  }
+  // 3. divisors near powers of two and with all-ones significands
+  for (int e = -40; e <= 40; ++e) {
+    for (uint32_t m : {0u, 1u, 0x7FFFFFu, 0x7FFFFEu, 0x400000u}) {
+      float d = from_bits(((uint32_t)(127 + e) << 23) | m);
+      bl::RowDiv r = bl::row_div_setup(d);
+      for (int a = 1; a < 200000; ++a) { check((float)a, r); check((float)-a, r); }
+    }
+  }
+  printf("%lld %lld %lld\n", checked, bad, corrected);
+  return 0;
+}
+'''
+
+
+def test_row_division_matches_ieee_division(tmp_path):
+    src = tmp_path / "row_div_check.cpp"
+    exe = tmp_path / "row_div_check"
+    src.write_text(ROW_DIV_SRC)
+    subprocess.run(["g++", "-O2", "-std=c++17", "-ffp-contract=off", "-I", CSRC, str(src),
+                    "-o", str(exe), "-lm"], check=True)
+    checked, bad, corrected = map(int, subprocess.run([str(exe)], capture_output=True, text=True,
+                                                      check=True).stdout.split())
+    assert checked > 30_000_000
+    assert bad == 0
+    # the correction step matters: a bare multiply by the reciprocal is off often
+    assert corrected > 1000
