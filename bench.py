@@ -1,10 +1,11 @@
 """Benchmark of the BitLinear forward pass on one MI355X.
 
 Default workload: decode (M=1) over the seven BitLinear projections of a
-d=2048 / ffn=8192 decoder layer -- one grouped forward per step.  The metric
-is GB/s of packed (2-bit) weights streamed, as a fraction of HBM bandwidth.
-A secondary measurement times the matrix-core prefill path (M=2048 over a
-d=2560 / ffn=6912 FFN) in int8 TOPS against the int8 MFMA peak.
+d=2048 / ffn=8192 decoder layer -- one grouped forward per step, which is one
+kernel launch (activation quantization is fused into the decode kernel).  The
+metric is GB/s of packed (2-bit) weights streamed, as a fraction of HBM
+bandwidth.  A secondary measurement times the matrix-core prefill path (M=2048
+over the d=2560 / ffn=6912 FFN) in int8 TOPS against the int8 MFMA peak.
 
 Protocol: inputs are seeded synthetic tensors resident in HBM before the
 timed region.  To measure HBM rather than the 256 MB Infinity Cache, each
@@ -12,14 +13,24 @@ step uses the next of R copies of the layer's packed weights (R copies span
 at least 1 GiB).  Steps are replayed from a captured HIP graph (one graph
 holds one pass over the R copies), so host launch overhead is not timed.
 The timed region is bracketed by torch.cuda.synchronize() and by HIP events
-recorded on the stream the kernels run on.
+recorded on the stream the kernels are launched on.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--m M]
+
+Profiling helpers (the summaries under profiles/ are written by these):
+
+    python bench.py --pmc-probe ...            eager steps + a copy kernel of known size
+    python bench.py --summarize-stats DIR      text summary of a rocprofv3 --stats run
+    python bench.py --summarize-pmc FDIR WDIR  HBM traffic per dispatch from FETCH_SIZE /
+                                               WRITE_SIZE runs, scaled by the copy kernel
 """
 
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -34,6 +45,12 @@ METRIC = "BitLinear decode GB/s of packed weights (% HBM peak); prefill int8 TOP
 HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, published
 MFMA_I8_PEAK_TOPS = 5000.0  # MI355X dense int8 matrix peak, published
 
+# Sources the decode kernel is built from; a traffic figure measured on other
+# sources is stale and is not reported.
+DECODE_SOURCES = ["decode.hip", "common.hpp", "row_div.hpp", "internal.hpp"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_kernel_decode_1b_m1_traffic.txt")
+COPY_PROBE_MIB = 512
+
 
 def parse():
     ap = argparse.ArgumentParser()
@@ -45,9 +62,24 @@ def parse():
     ap.add_argument("--rotate-bytes", type=float, default=float(1 << 30))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-context", action="store_true",
+                    help="skip the warm-cache and copy-bandwidth context numbers")
     ap.add_argument("--eager", action="store_true", help="launch steps from Python, no graph")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--pmc-probe", action="store_true",
+                    help="eager steps of the workload, then a copy kernel of known size")
+    ap.add_argument("--summarize-stats", metavar="DIR")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--command", default="", help="command line recorded in a summary")
     return ap.parse_args()
+
+
+def decode_sources_sha256() -> str:
+    h = hashlib.sha256()
+    for name in DECODE_SOURCES:
+        with open(os.path.join(ROOT, "bit_gemm_bitlinear_amd", "csrc", name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
 
 
 def dev_bf16(torch, bits, dev):
@@ -106,8 +138,9 @@ def time_steps(torch, calls, steps, warmup, eager):
     for _ in range(max(1, warmup // r)):
         g.replay()
     torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # graph replays are launched on the current stream: the events go there too
     stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     ev0.record(stream)
     for _ in range(reps):
@@ -116,6 +149,25 @@ def time_steps(torch, calls, steps, warmup, eager):
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     return t1 - t0, ev0.elapsed_time(ev1) / 1e3, reps * r
+
+
+def copy_bandwidth(torch, dev, mib=1024, reps=10):
+    """Context: a plain device copy (torch elementwise kernel), read+write bytes / time."""
+    n = mib * (1 << 20) // 4
+    a = torch.ones(n, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    for _ in range(2):
+        torch.neg(a, out=b)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(reps):
+        torch.neg(a, out=b)
+    ev1.record()
+    torch.cuda.synchronize()
+    s = ev0.elapsed_time(ev1) / 1e3 / reps
+    del a, b
+    return 2 * mib * (1 << 20) / s / 1e9
 
 
 def cpu_baseline(wls, wl, m, budget_s):
@@ -153,7 +205,7 @@ def cpu_baseline(wls, wl, m, budget_s):
         "sample": f"{passes} full pass(es) of the {wl.name} layer at M={m} "
                   f"({len(proj)} projections, {wl.packed_bytes} packed bytes each pass), "
                   f"{dt:.1f} s on host cores (numpy; BLAS threads={blas_threads}, "
-                  f"affinity={len(os.sched_getaffinity(0))})",
+                  f"affinity={len(os.sched_getaffinity(0))}, os.cpu_count={os.cpu_count()})",
     }
 
 
@@ -165,14 +217,127 @@ def prefill_measure(torch, bl, wls, dev, steps):
     tops = wl.ops(m) * n / ev_s / 1e12
     return {
         "workload": wl.name, "m": m, "value": tops, "unit": "TOPS",
+        "note": "end to end: activation quantization pass + MFMA GEMM, 3 projections",
         "ms_per_step": ev_s / n * 1e3, "ops_per_step": wl.ops(m), "steps": n,
         "roofline": {"bound": "mfma", "achieved": tops, "peak": MFMA_I8_PEAK_TOPS,
                      "unit": "TFLOP/s", "frac": tops / MFMA_I8_PEAK_TOPS, "traffic": None},
     }
 
 
+# ---------------------------------------------------------------------------
+# rocprofv3 output summaries
+
+
+def _csv_rows(pattern):
+    rows = []
+    for path in sorted(glob.glob(pattern, recursive=True)):
+        with open(path, newline="") as f:
+            rows.extend(csv.DictReader(f))
+    return rows
+
+
+def summarize_stats(d, command):
+    rows = _csv_rows(os.path.join(d, "**", "*kernel_stats.csv"))
+    if not rows:
+        sys.exit(f"no kernel_stats.csv under {d}")
+    out = ["# rocprofv3 kernel statistics", f"command: {command}", "",
+           f"{'calls':>7} {'avg_us':>9} {'min_us':>9} {'max_us':>9} {'total_%':>7}  kernel"]
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    for r in rows:
+        out.append(f"{int(r['Calls']):7d} {float(r['AverageNs'])/1e3:9.3f} "
+                   f"{float(r['MinNs'])/1e3:9.3f} {float(r['MaxNs'])/1e3:9.3f} "
+                   f"{float(r['Percentage']):7.2f}  {r['Name'][:140]}")
+    print("\n".join(out))
+
+
+def _per_kernel_counter(d, counter):
+    """Mean counter value per dispatch, by kernel name."""
+    rows = _csv_rows(os.path.join(d, "**", "*counter_collection.csv"))
+    acc = {}
+    for r in rows:
+        if r.get("Counter_Name") != counter:
+            continue
+        key = (r["Kernel_Name"], r.get("Dispatch_Id", r.get("Correlation_Id")))
+        acc[key] = acc.get(key, 0.0) + float(r["Counter_Value"])
+    by_name = {}
+    for (name, _), v in acc.items():
+        by_name.setdefault(name, []).append(v)
+    return by_name
+
+
+def summarize_pmc(fdir, wdir, command):
+    fetch = _per_kernel_counter(fdir, "FETCH_SIZE")
+    write = _per_kernel_counter(wdir, "WRITE_SIZE")
+    copy_name = next((n for n in fetch if "neg" in n.lower()), None)
+    dec_name = next((n for n in fetch if "decode_kernel" in n), None)
+    if copy_name is None or dec_name is None:
+        sys.exit(f"kernels not found: {list(fetch)[:8]}")
+    copy_bytes = COPY_PROBE_MIB * (1 << 20)
+    cf = float(np.median(fetch[copy_name]))
+    cw = float(np.median(write[copy_name]))
+    f_fac, w_fac = copy_bytes / (cf * 1024), copy_bytes / (cw * 1024)
+    df = float(np.mean(fetch[dec_name]))
+    dw = float(np.mean(write[dec_name]))
+    traffic = df * 1024 * f_fac + dw * 1024 * w_fac
+    lines = [
+        "# HBM traffic of the decode kernel (rocprofv3 PMC, one counter per run)",
+        f"command: {command}",
+        f"decode_sources_sha256: {decode_sources_sha256()}",
+        f"kernel: {dec_name[:140]}",
+        f"dispatches: {len(fetch[dec_name])} (FETCH_SIZE run), {len(write.get(dec_name, []))} (WRITE_SIZE run)",
+        f"FETCH_SIZE_KiB_per_dispatch: {df:.1f}",
+        f"WRITE_SIZE_KiB_per_dispatch: {dw:.1f}",
+        f"copy_kernel: {copy_name[:140]}",
+        f"copy_kernel_bytes_read: {copy_bytes}",
+        f"copy_kernel_bytes_written: {copy_bytes}",
+        f"copy_FETCH_SIZE_KiB: {cf:.1f}",
+        f"copy_WRITE_SIZE_KiB: {cw:.1f}",
+        f"fetch_scale: {f_fac:.4f}",
+        f"write_scale: {w_fac:.4f}",
+        f"traffic_bytes_per_dispatch: {traffic:.0f}",
+    ]
+    print("\n".join(lines))
+
+
+def read_traffic():
+    """Traffic figure of the committed PMC summary, or None if it is missing or
+    was measured on other decode-kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            kv = dict(l.split(": ", 1) for l in f.read().splitlines() if ": " in l)
+    except OSError:
+        return None
+    if kv.get("decode_sources_sha256") != decode_sources_sha256():
+        return None
+    try:
+        return float(kv["traffic_bytes_per_dispatch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def pmc_probe(torch, bl, wls, args):
+    dev = torch.device("cuda:0")
+    wl = wls.WORKLOADS[args.workload]
+    m = args.m if args.m is not None else wl.ms[0]
+    copies = max(1, int(np.ceil(args.rotate_bytes / wl.packed_bytes)))
+    calls = prepare(torch, bl, wls, wl, m, copies, dev)
+    time_steps(torch, calls, args.steps, 0, eager=True)
+    n = COPY_PROBE_MIB * (1 << 20) // 4
+    a = torch.ones(n, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        torch.neg(a, out=b)
+    torch.cuda.synchronize()
+    print(f"pmc probe: {args.steps} eager steps of {wl.name}, 3 copies of {COPY_PROBE_MIB} MiB",
+          flush=True)
+
+
 def main():
     args = parse()
+    if args.summarize_stats:
+        return summarize_stats(args.summarize_stats, args.command)
+    if args.summarize_pmc:
+        return summarize_pmc(*args.summarize_pmc, args.command)
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
               "(see the sharding notes in DESIGN.md); run with --gpus 1", file=sys.stderr)
@@ -182,6 +347,9 @@ def main():
     from bit_gemm_bitlinear_amd import bitlinear as bl
     from bit_gemm_bitlinear_amd import workloads as wls
 
+    if args.pmc_probe:
+        return pmc_probe(torch, bl, wls, args)
+
     dev = torch.device("cuda:0")
     wl = wls.WORKLOADS[args.workload]
     m = args.m if args.m is not None else wl.ms[0]
@@ -190,6 +358,7 @@ def main():
     host_s, ev_s, n = time_steps(torch, calls, args.steps, args.warmup, args.eager)
     per_step = ev_s / n
     gbs = wl.packed_bytes / per_step / 1e9
+    traffic = read_traffic() if (args.workload == "decode_1b_m1" and m == 1) else None
 
     out = {
         "metric": METRIC,
@@ -208,13 +377,27 @@ def main():
             "workload": wl.name, "m": m,
             "projections": [[p.name, p.n, p.k] for p in wl.projections],
             "packed_bytes_per_step": wl.packed_bytes,
+            "kernel_launches_per_step": 1,
             "rotated_weight_copies": copies,
             "launch": "eager" if args.eager else "hip-graph",
             "host_ms_per_step": host_s / n * 1e3,
         },
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": gbs / HBM_PEAK_GBS, "traffic": None},
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": traffic},
     }
+    if not args.no_context:
+        # the same step with one weight copy: resident in the Infinity Cache
+        w_calls = calls[:1] * len(calls)  # as many launches per graph, all on copy 0
+        _, w_s, w_n = time_steps(torch, w_calls, args.steps, args.warmup, args.eager)
+        del calls
+        out["context"] = {
+            "warm_mall_GBs": wl.packed_bytes / (w_s / w_n) / 1e9,
+            "warm_mall_note": "same step, one weight copy (16 MiB stays in the 256 MB Infinity Cache)",
+            "copy_GBs": copy_bandwidth(torch, dev),
+            "copy_note": "plain device copy of 1 GiB (read + write bytes / time), torch elementwise kernel",
+        }
+    else:
+        del calls
     if not args.no_prefill:
         out["prefill"] = prefill_measure(torch, bl, wls, dev, args.steps)
     if not args.no_cpu_baseline:

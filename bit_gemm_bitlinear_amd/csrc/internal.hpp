@@ -92,7 +92,7 @@ hipError_t launch_decode(const DecodeArgs& a, int total_wgs, size_t lds_bytes, h
 // ---- prefill contraction (prefill.hip) ----
 constexpr int kPrefillBM = 128;  // token rows per tile
 #ifndef BL_PREFILL_BN
-#define BL_PREFILL_BN 128
+#define BL_PREFILL_BN 256
 #endif
 constexpr int kPrefillBN = BL_PREFILL_BN;  // output columns per tile, 16-byte aligned weight rows
 constexpr int kPrefillRegBN = 256;  // output columns per tile, other weight rows
