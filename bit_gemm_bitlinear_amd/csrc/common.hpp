@@ -31,6 +31,17 @@ __device__ __forceinline__ const BL_CONST T* C(const T* p) {
   return (const BL_CONST T*)p;
 }
 
+// A uniform fp32 value read through the vector-memory path (a raw buffer
+// load of 4 bytes).  It retires on the vector-memory counter, in order with
+// the loads issued around it; an ordinary uniform load becomes a scalar load,
+// which retires on the counter that LDS operations share, so every LDS or
+// cross-lane wait after it would also wait for that memory round trip.
+__device__ __forceinline__ float load_f32_vmem(const float* p) {
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(p), (short)0, 4, 0x00020000);
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, 0, 0, 0));
+}
+
 // fp32(1e-5): the lower clamp of the absmax / absmean denominators.
 constexpr float kEps = 1e-5f;
 

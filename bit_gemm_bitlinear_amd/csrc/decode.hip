@@ -37,6 +37,7 @@ namespace {
 #ifndef BL_DECODE_WINDOW
 #define BL_DECODE_WINDOW 8
 #endif
+static_assert(BL_DECODE_WINDOW % 4 == 0, "ring slots hold whole tile rounds");
 
 constexpr int kThreads = 256;
 constexpr int kWindow = BL_DECODE_WINDOW;  // 16-byte weight chunks in flight per lane
@@ -105,16 +106,29 @@ __device__ __forceinline__ DecodeProj select_proj(int count, int* wl) {
   return P;
 }
 
+// Wave-wide max / sum: four DPP steps reduce each row of 16 lanes (quad
+// swaps, then rotations by 4 and 8), and the four row results are combined
+// from lanes 0, 16, 32 and 48.  Needs every lane active.  (Shuffles through
+// ds_bpermute would put six dependent LDS round trips on the path.)
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_reduce(uint32_t v, Op op) {
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));   // quad 1032
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));   // quad 2301
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x124, 0xF, 0xF, false));  // row_ror:4
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xF, 0xF, false));  // row_ror:8
+  const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+  const uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+  const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
+  const uint32_t d = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+  return op(op(a, b), op(c, d));
+}
+
 __device__ __forceinline__ uint32_t wave_max(uint32_t v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o));
-  return v;
+  return wave_reduce(v, [](uint32_t x, uint32_t y) { return max(x, y); });
 }
 
 __device__ __forceinline__ int32_t wave_sum(int32_t v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+  return (int32_t)wave_reduce((uint32_t)v, [](uint32_t x, uint32_t y) { return x + y; });
 }
 
 // Calls f(integral_constant<int, i>) for i = 0 .. N-1 (a compile-time loop).
@@ -134,7 +148,7 @@ __device__ __forceinline__ void static_for(F&& f) {
 struct Shared {
   RowDiv rd[kDecodeMaxM];     // per-row divisors x_scale * w_scale
   int32_t qs[kDecodeMaxM];    // code sums
-  uint32_t part[4][kFusedMaxM];
+  uint32_t part[4][kFusedMaxM];   // per-wave absmax
   int32_t flag;
 };
 
@@ -174,10 +188,16 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& A, const DecodePro
   v4i xin[NX];
   int units;
   if constexpr (FUSED) {
-    units = M * P.k / 8;  // 16-byte chunks of 8 bf16, row-contiguous (k % 16 == 0)
+    // thread tid owns the 16-element groups tid + kThreads * i: two 16-byte
+    // chunks each (rows are contiguous, k % 16 == 0)
+    units = M * P.k / 16;
 #pragma unroll
-    for (int i = 0; i < NX; ++i)
-      xin[i] = *G(reinterpret_cast<const v4i*>(P.x + 8 * (int64_t)min(tid + kThreads * i, units - 1)));
+    for (int i = 0; i < NX / 2; ++i) {
+      const int g = min(tid + kThreads * i, units - 1);
+      const v4i* src = reinterpret_cast<const v4i*>(P.x + 16 * (int64_t)g);
+      xin[2 * i] = *G(src);
+      xin[2 * i + 1] = *G(src + 1);
+    }
   } else {
     units = M * ns * 16;  // 16-byte code units of the staged K range
     const int upr = ns * 16;
@@ -188,7 +208,10 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& A, const DecodePro
       xin[i] = *G(reinterpret_cast<const v4i*>(P.q + (int64_t)m * P.ldq + sb * 256 + c * 16));
     }
   }
-  const float ws = P.y ? *C(P.w_scale) : 0.0f;
+  // w_scale through the vector-memory path: a scalar load would retire on
+  // the counter that LDS operations share, so the first cross-lane or LDS
+  // wait below would wait for it as well.
+  const float ws = P.y ? load_f32_vmem(P.w_scale) : 0.0f;
   if constexpr (!FUSED) {
     if (tid < M) {
       sh.qs[tid] = *G(P.qsum + tid);
@@ -200,17 +223,26 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& A, const DecodePro
   //    load every request through the fabric waits about as long as the whole
   //    weight stream, while an idle fabric answers in one round trip.
   if constexpr (FUSED) {
+    // row of each group without a division (M <= 4)
+    const int gpr = P.k >> 4;  // groups per row
+    int grow[NX / 2];
+#pragma unroll
+    for (int i = 0; i < NX / 2; ++i) {
+      const int g = tid + kThreads * i;
+      grow[i] = (g >= gpr) + (g >= 2 * gpr) + (g >= 3 * gpr);
+    }
     // per-row absmax over the bf16 magnitude bits (exact)
     uint32_t mx[kFusedMaxM] = {0, 0, 0, 0};
 #pragma unroll
-    for (int i = 0; i < NX; ++i) {
-      const int c = tid + kThreads * i;
-      if (c < units) {
-        const int m = (8 * c) / P.k;
-        const uint32_t a = max(absmax_bits4((uint32_t)xin[i].x, (uint32_t)xin[i].y),
-                               absmax_bits4((uint32_t)xin[i].z, (uint32_t)xin[i].w));
+    for (int i = 0; i < NX / 2; ++i) {
+      if (tid + kThreads * i < units) {
+        const v4i lo = xin[2 * i], hi = xin[2 * i + 1];
+        const uint32_t a = max(max(absmax_bits4((uint32_t)lo.x, (uint32_t)lo.y),
+                                   absmax_bits4((uint32_t)lo.z, (uint32_t)lo.w)),
+                               max(absmax_bits4((uint32_t)hi.x, (uint32_t)hi.y),
+                                   absmax_bits4((uint32_t)hi.z, (uint32_t)hi.w)));
 #pragma unroll
-        for (int r = 0; r < kFusedMaxM; ++r) mx[r] = (m == r) ? max(mx[r], a) : mx[r];
+        for (int r = 0; r < kFusedMaxM; ++r) mx[r] = (grow[i] == r) ? max(mx[r], a) : mx[r];
       }
     }
 #pragma unroll
@@ -220,10 +252,12 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& A, const DecodePro
         if (lane == 0) sh.part[wave][r] = v;
       }
     }
+    if (tid < M) sh.qs[tid] = 0;
     // zero the padding codes [k, 256*S) of every row meanwhile
     const int pad0 = P.k, padg = (S * 256 - P.k) / 16;  // k % 16 == 0
     for (int i = tid; i < M * padg; i += kThreads) {
-      const int m = i / padg, c = i - m * padg;
+      const int m = i >= padg ? (i >= 2 * padg ? (i >= 3 * padg ? 3 : 2) : 1) : 0;
+      const int c = i - m * padg;
       *reinterpret_cast<v4i*>(lds + m * lrow + pad0 + 16 * c) = v4i{0, 0, 0, 0};
     }
     __syncthreads();
@@ -233,51 +267,52 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& A, const DecodePro
       const uint32_t a = max(max(sh.part[0][r], sh.part[1][r]), max(sh.part[2][r], sh.part[3][r]));
       s[r] = act_scale(bf16_to_f32(a));
     }
-    __syncthreads();  // sh.part is reused for the code sums
-    // quantize: chunk c holds codes 8c..8c+7 of the flattened rows; inside
-    // the 16-group g = k/16, element 4b + a goes to byte 4a + b
+    // quantize a group: q = clamp(rint(x * s)), stored as q + 128 by the
+    // unsigned byte conversion (exact: q + 128 is an integer in [0, 255])
+    // and flipped back to two's complement with one xor per dword.  Element
+    // 4b + a of the group goes to byte 4a + b (the weight decode's order).
     int32_t sum[kFusedMaxM] = {0, 0, 0, 0};
 #pragma unroll
-    for (int i = 0; i < NX; ++i) {
-      const int c = tid + kThreads * i;
-      if (c < units) {
-        const int m = (8 * c) / P.k;
-        const int k0 = 8 * c - m * P.k;
+    for (int i = 0; i < NX / 2; ++i) {
+      const int g = tid + kThreads * i;
+      if (g < units) {
+        const int m = grow[i];
         float sc = s[0];
 #pragma unroll
         for (int r = 1; r < kFusedMaxM; ++r) sc = (m == r) ? s[r] : sc;
-        int32_t code[8];
-        const uint32_t w4[4] = {(uint32_t)xin[i].x, (uint32_t)xin[i].y, (uint32_t)xin[i].z,
-                                (uint32_t)xin[i].w};
-        int32_t part = 0;
+        const uint32_t w[8] = {(uint32_t)xin[2 * i].x, (uint32_t)xin[2 * i].y,
+                               (uint32_t)xin[2 * i].z, (uint32_t)xin[2 * i].w,
+                               (uint32_t)xin[2 * i + 1].x, (uint32_t)xin[2 * i + 1].y,
+                               (uint32_t)xin[2 * i + 1].z, (uint32_t)xin[2 * i + 1].w};
+        uint32_t d[4] = {0, 0, 0, 0};
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t b16 = (e & 1) ? (w4[e >> 1] >> 16) : (w4[e >> 1] & 0xFFFFu);
-          code[e] = quant_i8(bf16_to_f32(b16), sc);
-          part += code[e];
+        for (int e = 0; e < 16; ++e) {
+          const uint32_t bits = (e & 1) ? (w[e >> 1] & 0xFFFF0000u) : (w[e >> 1] << 16);
+          float t = __uint_as_float(bits) * sc;
+          t = fminf(fmaxf(rintf(t), -128.0f), 127.0f) + 128.0f;
+          d[e & 3] = __builtin_amdgcn_cvt_pk_u8_f32(t, (uint32_t)(e >> 2), d[e & 3]);
         }
+        uint32_t su = 0;
+#pragma unroll
+        for (int a = 0; a < 4; ++a) su = __builtin_amdgcn_sad_u8(d[a], 0u, su);
+        const int32_t part = (int32_t)su - 128 * 16;
 #pragma unroll
         for (int r = 0; r < kFusedMaxM; ++r) sum[r] += (m == r) ? part : 0;
-        // k0 = 16g + 8h: element e of the chunk is 4(2h + e/4) + e%4 of the group
-        int8_t* dst = lds + m * lrow + (k0 & ~15) + 2 * ((k0 >> 3) & 1);
-#pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          const uint32_t pair = ((uint32_t)code[a] & 0xFFu) | (((uint32_t)code[4 + a] & 0xFFu) << 8);
-          *reinterpret_cast<uint16_t*>(dst + 4 * a) = (uint16_t)pair;
-        }
+        const int k0 = 16 * (g - m * gpr);
+        *reinterpret_cast<v4i*>(lds + m * lrow + k0) =
+            v4i{(int32_t)(d[0] ^ 0x80808080u), (int32_t)(d[1] ^ 0x80808080u),
+                (int32_t)(d[2] ^ 0x80808080u), (int32_t)(d[3] ^ 0x80808080u)};
       }
     }
 #pragma unroll
     for (int r = 0; r < kFusedMaxM; ++r) {
       if (r < M) {
         const int32_t v = wave_sum(sum[r]);
-        if (lane == 0) sh.part[wave][r] = (uint32_t)v;
+        if (lane == 0) atomicAdd(&sh.qs[r], v);  // zeroed before the first barrier
       }
       if (tid == r && r < M && P.y) sh.rd[r] = row_div_setup(s[r] * ws);
     }
     __syncthreads();
-    if (tid < M)
-      sh.qs[tid] = (int32_t)(sh.part[0][tid] + sh.part[1][tid] + sh.part[2][tid] + sh.part[3][tid]);
   } else {
     const int upr = ns * 16;
 #pragma unroll
