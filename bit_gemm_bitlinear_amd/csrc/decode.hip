@@ -437,19 +437,36 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& A, const DecodePro
   if (P.ksplit == 1) return;
 
   // K split across WGs (never with fused quantization): the last WG of the
-  // row group finishes (integer addition, so the arrival order does not matter).
-  __threadfence();
+  // row group finishes (integer addition, so the arrival order does not
+  // matter).  The partial sums above are device-scope atomics; once every
+  // thread has seen its own acknowledged (memory counter at zero) and the
+  // workgroup has met, the counter increment is ordered after all of them,
+  // and the last WG reads the sums back with atomics as well.  No cache
+  // write-back fence is needed for data that only atomics touch.
+  if constexpr (FUSED) return;  // fused quantization never splits K across WGs
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (tid == 0) sh.flag = (atomicAdd(P.count + group, 1u) == (uint32_t)(P.ksplit - 1));
   __syncthreads();
   if (!sh.flag) return;
-  __threadfence();
-  for (int idx = tid; idx < nout; idx += kThreads) {
-    const int g = idx / grp, rem = idx - g * grp;
-    const int t = rem / (M * 16), rem2 = rem - t * M * 16, m = rem2 >> 4, c = rem2 & 15;
-    const int n = group * rows_wg + g * TWW * 16 + 16 * t + c;
-    if (n >= P.n) continue;
-    store_out(P, m, n, atomicAdd(P.part + (int64_t)m * P.n + n, 0), sh, ws);
+  // read-backs four at a time, all four in flight together
+  for (int base = tid; base < nout; base += 4 * kThreads) {
+    int32_t vals[4];
+    int outm[4], outn[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int idx = base + kThreads * i;
+      const int g = idx / grp, rem = idx - g * grp;
+      const int t = rem / (M * 16), rem2 = rem - t * M * 16;
+      outm[i] = rem2 >> 4;
+      outn[i] = group * rows_wg + g * TWW * 16 + 16 * t + (rem2 & 15);
+      vals[i] = (idx < nout && outn[i] < P.n)
+                    ? atomicAdd(P.part + (int64_t)outm[i] * P.n + outn[i], 0)
+                    : 0;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (base + kThreads * i < nout && outn[i] < P.n) store_out(P, outm[i], outn[i], vals[i], sh, ws);
   }
 }
 
