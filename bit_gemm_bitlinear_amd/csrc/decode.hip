@@ -39,11 +39,10 @@ namespace {
 #endif
 static_assert(BL_DECODE_WINDOW % 4 == 0, "ring slots hold whole tile rounds");
 
-constexpr int kThreads = 256;
 constexpr int kWindow = BL_DECODE_WINDOW;  // 16-byte weight chunks in flight per lane
 constexpr int kWaveChunks = 16;            // target chunks streamed per wave
 constexpr int kWaveMaxChunks = 24;         // most chunks one wave streams
-constexpr int kStageUnits = kDecodeLdsA / 16 / kThreads;  // 16-byte code units per thread
+constexpr int kStageUnits = kDecodeLdsA / 16 / 256;  // 16-byte code units per activation thread
 
 // 16 bytes of a packed row at byte offset `off` (a multiple of 16).  Parts
 // past `rowbytes` read the row's last bytes instead (multiplied by zero).
@@ -145,55 +144,70 @@ __device__ __forceinline__ void static_for(F&& f) {
 }
 
 // Per-WG scalars shared by the prologue and the epilogue.
+// Per-WG scalars shared by the activation side and the epilogue.
 struct Shared {
-  RowDiv rd[kDecodeMaxM];     // per-row divisors x_scale * w_scale
-  int32_t qs[kDecodeMaxM];    // code sums
-  uint32_t part[4][kFusedMaxM];   // per-wave absmax
+  RowDiv rd[kDecodeMaxM];        // per-row divisors x_scale * w_scale
+  int32_t qs[kDecodeMaxM];       // code sums
+  uint32_t part[4][kFusedMaxM];  // per-wave absmax
   int32_t flag;
+  // split shape: LDS handshakes between the two wave roles
+  int32_t x_issued;    // activation waves whose loads are issued
+  int32_t amax_count;  // activation waves that posted their absmax
+  int32_t ready;       // activation waves done with codes and scalars
 };
+
+// Waits until *c reaches `target` (other waves of this workgroup add to it).
+// Only LDS is involved, so a waiting wave's outstanding weight loads are left
+// alone.  The bound only guarantees an exit.
+__device__ __forceinline__ void lds_wait(const int32_t* c, int target) {
+  for (int it = 0; it < (1 << 24); ++it) {
+    if (__hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= target) break;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Publishes this wave's LDS writes, then adds one to *c.
+__device__ __forceinline__ void lds_post(int32_t* c) {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  if ((threadIdx.x & 63) == 0) __hip_atomic_fetch_add(c, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
 
 // Writes one output (bf16, or the int32 accumulator for inspection).
 __device__ __forceinline__ void store_out(const DecodeProj& P, int m, int n, int32_t acc,
-                                          const Shared& sh, float ws) {
-  (void)ws;
+                                          const Shared& sh) {
   if (P.y)
     *G(P.y + (int64_t)m * P.n + n) = dequant_bf16_row(acc - sh.qs[m], sh.rd[m]);
   else
     *G(P.acc_out + (int64_t)m * P.n + n) = acc - sh.qs[m];
 }
 
-template <int TWW, int MODE, bool FUSED>
-__device__ __forceinline__ void decode_body(const DecodeArgs& A, const DecodeProj& P, int wl,
-                                            int8_t* __restrict__ lds, Shared& sh) {
+// The activation side, run by 256 threads (xt = 0..255, four waves): the
+// activation codes of the WG's K range go to LDS, plus the per-row code sums
+// and divisors.  Fused: quantize the bf16 rows (activation_norm_quant: exact
+// integer absmax over the bf16 magnitude bits, one fp32 division per row,
+// one multiply and round per code).  Otherwise: stage the codes act_quant.hip
+// prepared.  The four waves meet through barriers (single shape) or LDS
+// counters (split shape, where the streaming waves must not wait with them).
+template <bool SPLIT, bool FUSED>
+__device__ __forceinline__ void prepare_codes(const DecodeArgs& A, const DecodeProj& P, int sb,
+                                              int ns, int8_t* __restrict__ lds, Shared& sh) {
+  constexpr int NA = 256;  // activation threads
   const int M = A.m;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int ln = lane & 15, lg = lane >> 4;
-  // WG -> (row group, K part); wave -> (row wave wr, K wave wk_i)
-  const int group = wl / P.ksplit, kpart = wl - group * P.ksplit;
-  const int wr = wave / P.wk, wki = wave - wr * P.wk;
-  const int rows_wg = (4 / P.wk) * TWW * 16;
-  const int row0 = group * rows_wg + wr * TWW * 16;
-  const int S = (P.k + 255) >> 8;
-  const int sb = kpart * P.kspw;
-  const int ns = min(S, sb + P.kspw) - sb;  // slabs of this WG
-  const int nsw = (ns + P.wk - 1) / P.wk;   // slabs per wave
-  const int ws0 = min(ns, wki * nsw);       // first slab of this wave (relative)
-  const int nw = min(ns, ws0 + nsw) - ws0;  // slabs of this wave (may be 0)
-  const int rowbytes = P.k >> 2;
+  const int xt = threadIdx.x & (NA - 1);
+  const int lane = xt & 63, xw = xt >> 6;
   const int lrow = A.lds_row;
-
-  // 1. activations (bf16 rows, or codes staged by act_quant.hip)
+  const int S = (P.k + 255) >> 8;
   constexpr int NX = FUSED ? kFusedChunks : kStageUnits;
   v4i xin[NX];
   int units;
   if constexpr (FUSED) {
-    // thread tid owns the 16-element groups tid + kThreads * i: two 16-byte
-    // chunks each (rows are contiguous, k % 16 == 0)
+    // thread xt owns the 16-element groups xt + NA * i: two 16-byte chunks
+    // each (rows are contiguous, k % 16 == 0)
     units = M * P.k / 16;
 #pragma unroll
     for (int i = 0; i < NX / 2; ++i) {
-      const int g = min(tid + kThreads * i, units - 1);
+      const int g = min(xt + NA * i, units - 1);
       const v4i* src = reinterpret_cast<const v4i*>(P.x + 16 * (int64_t)g);
       xin[2 * i] = *G(src);
       xin[2 * i + 1] = *G(src + 1);
@@ -203,7 +217,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& A, const DecodePro
     const int upr = ns * 16;
 #pragma unroll
     for (int i = 0; i < NX; ++i) {
-      const int u = min(tid + kThreads * i, units - 1);
+      const int u = min(xt + NA * i, units - 1);
       const int m = u / upr, c = u - m * upr;
       xin[i] = *G(reinterpret_cast<const v4i*>(P.q + (int64_t)m * P.ldq + sb * 256 + c * 16));
     }
@@ -212,30 +226,38 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& A, const DecodePro
   // the counter that LDS operations share, so the first cross-lane or LDS
   // wait below would wait for it as well.
   const float ws = P.y ? load_f32_vmem(P.w_scale) : 0.0f;
-  if constexpr (!FUSED) {
-    if (tid < M) {
-      sh.qs[tid] = *G(P.qsum + tid);
-      if (P.y) sh.rd[tid] = row_div_setup(*G(P.x_scale + tid) * ws);
-    }
+  if constexpr (SPLIT) {
+    __builtin_amdgcn_sched_barrier(0);
+    lds_post(&sh.x_issued);  // the streaming waves queue their loads behind these
   }
-
-  // 2. activation codes -> LDS, before any weight request: under a full HBM
-  //    load every request through the fabric waits about as long as the whole
-  //    weight stream, while an idle fabric answers in one round trip.
-  if constexpr (FUSED) {
+  if constexpr (!FUSED) {
+    if (xt < M) {
+      sh.qs[xt] = *G(P.qsum + xt);
+      if (P.y) sh.rd[xt] = row_div_setup(*G(P.x_scale + xt) * ws);
+    }
+    const int upr = ns * 16;
+#pragma unroll
+    for (int i = 0; i < NX; ++i) {
+      const int u = xt + NA * i;
+      if (u < units) {
+        const int m = u / upr, c = u - m * upr;
+        *reinterpret_cast<v4i*>(lds + m * lrow + c * 16) = xin[i];
+      }
+    }
+  } else {
     // row of each group without a division (M <= 4)
     const int gpr = P.k >> 4;  // groups per row
     int grow[NX / 2];
 #pragma unroll
     for (int i = 0; i < NX / 2; ++i) {
-      const int g = tid + kThreads * i;
+      const int g = xt + NA * i;
       grow[i] = (g >= gpr) + (g >= 2 * gpr) + (g >= 3 * gpr);
     }
     // per-row absmax over the bf16 magnitude bits (exact)
     uint32_t mx[kFusedMaxM] = {0, 0, 0, 0};
 #pragma unroll
     for (int i = 0; i < NX / 2; ++i) {
-      if (tid + kThreads * i < units) {
+      if (xt + NA * i < units) {
         const v4i lo = xin[2 * i], hi = xin[2 * i + 1];
         const uint32_t a = max(max(absmax_bits4((uint32_t)lo.x, (uint32_t)lo.y),
                                    absmax_bits4((uint32_t)lo.z, (uint32_t)lo.w)),
@@ -249,18 +271,22 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& A, const DecodePro
     for (int r = 0; r < kFusedMaxM; ++r) {
       if (r < M) {
         const uint32_t v = wave_max(mx[r]);
-        if (lane == 0) sh.part[wave][r] = v;
+        if (lane == 0) sh.part[xw][r] = v;
       }
     }
-    if (tid < M) sh.qs[tid] = 0;
+    if (xt < M) sh.qs[xt] = 0;
+    if constexpr (SPLIT) lds_post(&sh.amax_count);
     // zero the padding codes [k, 256*S) of every row meanwhile
     const int pad0 = P.k, padg = (S * 256 - P.k) / 16;  // k % 16 == 0
-    for (int i = tid; i < M * padg; i += kThreads) {
+    for (int i = xt; i < M * padg; i += NA) {
       const int m = i >= padg ? (i >= 2 * padg ? (i >= 3 * padg ? 3 : 2) : 1) : 0;
       const int c = i - m * padg;
       *reinterpret_cast<v4i*>(lds + m * lrow + pad0 + 16 * c) = v4i{0, 0, 0, 0};
     }
-    __syncthreads();
+    if constexpr (SPLIT)
+      lds_wait(&sh.amax_count, 4);
+    else
+      __syncthreads();
     float s[kFusedMaxM];
 #pragma unroll
     for (int r = 0; r < kFusedMaxM; ++r) {
@@ -274,7 +300,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& A, const DecodePro
     int32_t sum[kFusedMaxM] = {0, 0, 0, 0};
 #pragma unroll
     for (int i = 0; i < NX / 2; ++i) {
-      const int g = tid + kThreads * i;
+      const int g = xt + NA * i;
       if (g < units) {
         const int m = grow[i];
         float sc = s[0];
@@ -308,32 +334,53 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& A, const DecodePro
     for (int r = 0; r < kFusedMaxM; ++r) {
       if (r < M) {
         const int32_t v = wave_sum(sum[r]);
-        if (lane == 0) atomicAdd(&sh.qs[r], v);  // zeroed before the first barrier
+        if (lane == 0) atomicAdd(&sh.qs[r], v);  // zeroed before the absmax meeting
       }
-      if (tid == r && r < M && P.y) sh.rd[r] = row_div_setup(s[r] * ws);
+      if (xt == r && r < M && P.y) sh.rd[r] = row_div_setup(s[r] * ws);
     }
-    __syncthreads();
-  } else {
-    const int upr = ns * 16;
-#pragma unroll
-    for (int i = 0; i < NX; ++i) {
-      const int u = tid + kThreads * i;
-      if (u < units) {
-        const int m = u / upr, c = u - m * upr;
-        *reinterpret_cast<v4i*>(lds + m * lrow + c * 16) = xin[i];
-      }
-    }
-    __syncthreads();
   }
-  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (SPLIT)
+    lds_post(&sh.ready);
+  else
+    __syncthreads();
+}
 
-  // 3. weights: this wave streams its TWW row tiles over its K slabs through a
-  //    ring of kWindow 16-byte chunks per lane (chunk = 64 weights of one row
-  //    = four K-steps), slab-major so each A fragment feeds TWW tiles.  Every
-  //    load is unconditional (past the end it repeats the last chunk, a cache
-  //    hit that is never used), so the memory-counter waits are exact.
-  constexpr int W = kWindow;
-  static_assert(W % TWW == 0, "a ring slot always holds the same row tile");
+// Consumes one 16-byte weight chunk (64 weights of one row, four K-steps of
+// the 16x16x64 int8 matrix-core op), expanded in registers to codes
+// c = u + 1 (common.hpp).
+__device__ __forceinline__ void mma_chunk(v4i& acc, const v4i (&a)[4], const v4i b) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) acc = mfma_16x16x64_i8(a[j], decode16((uint32_t)b[j]), acc);
+}
+
+template <int TWW, int MODE, bool FUSED, bool SPLIT>
+__device__ __forceinline__ void decode_body(const DecodeArgs& A, const DecodeProj& P, int wl,
+                                            int8_t* __restrict__ lds, Shared& sh) {
+  constexpr int NT = SPLIT ? 512 : 256;
+  const int M = A.m;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int ln = lane & 15, lg = lane >> 4;
+  const bool streamer = tid < 256;  // waves 0-3 stream weights and hold the sums
+  const int sw = wave & 3;
+  // WG -> (row group, K part); streaming wave -> (row wave wr, K wave wk_i)
+  const int group = wl / P.ksplit, kpart = wl - group * P.ksplit;
+  const int wr = sw / P.wk, wki = sw - wr * P.wk;
+  const int rows_wg = (4 / P.wk) * TWW * 16;
+  const int row0 = group * rows_wg + wr * TWW * 16;
+  const int S = (P.k + 255) >> 8;
+  const int sb = kpart * P.kspw;
+  const int ns = min(S, sb + P.kspw) - sb;  // slabs of this WG
+  const int nsw = (ns + P.wk - 1) / P.wk;   // slabs per wave
+  const int ws0 = min(ns, wki * nsw);       // first slab of this wave (relative)
+  const int nw = min(ns, ws0 + nsw) - ws0;  // slabs of this wave (may be 0)
+  const int rowbytes = P.k >> 2;
+  const int lrow = A.lds_row;
+
+  // weights: this wave streams its TWW row tiles over its K slabs, slab-major
+  // so each A fragment feeds TWW tiles.  Every load is unconditional (past
+  // the end it repeats the last chunk, a cache hit that is never used), so
+  // the memory-counter waits are exact.
   const int NI = TWW * nw;
   const int last = max(NI - 1, 0);
   auto wload = [&](int it) {
@@ -343,86 +390,120 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& A, const DecodePro
     return load_w16<MODE>(P.packed + (int64_t)row * rowbytes, (sb + ws0 + ls) * 64 + 16 * lg,
                           rowbytes);
   };
-  v4i ring[W];
+  const bool live = ln < M;
+  const int8_t* abase = lds + (live ? ln : 0) * lrow + 64 * lg + ws0 * 256;
+  auto afrag = [&](int ls, v4i (&a)[4]) {
 #pragma unroll
-  for (int d = 0; d < W; ++d) ring[d] = wload(d);
-
+    for (int j = 0; j < 4; ++j) {
+      const v4i v = *reinterpret_cast<const v4i*>(abase + ls * 256 + 16 * j);
+      a[j] = live ? v : v4i{0, 0, 0, 0};
+    }
+  };
   v4i acc[TWW];
 #pragma unroll
   for (int t = 0; t < TWW; ++t) acc[t] = v4i{0, 0, 0, 0};
-  const bool live = ln < M;
-  const int8_t* abase = lds + (live ? ln : 0) * lrow + 64 * lg + ws0 * 256;
-  v4i a[4];
-  // One round consumes ring slots 0..W-1 (items base..base+W-1); with
-  // REFILL each slot is reloaded with the item one round ahead right after
-  // it is read.  Rounds are nested so every executed path is straight-line
-  // code: the memory-counter waits stay exact and no load is wasted.
-  auto round = [&](int base, auto refill) {
-    static_for<W>([&](auto dc) {
-      constexpr int d = decltype(dc)::value;
-      const int it = base + d;
-      const v4i b = ring[d];
-      if constexpr (decltype(refill)::value) ring[d] = wload(it + W);
-      if (it < NI) {
-        constexpr int t = d % TWW;  // base is a multiple of W, W of TWW
-        if constexpr (t == 0) {
-          const int ls = base / TWW + d / TWW;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const v4i v = *reinterpret_cast<const v4i*>(abase + ls * 256 + 16 * j);
-            a[j] = live ? v : v4i{0, 0, 0, 0};
-          }
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[t] = mfma_16x16x64_i8(a[j], decode16((uint32_t)b[j]), acc[t]);
-      }
-    });
-  };
-  using Yes = std::true_type;
-  using No = std::false_type;
-  static_assert(kWaveMaxChunks <= 3 * W, "at most three rounds");
-  if (NI <= W) {
-    round(0, No{});
-  } else {
-    round(0, Yes{});
-    if (NI <= 2 * W) {
-      round(W, No{});
+
+  if constexpr (SPLIT) {
+    // waves 4-7 prepare the codes; waves 0-3 put all of their weight loads
+    // in flight (behind the activation loads) and start on them as soon as
+    // the codes are ready.
+    if (!streamer) {
+      prepare_codes<true, FUSED>(A, P, sb, ns, lds, sh);
     } else {
-      round(W, Yes{});
-      round(2 * W, No{});
+      constexpr int NC = kWaveChunks;
+      lds_wait(&sh.x_issued, 4);
+      for (int base = 0; base < max(NI, 1); base += NC) {
+        v4i ring[NC];
+#pragma unroll
+        for (int d = 0; d < NC; ++d) ring[d] = wload(base + d);
+        __builtin_amdgcn_sched_barrier(0);
+        if (base == 0) lds_wait(&sh.ready, 4);
+        v4i a[4];
+        static_for<NC>([&](auto dc) {
+          constexpr int d = decltype(dc)::value;
+          constexpr int t = d % TWW;
+          if (base + d < NI) {
+            if constexpr (t == 0) afrag((base + d) / TWW, a);
+            mma_chunk(acc[t], a, ring[d]);
+          }
+        });
+      }
+    }
+  } else {
+    // all four waves prepare the codes, then stream through a ring of
+    // kWindow chunks (one round consumes slots 0..W-1; with REFILL each slot
+    // is reloaded one round ahead right after it is read; rounds are nested
+    // so every executed path is straight-line code)
+    prepare_codes<false, FUSED>(A, P, sb, ns, lds, sh);
+    __builtin_amdgcn_sched_barrier(0);
+    constexpr int W = kWindow;
+    static_assert(W % 4 == 0, "a ring slot always holds the same row tile");
+    v4i ring[W];
+#pragma unroll
+    for (int d = 0; d < W; ++d) ring[d] = wload(d);
+    v4i a[4];
+    auto round = [&](int base, auto refill) {
+      static_for<W>([&](auto dc) {
+        constexpr int d = decltype(dc)::value;
+        constexpr int t = d % TWW;  // base is a multiple of W, W of TWW
+        const int it = base + d;
+        const v4i b = ring[d];
+        if constexpr (decltype(refill)::value) ring[d] = wload(it + W);
+        if (it < NI) {
+          if constexpr (t == 0) afrag(it / TWW, a);
+          mma_chunk(acc[t], a, b);
+        }
+      });
+    };
+    using Yes = std::true_type;
+    using No = std::false_type;
+    static_assert(kWaveMaxChunks <= 3 * W, "at most three rounds");
+    if (NI <= W) {
+      round(0, No{});
+    } else {
+      round(0, Yes{});
+      if (NI <= 2 * W) {
+        round(W, No{});
+      } else {
+        round(W, Yes{});
+        round(2 * W, No{});
+      }
     }
   }
 
-  // 4. epilogue.  Lane (ln, lg) holds rows m = 4*lg + r of output column
-  //    row0 + 16*t + ln.
+  // epilogue.  Streaming lane (ln, lg) holds rows m = 4*lg + r of output
+  // column row0 + 16*t + ln.
   if (P.wk == 1 && P.ksplit == 1) {
+    if (!streamer) return;
 #pragma unroll
     for (int t = 0; t < TWW; ++t) {
       const int n = row0 + 16 * t + ln;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int m = 4 * lg + r;
-        if (m < M && n < P.n) store_out(P, m, n, acc[t][r], sh, ws);
+        if (m < M && n < P.n) store_out(P, m, n, acc[t][r], sh);
       }
     }
     return;
   }
-  // K split across the waves of a row group: partial sums meet in LDS
-  // (a region after the staged codes, so no barrier is needed before writing)
+  // K split across the streaming waves of a row group: partial sums meet in
+  // LDS (a region after the staged codes, so no barrier is needed before
+  // writing), then every wave of the WG finishes.
   int32_t* red = reinterpret_cast<int32_t*>(lds + M * lrow);
+  if (streamer) {
 #pragma unroll
-  for (int t = 0; t < TWW; ++t) {
+    for (int t = 0; t < TWW; ++t) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int m = 4 * lg + r;
-      if (m < M) red[((wave * TWW + t) * M + m) * 16 + ln] = acc[t][r];
+      for (int r = 0; r < 4; ++r) {
+        const int m = 4 * lg + r;
+        if (m < M) red[((sw * TWW + t) * M + m) * 16 + ln] = acc[t][r];
+      }
     }
   }
   __syncthreads();
   const int nout = (4 / P.wk) * TWW * M * 16;  // outputs of this WG
   const int grp = TWW * M * 16;                 // outputs per row wave
-  for (int idx = tid; idx < nout; idx += kThreads) {
+  for (int idx = tid; idx < nout; idx += NT) {
     const int g = idx / grp, rem = idx - g * grp;  // g = row wave
     const int t = rem / (M * 16), rem2 = rem - t * M * 16, m = rem2 >> 4, c = rem2 & 15;
     const int n = group * rows_wg + g * TWW * 16 + 16 * t + c;
@@ -430,7 +511,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& A, const DecodePro
     for (int q = 0; q < P.wk; ++q) v += red[(((g * P.wk + q) * TWW + t) * M + m) * 16 + c];
     if (n >= P.n) continue;
     if (P.ksplit == 1)
-      store_out(P, m, n, v, sh, ws);
+      store_out(P, m, n, v, sh);
     else
       atomicAdd(P.part + (int64_t)m * P.n + n, v);
   }
@@ -450,12 +531,12 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& A, const DecodePro
   __syncthreads();
   if (!sh.flag) return;
   // read-backs four at a time, all four in flight together
-  for (int base = tid; base < nout; base += 4 * kThreads) {
+  for (int base = tid; base < nout; base += 4 * NT) {
     int32_t vals[4];
     int outm[4], outn[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int idx = base + kThreads * i;
+      const int idx = base + NT * i;
       const int g = idx / grp, rem = idx - g * grp;
       const int t = rem / (M * 16), rem2 = rem - t * M * 16;
       outm[i] = rem2 >> 4;
@@ -466,32 +547,43 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& A, const DecodePro
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      if (base + kThreads * i < nout && outn[i] < P.n) store_out(P, outm[i], outn[i], vals[i], sh, ws);
+      if (base + NT * i < nout && outn[i] < P.n) store_out(P, outm[i], outn[i], vals[i], sh);
   }
 }
 
-template <int TWW, int MODE>
+template <int TWW, int MODE, bool SPLIT>
 __device__ __forceinline__ void decode_tw(const DecodeArgs& A, const DecodeProj& P, int wl,
                                           int8_t* lds, Shared& sh) {
   if constexpr (MODE == 0) {
     if (P.x) {
-      decode_body<TWW, MODE, true>(A, P, wl, lds, sh);
+      decode_body<TWW, MODE, true, SPLIT>(A, P, wl, lds, sh);
       return;
     }
   }
-  decode_body<TWW, MODE, false>(A, P, wl, lds, sh);
+  decode_body<TWW, MODE, false, SPLIT>(A, P, wl, lds, sh);
 }
 
-template <int MODE>
-__global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs A) {
+// SPLIT: 8 waves, for launches that fit on the chip in one wave of WGs (the
+// activation work of a WG then overlaps its weight stream instead of
+// preceding it); otherwise 4 waves, so that several WGs share a CU.
+template <int MODE, bool SPLIT>
+__global__ __launch_bounds__(SPLIT ? 512 : 256) void decode_kernel(const DecodeArgs A) {
   extern __shared__ __align__(16) int8_t lds[];
   __shared__ Shared sh;
+  if constexpr (SPLIT) {
+    if (threadIdx.x == 0) {
+      sh.x_issued = 0;
+      sh.amax_count = 0;
+      sh.ready = 0;
+    }
+  }
   int wl;
   const DecodeProj P = select_proj(A.count, &wl);
+  if constexpr (SPLIT) __syncthreads();  // counters are zero before anyone posts
   switch (P.tww) {
-    case 1: decode_tw<1, MODE>(A, P, wl, lds, sh); break;
-    case 2: decode_tw<2, MODE>(A, P, wl, lds, sh); break;
-    default: decode_tw<4, MODE>(A, P, wl, lds, sh); break;
+    case 1: decode_tw<1, MODE, SPLIT>(A, P, wl, lds, sh); break;
+    case 2: decode_tw<2, MODE, SPLIT>(A, P, wl, lds, sh); break;
+    default: decode_tw<4, MODE, SPLIT>(A, P, wl, lds, sh); break;
   }
 }
 
@@ -531,12 +623,25 @@ size_t decode_lds_bytes(int64_t m, int lds_row) {
 }
 
 hipError_t launch_decode(const DecodeArgs& a, int total_wgs, size_t lds_bytes, hipStream_t s) {
-  if (a.load_mode == 0)
-    decode_kernel<0><<<(unsigned)total_wgs, kThreads, lds_bytes, s>>>(a);
+  // CUs of the current device (cached per device id)
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) n = 1;
+    cus[dev] = n > 0 ? n : 1;
+  }
+  const bool split = a.load_mode == 0 && total_wgs <= cus[dev];
+  const dim3 grid((unsigned)total_wgs);
+  if (split)
+    decode_kernel<0, true><<<grid, 512, lds_bytes, s>>>(a);
+  else if (a.load_mode == 0)
+    decode_kernel<0, false><<<grid, 256, lds_bytes, s>>>(a);
   else if (a.load_mode == 1)
-    decode_kernel<1><<<(unsigned)total_wgs, kThreads, lds_bytes, s>>>(a);
+    decode_kernel<1, false><<<grid, 256, lds_bytes, s>>>(a);
   else
-    decode_kernel<2><<<(unsigned)total_wgs, kThreads, lds_bytes, s>>>(a);
+    decode_kernel<2, false><<<grid, 256, lds_bytes, s>>>(a);
   return hipGetLastError();
 }
 
