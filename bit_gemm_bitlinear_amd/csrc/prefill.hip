@@ -255,21 +255,26 @@ __device__ __forceinline__ void dma16(const void* src, int8_t* lds_dst) {
                                    (__attribute__((address_space(3))) void*)lds_dst, 16, 0, 0);
 }
 
-template <int BNT>
+template <int BNT, int WMI, int NW>
 struct Cfg {
+  static constexpr int kNT = 64 * NW;  // threads
   static constexpr int kAChunks = BM * 16;
   static constexpr int kBChunks = BNT * 4;
   static constexpr int kStageBytes = (kAChunks + kBChunks) * 16;
-  static constexpr int kADma = kAChunks / kThreads;
-  static constexpr int kBDma = kBChunks / kThreads;
-  static constexpr int kDma = kADma + kBDma;  // DMA instructions per thread per slab
-  static constexpr int WN = BNT / 64;         // 32-column tiles per wave
+  static constexpr int kADma = kAChunks / kNT;
+  static constexpr int kBDma = kBChunks / kNT;
+  static constexpr int kDma = kADma + kBDma;    // DMA instructions per thread per slab
+  static constexpr int kWavesM = BM / (32 * WMI);  // waves along the tile's rows
+  static constexpr int kWavesN = NW / kWavesM;     // waves along its columns
+  static constexpr int WNF = BNT / (32 * kWavesN);  // 32-column tiles per wave
+  static_assert(kWavesM * kWavesN == NW && WNF >= 1, "the waves cover the tile");
+  static_assert(kADma * kNT == kAChunks && kBDma * kNT == kBChunks, "whole DMA blocks");
 };
 
-template <int BNT>
+template <int BNT, int WMI, int NW>
 __device__ __forceinline__ void issue_stage(const PrefillProj& P, int m0, int n0, int slab,
                                             int8_t* __restrict__ st) {
-  using K = Cfg<BNT>;
+  using K = Cfg<BNT, WMI, NW>;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
   for (int i = 0; i < K::kADma; ++i) {
@@ -291,11 +296,17 @@ __device__ __forceinline__ void issue_stage(const PrefillProj& P, int m0, int n0
   }
 }
 
-template <int BNT, int NST>
-__global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs A) {
-  using K = Cfg<BNT>;
-  constexpr int WN = K::WN;
+// WMI = 32-row tiles per wave.  With WMI = 4 each wave covers all 128 rows of
+// the tile and its own columns, so every weight column is expanded once per
+// workgroup; with WMI = 2 two waves share (and both expand) each column.
+template <int BNT, int NST, int WMI, int NW>
+__global__ __launch_bounds__(64 * NW) void prefill_kernel(const PrefillArgs A) {
+  using K = Cfg<BNT, WMI, NW>;
+  constexpr int kNT = K::kNT;
+  constexpr int WNF = K::WNF;
   extern __shared__ __align__(16) int8_t smem[];
+  __shared__ int32_t s_qs[BM];
+  __shared__ RowDiv s_rd[BM];
   int pi = 0;
 #pragma unroll
   for (int i = 1; i < kMaxProj; ++i) pi += (i < A.count && (int)blockIdx.x >= A.tile_begin[i]);
@@ -307,21 +318,31 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs A) 
   const int lj = lane & 31, lg = lane >> 5;
   const int m0 = tm * BM;
   const int n0 = tn * BNT;
-  const int wm0 = (wave & 1) * 64;             // wave's rows within the tile
-  const int wn0 = (wave >> 1) * (BNT / 2);     // wave's columns within the tile
+  const int wm0 = (wave % K::kWavesM) * 32 * WMI;  // wave's rows within the tile
+  const int wn0 = (wave / K::kWavesM) * 32 * WNF;  // wave's columns within the tile
   const int S = (P.k + 255) >> 8;
+  const bool bf = P.y != nullptr;
 
-  v16i acc[2][WN];
+  // per-row code sums and divisors, fetched now (vector loads, retired in
+  // order ahead of the slab loads) and published by the loop's barriers
+  if (tid < BM) {
+    const int m = min(m0 + tid, A.m - 1);
+    const float ws = bf ? load_f32_vmem(P.w_scale) : 0.0f;
+    s_qs[tid] = *G(P.qsum + m);
+    s_rd[tid] = row_div_setup(bf ? *G(P.x_scale + m) * ws : 1.0f);
+  }
+
+  v16i acc[WMI][WNF];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < WMI; ++i)
 #pragma unroll
-    for (int f = 0; f < WN; ++f)
+    for (int f = 0; f < WNF; ++f)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][f][r] = 0;
 
 #pragma unroll
   for (int p = 0; p < NST - 1; ++p)
-    if (p < S) issue_stage<BNT>(P, m0, n0, p, smem + p * K::kStageBytes);
+    if (p < S) issue_stage<BNT, WMI, NW>(P, m0, n0, p, smem + p * K::kStageBytes);
 
   for (int s = 0; s < S; ++s) {
     // wait for slab s: the slabs issued after it (at most NST-2) may still fly
@@ -337,13 +358,13 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs A) 
     __builtin_amdgcn_s_barrier();  // every wave's slab-s data is in LDS, and
                                    // every wave is done with slab s-1's buffer
     if (s + NST - 1 < S)
-      issue_stage<BNT>(P, m0, n0, s + NST - 1, smem + ((s + NST - 1) % NST) * K::kStageBytes);
+      issue_stage<BNT, WMI, NW>(P, m0, n0, s + NST - 1, smem + ((s + NST - 1) % NST) * K::kStageBytes);
     const int8_t* abuf = smem + (s % NST) * K::kStageBytes;
     const int8_t* bbuf = abuf + K::kAChunks * 16;
     // weight chunks of this lane: column wn0 + 32f + lj, chunks 2lg and 2lg+1
-    v4i b[WN][2];
+    v4i b[WNF][2];
 #pragma unroll
-    for (int f = 0; f < WN; ++f) {
+    for (int f = 0; f < WNF; ++f) {
       const int j = wn0 + 32 * f + lj;
 #pragma unroll
       for (int h = 0; h < 2; ++h)
@@ -351,58 +372,41 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs A) 
     }
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-      v4i a[2];
+      v4i a[WMI];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
+      for (int i = 0; i < WMI; ++i) {
         const int r = wm0 + 32 * i + lj;
         a[i] = *reinterpret_cast<const v4i*>(abuf + 16 * (r * 16 + ((8 * lg + ks) ^ (r & 15))));
       }
 #pragma unroll
-      for (int f = 0; f < WN; ++f) {
+      for (int f = 0; f < WNF; ++f) {
         const v4i bq = decode16((uint32_t)b[f][ks >> 2][ks & 3]);
 #pragma unroll
-        for (int i = 0; i < 2; ++i) acc[i][f] = mfma_32x32x32_i8(a[i], bq, acc[i][f]);
+        for (int i = 0; i < WMI; ++i) acc[i][f] = mfma_32x32x32_i8(a[i], bq, acc[i][f]);
       }
     }
   }
 
   // epilogue: lane holds C[8*(r/4) + 4*lg + r%4][lj] of each 32x32 tile.
-  // Per-row code sums and divisors of this lane's 32 rows are fetched with
-  // all loads in flight at once; the finished values go through LDS (the
-  // stage buffers are free now) so that global stores are whole 16-byte
-  // pieces of output rows.
-  const bool bf = P.y != nullptr;
-  int32_t qs[2][4][4];
-  RowDiv rd[2][4][4];
-  int fast = 1;
-  const float ws = bf ? *C(P.w_scale) : 0.0f;
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int m = min(m0 + wm0 + 32 * i + 8 * q4 + 4 * lg + e, A.m - 1);
-        qs[i][q4][e] = *G(P.qsum + m);
-        rd[i][q4][e] = row_div_setup(bf ? *G(P.x_scale + m) * ws : 1.0f);
-        fast &= rd[i][q4][e].fast;
-      }
+  // The finished values go through LDS (the stage buffers are free now) so
+  // that global stores are whole 16-byte pieces of output rows.
   const int esz = bf ? 2 : 4;
   const int orow = BNT * esz + 16;  // LDS bytes per output row (padded)
   // one decision per workgroup instead of one per value: every divisor in
   // the fast range (rows past M are clamped copies of the last row)
-  const int all_fast = __syncthreads_and(fast);  // also: every wave is done with the stage buffers
+  const int all_fast = __syncthreads_and(tid >= BM || s_rd[tid].fast);  // also: every wave
+                                                                         // is done with the stage buffers
   auto put = [&](auto mode) {
     constexpr int MODE_OUT = decltype(mode)::value;  // 0 bf16 fast, 1 bf16, 2 int32
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < WMI; ++i) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int ml = wm0 + 32 * i + 8 * (r >> 2) + 4 * lg + (r & 3);
-        const int32_t q = qs[i][r >> 2][r & 3];
-        const RowDiv d = rd[i][r >> 2][r & 3];
+        const int32_t q = s_qs[ml];
+        const RowDiv d = s_rd[ml];
 #pragma unroll
-        for (int f = 0; f < WN; ++f) {
+        for (int f = 0; f < WNF; ++f) {
           const int nl = wn0 + 32 * f + lj;
           const int32_t v = acc[i][f][r] - q;
           if constexpr (MODE_OUT == 0)
@@ -426,7 +430,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs A) 
   const int per = 16 / esz;               // outputs per piece
   const bool wide = (P.n % per) == 0;     // rows of the output are 16-byte aligned
   int8_t* out = bf ? reinterpret_cast<int8_t*>(P.y) : reinterpret_cast<int8_t*>(P.acc_out);
-  for (int idx = tid; idx < BM * chunks_row; idx += kThreads) {
+  for (int idx = tid; idx < BM * chunks_row; idx += kNT) {
     const int ml = idx / chunks_row, c = idx - ml * chunks_row;
     const int m = m0 + ml, n = n0 + c * per;
     if (m >= A.m || n >= P.n) continue;
@@ -445,24 +449,31 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs A) 
   }
 }
 
-// Slab buffers of the main variant.
+// Slab buffers and wave layout of the main variant.
 #ifndef BL_PREFILL_NST
 #define BL_PREFILL_NST 2
+#endif
+#ifndef BL_PREFILL_WMI
+#define BL_PREFILL_WMI 2
+#endif
+#ifndef BL_PREFILL_NW
+#define BL_PREFILL_NW 8
 #endif
 
 }  // namespace
 
 hipError_t launch_prefill(const PrefillArgs& a, int total_tiles, hipStream_t s) {
   if (a.load_mode == 0) {
-    constexpr int BNT = BL_PREFILL_BN, NST = BL_PREFILL_NST;
-    constexpr size_t stages = (size_t)NST * Cfg<BNT>::kStageBytes;
+    constexpr int BNT = BL_PREFILL_BN, NST = BL_PREFILL_NST, WMI = BL_PREFILL_WMI,
+                  NW = BL_PREFILL_NW;
+    constexpr size_t stages = (size_t)NST * Cfg<BNT, WMI, NW>::kStageBytes;
     constexpr size_t out = (size_t)BM * (BNT * 4 + 16);  // int32 output staging
     constexpr size_t lds = stages > out ? stages : out;
     static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&prefill_kernel<BNT, NST>),
+        reinterpret_cast<const void*>(&prefill_kernel<BNT, NST, WMI, NW>),
         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (attr != hipSuccess) return attr;
-    prefill_kernel<BNT, NST><<<(unsigned)total_tiles, kThreads, lds, s>>>(a);
+    prefill_kernel<BNT, NST, WMI, NW><<<(unsigned)total_tiles, 64 * NW, lds, s>>>(a);
   } else if (a.load_mode == 1) {
     prefill_reg_kernel<1><<<(unsigned)total_tiles, kThreads, 0, s>>>(a);
   } else {
