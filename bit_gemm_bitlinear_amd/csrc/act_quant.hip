@@ -167,6 +167,89 @@ __global__ __launch_bounds__(kThreads) void act_quant_public_kernel(
   if (threadIdx.x == 0) x_scale[m] = s;
 }
 
+// Wave-wide max / sum by DPP steps (quad swaps, row rotations) and four
+// readlanes; every lane active.
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_reduce(uint32_t v, Op op) {
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));   // quad 1032
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));   // quad 2301
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x124, 0xF, 0xF, false));  // row_ror:4
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xF, 0xF, false));  // row_ror:8
+  const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+  const uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+  const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
+  const uint32_t d = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+  return op(op(a, b), op(c, d));
+}
+
+// Rows with k % 8 == 0 (16-byte aligned): thread t owns the 16-code groups
+// t + kThreads * b, two 16-byte loads each, all issued before any is used.
+// The codes are packed straight into the internal order with the unsigned
+// byte conversion (q + 128 is an exact integer in [0, 255]) and one xor per
+// dword; the code sum comes from byte sums.  One barrier for the absmax, one
+// for the code sum.
+__device__ __forceinline__ void quant_row_internal_fast(const uint16_t* __restrict__ xr, int k,
+                                                        int ngroups, v4i* __restrict__ qv,
+                                                        uint32_t* red, int32_t* qsum,
+                                                        float* x_scale) {
+  constexpr int NB = kBatch;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  v4i lo[NB], hi[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const int g = tid + kThreads * b;
+    const int e0 = min(16 * g, k - 8), e1 = min(16 * g + 8, k - 8);
+    lo[b] = *reinterpret_cast<const v4i*>(xr + e0);
+    hi[b] = *reinterpret_cast<const v4i*>(xr + e1);
+    if (16 * g >= k) lo[b] = v4i{0, 0, 0, 0};
+    if (16 * g + 8 >= k) hi[b] = v4i{0, 0, 0, 0};
+  }
+  uint32_t amax = 0;
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+    amax = max(amax, max(max(absmax_bits4((uint32_t)lo[b].x, (uint32_t)lo[b].y),
+                             absmax_bits4((uint32_t)lo[b].z, (uint32_t)lo[b].w)),
+                         max(absmax_bits4((uint32_t)hi[b].x, (uint32_t)hi[b].y),
+                             absmax_bits4((uint32_t)hi[b].z, (uint32_t)hi[b].w))));
+  amax = wave_reduce(amax, [](uint32_t x, uint32_t y) { return max(x, y); });
+  if (lane == 0) red[wave] = amax;
+  __syncthreads();
+  const float s = act_scale(bf16_to_f32(max(max(red[0], red[1]), max(red[2], red[3]))));
+  uint32_t usum = 0;  // sum of q + 128 over this thread's groups
+  int ng = 0;
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const int g = tid + kThreads * b;
+    if (g < ngroups) {
+      const uint32_t w[8] = {(uint32_t)lo[b].x, (uint32_t)lo[b].y, (uint32_t)lo[b].z,
+                             (uint32_t)lo[b].w, (uint32_t)hi[b].x, (uint32_t)hi[b].y,
+                             (uint32_t)hi[b].z, (uint32_t)hi[b].w};
+      uint32_t d[4] = {0, 0, 0, 0};
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const uint32_t bits = (e & 1) ? (w[e >> 1] & 0xFFFF0000u) : (w[e >> 1] << 16);
+        float t = __uint_as_float(bits) * s;
+        t = fminf(fmaxf(rintf(t), -128.0f), 127.0f) + 128.0f;
+        d[e & 3] = __builtin_amdgcn_cvt_pk_u8_f32(t, (uint32_t)(e >> 2), d[e & 3]);
+      }
+#pragma unroll
+      for (int a = 0; a < 4; ++a) usum = __builtin_amdgcn_sad_u8(d[a], 0u, usum);
+      ++ng;
+      qv[g] = v4i{(int32_t)(d[0] ^ 0x80808080u), (int32_t)(d[1] ^ 0x80808080u),
+                  (int32_t)(d[2] ^ 0x80808080u), (int32_t)(d[3] ^ 0x80808080u)};
+    }
+  }
+  int32_t sum = (int32_t)usum - 128 * 16 * ng;
+  sum = (int32_t)wave_reduce((uint32_t)sum, [](uint32_t x, uint32_t y) { return x + y; });
+  __syncthreads();  // red[] is reused
+  if (lane == 0) red[wave] = (uint32_t)sum;
+  __syncthreads();
+  if (tid == 0) {
+    *qsum = (int32_t)(red[0] + red[1] + red[2] + red[3]);
+    *x_scale = s;
+  }
+}
+
 __global__ __launch_bounds__(kThreads) void act_quant_internal_kernel(const ActQuantArgs a) {
   __shared__ uint32_t red[4];
   const int b = blockIdx.x;
@@ -190,6 +273,11 @@ __global__ __launch_bounds__(kThreads) void act_quant_internal_kernel(const ActQ
   int32_t sum = 0;
   v4i* qv = reinterpret_cast<v4i*>(qr);
   float s = 0.0f;
+  if (J.x && (J.k & 7) == 0 && J.ldq / 16 <= kThreads * kBatch) {
+    quant_row_internal_fast(J.x + (int64_t)m * J.k, J.k, J.ldq / 16, qv, red, J.qsum + m,
+                            J.x_scale + m);
+    return;
+  }
   if (J.x) {
     s = quant_row(J.x + (int64_t)m * J.k, J.k, J.ldq / 16, red,
                   [&](int g, const int32_t(&c)[16]) {
