@@ -290,8 +290,11 @@ __device__ __forceinline__ void prepare_codes(const DecodeArgs& A, const DecodeP
     float s[kFusedMaxM];
 #pragma unroll
     for (int r = 0; r < kFusedMaxM; ++r) {
-      const uint32_t a = max(max(sh.part[0][r], sh.part[1][r]), max(sh.part[2][r], sh.part[3][r]));
-      s[r] = act_scale(bf16_to_f32(a));
+      s[r] = 0.0f;
+      if (r < M) {
+        const uint32_t a = max(max(sh.part[0][r], sh.part[1][r]), max(sh.part[2][r], sh.part[3][r]));
+        s[r] = act_scale(bf16_to_f32(a));
+      }
     }
     // quantize a group: q = clamp(rint(x * s)), stored as q + 128 by the
     // unsigned byte conversion (exact: q + 128 is an integer in [0, 255])
@@ -501,12 +504,14 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& A, const DecodePro
     }
   }
   __syncthreads();
-  const int nout = (4 / P.wk) * TWW * M * 16;  // outputs of this WG
-  const int grp = TWW * M * 16;                 // outputs per row wave
+  // output idx -> row m and local column nl; rows_wg and TWW * 16 are powers
+  // of two, so the split is shifts and masks
+  const int lrw = 31 - __builtin_clz(rows_wg), ltw = 31 - __builtin_clz(TWW * 16);
+  const int nout = M << lrw;  // outputs of this WG
   for (int idx = tid; idx < nout; idx += NT) {
-    const int g = idx / grp, rem = idx - g * grp;  // g = row wave
-    const int t = rem / (M * 16), rem2 = rem - t * M * 16, m = rem2 >> 4, c = rem2 & 15;
-    const int n = group * rows_wg + g * TWW * 16 + 16 * t + c;
+    const int m = idx >> lrw, nl = idx & (rows_wg - 1);
+    const int g = nl >> ltw, t = (nl >> 4) & (TWW - 1), c = nl & 15;  // g = row wave
+    const int n = group * rows_wg + nl;
     int32_t v = 0;
     for (int q = 0; q < P.wk; ++q) v += red[(((g * P.wk + q) * TWW + t) * M + m) * 16 + c];
     if (n >= P.n) continue;
@@ -537,10 +542,8 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& A, const DecodePro
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int idx = base + NT * i;
-      const int g = idx / grp, rem = idx - g * grp;
-      const int t = rem / (M * 16), rem2 = rem - t * M * 16;
-      outm[i] = rem2 >> 4;
-      outn[i] = group * rows_wg + g * TWW * 16 + 16 * t + (rem2 & 15);
+      outm[i] = idx >> lrw;
+      outn[i] = group * rows_wg + (idx & (rows_wg - 1));
       vals[i] = (idx < nout && outn[i] < P.n)
                     ? atomicAdd(P.part + (int64_t)outm[i] * P.n + outn[i], 0)
                     : 0;
