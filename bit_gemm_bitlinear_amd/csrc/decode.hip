@@ -182,6 +182,18 @@ __device__ __forceinline__ void store_out(const DecodeProj& P, int m, int n, int
     *G(P.acc_out + (int64_t)m * P.n + n) = acc - sh.qs[m];
 }
 
+// Stores the 16 codes of group g (dword a, byte b = code 4b + a of the group)
+// into a row of the LDS code image.  Within each 32-code block (groups 2i,
+// 2i+1 = halves h) the dwords are ordered for the paired matrix-core ops of
+// mma_chunk: [a=0 of h=0, a=2 of h=0, a=0 of h=1, a=2 of h=1, a=1 of h=0,
+// a=3 of h=0, a=1 of h=1, a=3 of h=1].
+__device__ __forceinline__ void put_group(int8_t* row, int g, v4i v) {
+  int8_t* blk = row + 32 * (g >> 1) + 8 * (g & 1);
+  typedef int32_t v2i __attribute__((ext_vector_type(2)));
+  *reinterpret_cast<v2i*>(blk) = v2i{v.x, v.z};
+  *reinterpret_cast<v2i*>(blk + 16) = v2i{v.y, v.w};
+}
+
 // The activation side, run by 256 threads (xt = 0..255, four waves): the
 // activation codes of the WG's K range go to LDS, plus the per-row code sums
 // and divisors.  Fused: quantize the bf16 rows (activation_norm_quant: exact
@@ -241,7 +253,7 @@ __device__ __forceinline__ void prepare_codes(const DecodeArgs& A, const DecodeP
       const int u = xt + NA * i;
       if (u < units) {
         const int m = u / upr, c = u - m * upr;
-        *reinterpret_cast<v4i*>(lds + m * lrow + c * 16) = xin[i];
+        put_group(lds + m * lrow, c, xin[i]);
       }
     }
   } else {
@@ -281,7 +293,7 @@ __device__ __forceinline__ void prepare_codes(const DecodeArgs& A, const DecodeP
     for (int i = xt; i < M * padg; i += NA) {
       const int m = i >= padg ? (i >= 2 * padg ? (i >= 3 * padg ? 3 : 2) : 1) : 0;
       const int c = i - m * padg;
-      *reinterpret_cast<v4i*>(lds + m * lrow + pad0 + 16 * c) = v4i{0, 0, 0, 0};
+      put_group(lds + m * lrow, (pad0 >> 4) + c, v4i{0, 0, 0, 0});
     }
     if constexpr (SPLIT)
       lds_wait(&sh.amax_count, 4);
@@ -328,9 +340,9 @@ __device__ __forceinline__ void prepare_codes(const DecodeArgs& A, const DecodeP
 #pragma unroll
         for (int r = 0; r < kFusedMaxM; ++r) sum[r] += (m == r) ? part : 0;
         const int k0 = 16 * (g - m * gpr);
-        *reinterpret_cast<v4i*>(lds + m * lrow + k0) =
-            v4i{(int32_t)(d[0] ^ 0x80808080u), (int32_t)(d[1] ^ 0x80808080u),
-                (int32_t)(d[2] ^ 0x80808080u), (int32_t)(d[3] ^ 0x80808080u)};
+        put_group(lds + m * lrow, k0 >> 4,
+                  v4i{(int32_t)(d[0] ^ 0x80808080u), (int32_t)(d[1] ^ 0x80808080u),
+                      (int32_t)(d[2] ^ 0x80808080u), (int32_t)(d[3] ^ 0x80808080u)});
       }
     }
 #pragma unroll
@@ -351,9 +363,25 @@ __device__ __forceinline__ void prepare_codes(const DecodeArgs& A, const DecodeP
 // Consumes one 16-byte weight chunk (64 weights of one row, four K-steps of
 // the 16x16x64 int8 matrix-core op), expanded in registers to codes
 // c = u + 1 (common.hpp).
-__device__ __forceinline__ void mma_chunk(v4i& acc, const v4i (&a)[4], const v4i b) {
+//
+// Two matrix-core ops per pair of packed dwords p, p': one on the codes of
+// weights 4b and 4b+2 of each byte b (p & 0x03030303 and (p >> 4) &
+// 0x03030303), one on 4x the codes of weights 4b+1 and 4b+3 (the same masks
+// shifted by 2, with no shift back).  That is five bit operations per packed
+// dword instead of seven; the second accumulator holds four times its sum,
+// which is divided out exactly at the end.  The activation codes are laid out
+// in LDS to match (put_group).
+__device__ __forceinline__ void mma_chunk(v4i& acc1, v4i& acc4, const v4i (&a)[4], const v4i b) {
+  constexpr uint32_t M1 = 0x03030303u, M4 = 0x0C0C0C0Cu;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) acc = mfma_16x16x64_i8(a[j], decode16((uint32_t)b[j]), acc);
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t p0 = (uint32_t)b[2 * h], p1 = (uint32_t)b[2 * h + 1];
+    const uint32_t t0 = p0 >> 4, t1 = p1 >> 4;
+    const v4i b1 = v4i{(int32_t)(p0 & M1), (int32_t)(t0 & M1), (int32_t)(p1 & M1), (int32_t)(t1 & M1)};
+    const v4i b4 = v4i{(int32_t)(p0 & M4), (int32_t)(t0 & M4), (int32_t)(p1 & M4), (int32_t)(t1 & M4)};
+    acc1 = mfma_16x16x64_i8(a[2 * h], b1, acc1);
+    acc4 = mfma_16x16x64_i8(a[2 * h + 1], b4, acc4);
+  }
 }
 
 template <int TWW, int MODE, bool FUSED, bool SPLIT>
@@ -402,9 +430,9 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& A, const DecodePro
       a[j] = live ? v : v4i{0, 0, 0, 0};
     }
   };
-  v4i acc[TWW];
+  v4i acc[TWW], acc4[TWW];  // sums over weights 4b, 4b+2 and 4x those over 4b+1, 4b+3
 #pragma unroll
-  for (int t = 0; t < TWW; ++t) acc[t] = v4i{0, 0, 0, 0};
+  for (int t = 0; t < TWW; ++t) acc[t] = acc4[t] = v4i{0, 0, 0, 0};
 
   if constexpr (SPLIT) {
     // waves 4-7 prepare the codes; waves 0-3 put all of their weight loads
@@ -427,7 +455,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& A, const DecodePro
           constexpr int t = d % TWW;
           if (base + d < NI) {
             if constexpr (t == 0) afrag((base + d) / TWW, a);
-            mma_chunk(acc[t], a, ring[d]);
+            mma_chunk(acc[t], acc4[t], a, ring[d]);
           }
         });
       }
@@ -454,7 +482,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& A, const DecodePro
         if constexpr (decltype(refill)::value) ring[d] = wload(it + W);
         if (it < NI) {
           if constexpr (t == 0) afrag(it / TWW, a);
-          mma_chunk(acc[t], a, b);
+          mma_chunk(acc[t], acc4[t], a, b);
         }
       });
     };
@@ -473,6 +501,9 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& A, const DecodePro
       }
     }
   }
+
+#pragma unroll
+  for (int t = 0; t < TWW; ++t) acc[t] += acc4[t] >> 2;  // exact: multiples of 4
 
   // epilogue.  Streaming lane (ln, lg) holds rows m = 4*lg + r of output
   // column row0 + 16*t + ln.
