@@ -71,6 +71,8 @@ def parse():
     ap.add_argument("--summarize-stats", metavar="DIR")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--command", default="", help="command line recorded in a summary")
+    ap.add_argument("--curve", action="store_true",
+                    help="decode GB/s against weight bytes for one projection (1 MiB .. 1 GiB)")
     return ap.parse_args()
 
 
@@ -218,10 +220,36 @@ def prefill_measure(torch, bl, wls, dev, steps):
     return {
         "workload": wl.name, "m": m, "value": tops, "unit": "TOPS",
         "note": "end to end: activation quantization pass + MFMA GEMM, 3 projections",
+        "library_int8_gemm_TOPS": library_int8_gemm(torch, wl, m, dev),
+        "library_int8_gemm_note": "context: torch._int_mm (dense int8 x int8 -> int32, "
+                                  "vendor GEMM library) on the same three shapes",
         "ms_per_step": ev_s / n * 1e3, "ops_per_step": wl.ops(m), "steps": n,
         "roofline": {"bound": "mfma", "achieved": tops, "peak": MFMA_I8_PEAK_TOPS,
                      "unit": "TFLOP/s", "frac": tops / MFMA_I8_PEAK_TOPS, "traffic": None},
     }
+
+
+def library_int8_gemm(torch, wl, m, dev, reps=20):
+    """Dense int8 GEMM of the vendor library on the same shapes (context only)."""
+    try:
+        mats = []
+        for p in wl.projections:
+            a = torch.randint(-127, 128, (m, p.k), dtype=torch.int8, device=dev)
+            b = torch.randint(-1, 2, (p.k, p.n), dtype=torch.int8, device=dev)
+            mats.append((a, b))
+        for a, b in mats:
+            torch._int_mm(a, b)
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        for _ in range(reps):
+            for a, b in mats:
+                torch._int_mm(a, b)
+        ev1.record()
+        torch.cuda.synchronize()
+        return wl.ops(m) * reps / (ev0.elapsed_time(ev1) / 1e3) / 1e12
+    except Exception as e:  # pragma: no cover - depends on the installed torch
+        return f"unavailable: {type(e).__name__}"
 
 
 # ---------------------------------------------------------------------------
@@ -332,6 +360,27 @@ def pmc_probe(torch, bl, wls, args):
           flush=True)
 
 
+def bandwidth_curve(torch, bl, dev, k=4096, sizes_mib=(1, 4, 16, 64, 256, 1024)):
+    """Decode (M=1) on a single N x K projection of random packed bytes (code 3
+    included: timing only), cold: rotated over copies spanning >= 1 GiB."""
+    rows = []
+    g = torch.Generator(device="cpu").manual_seed(1)
+    x = torch.randn(1, k, generator=g).to(torch.bfloat16).to(dev)
+    ws = torch.ones(1, dtype=torch.float32, device=dev)
+    for mib in sizes_mib:
+        n = mib * (1 << 20) * 4 // k
+        copies = max(1, (1 << 30) // (mib << 20)) if mib < 1024 else 2
+        base = torch.randint(0, 256, (n, k // 4), dtype=torch.uint8, device=dev)
+        calls = [bl.GroupedCall([x], [base if c == 0 else base.clone()], [ws]) for c in range(copies)]
+        steps = max(64, min(4096, 256 * copies // max(1, mib // 16)))
+        _, ev_s, nrun = time_steps(torch, calls, steps, min(64, steps), False)
+        us = ev_s / nrun * 1e6
+        rows.append({"MiB": mib, "n": n, "k": k, "us": us, "GBs": (mib << 20) / (us * 1e-6) / 1e9})
+        del calls, base
+        torch.cuda.empty_cache()
+    return rows
+
+
 def main():
     args = parse()
     if args.summarize_stats:
@@ -349,6 +398,10 @@ def main():
 
     if args.pmc_probe:
         return pmc_probe(torch, bl, wls, args)
+    if args.curve:
+        for r in bandwidth_curve(torch, bl, torch.device("cuda:0")):
+            print(json.dumps(r), flush=True)
+        return
 
     dev = torch.device("cuda:0")
     wl = wls.WORKLOADS[args.workload]
