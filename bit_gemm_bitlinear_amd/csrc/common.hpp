@@ -64,13 +64,10 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
   return __uint_as_float(bits16 << 16);
 }
 
-// fp32 -> bf16, round to nearest even; NaN stays a quiet NaN (a select,
-// not a branch).
+// fp32 -> bf16, round to nearest even: gfx950's v_cvt_pk_bf16_f32 (one
+// instruction; NaN stays NaN).
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  const uint32_t u = __float_as_uint(f);
-  const uint32_t rounded = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-  const uint32_t quiet = (u >> 16) | 0x40u;
-  return (uint16_t)(((u & 0x7FFFFFFFu) > 0x7F800000u) ? quiet : rounded);
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
 // Per-token scale from the row's absmax: 127 / max(amax, 1e-5).
