@@ -143,7 +143,6 @@ __device__ __forceinline__ void static_for(F&& f) {
   static_for_impl<0, N>(f);
 }
 
-// Per-WG scalars shared by the prologue and the epilogue.
 // Per-WG scalars shared by the activation side and the epilogue.
 struct Shared {
   RowDiv rd[kDecodeMaxM];        // per-row divisors x_scale * w_scale
@@ -151,7 +150,6 @@ struct Shared {
   uint32_t part[4][kFusedMaxM];  // per-wave absmax
   int32_t flag;
   // split shape: LDS handshakes between the two wave roles
-  int32_t x_issued;    // activation waves whose loads are issued
   int32_t amax_count;  // activation waves that posted their absmax
   int32_t ready;       // activation waves done with codes and scalars
 };
@@ -194,38 +192,33 @@ __device__ __forceinline__ void put_group(int8_t* row, int g, v4i v) {
   *reinterpret_cast<v2i*>(blk + 16) = v2i{v.y, v.w};
 }
 
-// The activation side, run by 256 threads (xt = 0..255, four waves): the
-// activation codes of the WG's K range go to LDS, plus the per-row code sums
-// and divisors.  Fused: quantize the bf16 rows (activation_norm_quant: exact
-// integer absmax over the bf16 magnitude bits, one fp32 division per row,
-// one multiply and round per code).  Otherwise: stage the codes act_quant.hip
-// prepared.  The four waves meet through barriers (single shape) or LDS
-// counters (split shape, where the streaming waves must not wait with them).
-template <bool SPLIT, bool FUSED>
-__device__ __forceinline__ void prepare_codes(const DecodeArgs& A, const DecodeProj& P, int sb,
-                                              int ns, int8_t* __restrict__ lds, Shared& sh) {
-  constexpr int NA = 256;  // activation threads
+// The activation side is run by 256 threads (xt = 0..255, four waves).
+// load_codes issues its loads: the bf16 rows (fused quantization) or the
+// codes act_quant.hip prepared, and w_scale.
+template <bool FUSED>
+constexpr int kXChunks = FUSED ? kFusedChunks : kStageUnits;
+
+template <bool FUSED>
+__device__ __forceinline__ void load_codes(const DecodeArgs& A, const DecodeProj& P, int sb, int ns,
+                                           v4i (&xin)[kXChunks<FUSED>], float& ws) {
+  constexpr int NA = 256;
+  constexpr int NX = kXChunks<FUSED>;
   const int M = A.m;
   const int xt = threadIdx.x & (NA - 1);
-  const int lane = xt & 63, xw = xt >> 6;
-  const int lrow = A.lds_row;
-  const int S = (P.k + 255) >> 8;
-  constexpr int NX = FUSED ? kFusedChunks : kStageUnits;
-  v4i xin[NX];
-  int units;
   if constexpr (FUSED) {
     // thread xt owns the 16-element groups xt + NA * i: two 16-byte chunks
     // each (rows are contiguous, k % 16 == 0)
-    units = M * P.k / 16;
+    const int units = M * (P.k >> 4);
 #pragma unroll
     for (int i = 0; i < NX / 2; ++i) {
-      const int g = min(xt + NA * i, units - 1);
-      const v4i* src = reinterpret_cast<const v4i*>(P.x + 16 * (int64_t)g);
-      xin[2 * i] = *G(src);
-      xin[2 * i + 1] = *G(src + 1);
+      if (xt + NA * i < units) {
+        const v4i* src = reinterpret_cast<const v4i*>(P.x + 16 * (int64_t)(xt + NA * i));
+        xin[2 * i] = *G(src);
+        xin[2 * i + 1] = *G(src + 1);
+      }
     }
   } else {
-    units = M * ns * 16;  // 16-byte code units of the staged K range
+    const int units = M * ns * 16;  // 16-byte code units of the staged K range
     const int upr = ns * 16;
 #pragma unroll
     for (int i = 0; i < NX; ++i) {
@@ -237,11 +230,28 @@ __device__ __forceinline__ void prepare_codes(const DecodeArgs& A, const DecodeP
   // w_scale through the vector-memory path: a scalar load would retire on
   // the counter that LDS operations share, so the first cross-lane or LDS
   // wait below would wait for it as well.
-  const float ws = P.y ? load_f32_vmem(P.w_scale) : 0.0f;
-  if constexpr (SPLIT) {
-    __builtin_amdgcn_sched_barrier(0);
-    lds_post(&sh.x_issued);  // the streaming waves queue their loads behind these
-  }
+  ws = P.y ? load_f32_vmem(P.w_scale) : 0.0f;
+}
+
+// prepare_codes puts the activation codes of the WG's K range in LDS, plus
+// the per-row code sums and divisors.  Fused: quantize the bf16 rows
+// (activation_norm_quant: exact integer absmax over the bf16 magnitude bits,
+// one fp32 division per row, one multiply and round per code).  Otherwise:
+// stage the loaded codes.  The four waves meet through barriers (single
+// shape) or LDS counters (split shape, where the streaming waves must not
+// wait with them).
+template <bool SPLIT, bool FUSED>
+__device__ __forceinline__ void prepare_codes(const DecodeArgs& A, const DecodeProj& P, int ns,
+                                              const v4i (&xin)[kXChunks<FUSED>], const float ws,
+                                              int8_t* __restrict__ lds, Shared& sh) {
+  constexpr int NA = 256;  // activation threads
+  constexpr int NX = kXChunks<FUSED>;
+  const int M = A.m;
+  const int xt = threadIdx.x & (NA - 1);
+  const int lane = xt & 63, xw = xt >> 6;
+  const int lrow = A.lds_row;
+  const int S = (P.k + 255) >> 8;
+  const int units = FUSED ? M * (P.k >> 4) : M * ns * 16;
   if constexpr (!FUSED) {
     if (xt < M) {
       sh.qs[xt] = *G(P.qsum + xt);
@@ -308,10 +318,13 @@ __device__ __forceinline__ void prepare_codes(const DecodeArgs& A, const DecodeP
         s[r] = act_scale(bf16_to_f32(a));
       }
     }
-    // quantize a group: q = clamp(rint(x * s)), stored as q + 128 by the
-    // unsigned byte conversion (exact: q + 128 is an integer in [0, 255])
-    // and flipped back to two's complement with one xor per dword.  Element
-    // 4b + a of the group goes to byte 4a + b (the weight decode's order).
+    // quantize a group: q = rint(x * s).  |x * s| <= 127 * (1 + 2^-24)
+    // (s = RN(127 / amax), |x| <= amax), so the clamp to [-128, 127] never
+    // binds and q lies in [-127, 127].  Adding 1.5 * 2^23 to t = RN(x * s)
+    // rounds it to an integer with ties to even (the spacing of floats there
+    // is 1, and 1.5 * 2^23 is even) and leaves q in two's complement in the
+    // low byte of the sum's bits.  Element 4b + a of the group goes to byte b
+    // of dword a (the weight decode's order), gathered by byte permutes.
     int32_t sum[kFusedMaxM] = {0, 0, 0, 0};
 #pragma unroll
     for (int i = 0; i < NX / 2; ++i) {
@@ -325,24 +338,27 @@ __device__ __forceinline__ void prepare_codes(const DecodeArgs& A, const DecodeP
                                (uint32_t)xin[2 * i].z, (uint32_t)xin[2 * i].w,
                                (uint32_t)xin[2 * i + 1].x, (uint32_t)xin[2 * i + 1].y,
                                (uint32_t)xin[2 * i + 1].z, (uint32_t)xin[2 * i + 1].w};
-        uint32_t d[4] = {0, 0, 0, 0};
+        uint32_t r[16];
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const uint32_t bits = (e & 1) ? (w[e >> 1] & 0xFFFF0000u) : (w[e >> 1] << 16);
-          float t = __uint_as_float(bits) * sc;
-          t = fminf(fmaxf(rintf(t), -128.0f), 127.0f) + 128.0f;
-          d[e & 3] = __builtin_amdgcn_cvt_pk_u8_f32(t, (uint32_t)(e >> 2), d[e & 3]);
+          const float t = __uint_as_float(bits) * sc;
+          r[e] = __float_as_uint(t + 12582912.0f);
         }
-        uint32_t su = 0;
+        uint32_t d[4];
+        int32_t part = 0;
 #pragma unroll
-        for (int a = 0; a < 4; ++a) su = __builtin_amdgcn_sad_u8(d[a], 0u, su);
-        const int32_t part = (int32_t)su - 128 * 16;
+        for (int a = 0; a < 4; ++a) {
+          const uint32_t lo = __builtin_amdgcn_perm(r[a + 4], r[a], 0x0c0c0400u);
+          const uint32_t hi = __builtin_amdgcn_perm(r[a + 12], r[a + 8], 0x0c0c0400u);
+          d[a] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+          part = __builtin_amdgcn_sdot4((int32_t)d[a], 0x01010101, part, false);
+        }
 #pragma unroll
-        for (int r = 0; r < kFusedMaxM; ++r) sum[r] += (m == r) ? part : 0;
+        for (int r2 = 0; r2 < kFusedMaxM; ++r2) sum[r2] += (m == r2) ? part : 0;
         const int k0 = 16 * (g - m * gpr);
         put_group(lds + m * lrow, k0 >> 4,
-                  v4i{(int32_t)(d[0] ^ 0x80808080u), (int32_t)(d[1] ^ 0x80808080u),
-                      (int32_t)(d[2] ^ 0x80808080u), (int32_t)(d[3] ^ 0x80808080u)});
+                  v4i{(int32_t)d[0], (int32_t)d[1], (int32_t)d[2], (int32_t)d[3]});
       }
     }
 #pragma unroll
@@ -394,15 +410,17 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& A, const DecodePro
   const int ln = lane & 15, lg = lane >> 4;
   const bool streamer = tid < 256;  // waves 0-3 stream weights and hold the sums
   const int sw = wave & 3;
-  // WG -> (row group, K part); streaming wave -> (row wave wr, K wave wk_i)
-  const int group = wl / P.ksplit, kpart = wl - group * P.ksplit;
-  const int wr = sw / P.wk, wki = sw - wr * P.wk;
-  const int rows_wg = (4 / P.wk) * TWW * 16;
+  // WG -> (row group, K part); streaming wave -> (row wave wr, K wave wk_i).
+  // wk is 1, 2 or 4: shifts and masks, no divisions ahead of the first loads.
+  const int lwk = __builtin_ctz((unsigned)P.wk);
+  const int group = P.ksplit == 1 ? wl : wl / P.ksplit, kpart = wl - group * P.ksplit;
+  const int wr = sw >> lwk, wki = sw & (P.wk - 1);
+  const int rows_wg = (TWW * 64) >> lwk;
   const int row0 = group * rows_wg + wr * TWW * 16;
   const int S = (P.k + 255) >> 8;
   const int sb = kpart * P.kspw;
   const int ns = min(S, sb + P.kspw) - sb;  // slabs of this WG
-  const int nsw = (ns + P.wk - 1) / P.wk;   // slabs per wave
+  const int nsw = (ns + P.wk - 1) >> lwk;   // slabs per wave
   const int ws0 = min(ns, wki * nsw);       // first slab of this wave (relative)
   const int nw = min(ns, ws0 + nsw) - ws0;  // slabs of this wave (may be 0)
   const int rowbytes = P.k >> 2;
@@ -421,14 +439,12 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& A, const DecodePro
     return load_w16<MODE>(P.packed + (int64_t)row * rowbytes, (sb + ws0 + ls) * 64 + 16 * lg,
                           rowbytes);
   };
-  const bool live = ln < M;
-  const int8_t* abase = lds + (live ? ln : 0) * lrow + 64 * lg + ws0 * 256;
+  // token rows m >= M of the A operand repeat row 0: output rows m >= M
+  // are never stored, and rows do not mix in the product
+  const int8_t* abase = lds + (ln < M ? ln : 0) * lrow + 64 * lg + ws0 * 256;
   auto afrag = [&](int ls, v4i (&a)[4]) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const v4i v = *reinterpret_cast<const v4i*>(abase + ls * 256 + 16 * j);
-      a[j] = live ? v : v4i{0, 0, 0, 0};
-    }
+    for (int j = 0; j < 4; ++j) a[j] = *reinterpret_cast<const v4i*>(abase + ls * 256 + 16 * j);
   };
   v4i acc[TWW], acc4[TWW];  // sums over weights 4b, 4b+2 and 4x those over 4b+1, 4b+3
 #pragma unroll
@@ -436,13 +452,22 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& A, const DecodePro
 
   if constexpr (SPLIT) {
     // waves 4-7 prepare the codes; waves 0-3 put all of their weight loads
-    // in flight (behind the activation loads) and start on them as soon as
-    // the codes are ready.
+    // in flight and start on them as soon as the codes are ready.  The
+    // activation loads are issued before the workgroup's first barrier,
+    // the weight loads after it, so that the activations do not queue
+    // behind the weights.
     if (!streamer) {
-      prepare_codes<true, FUSED>(A, P, sb, ns, lds, sh);
+      v4i xin[kXChunks<FUSED>];
+      float ws;
+      load_codes<FUSED>(A, P, sb, ns, xin, ws);
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");  // counters are zero
+      prepare_codes<true, FUSED>(A, P, ns, xin, ws, lds, sh);
     } else {
       constexpr int NC = kWaveChunks;
-      lds_wait(&sh.x_issued, 4);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");  // counters zeroed
+      __builtin_amdgcn_s_barrier();
       for (int base = 0; base < max(NI, 1); base += NC) {
         v4i ring[NC];
 #pragma unroll
@@ -465,7 +490,12 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& A, const DecodePro
     // kWindow chunks (one round consumes slots 0..W-1; with REFILL each slot
     // is reloaded one round ahead right after it is read; rounds are nested
     // so every executed path is straight-line code)
-    prepare_codes<false, FUSED>(A, P, sb, ns, lds, sh);
+    {
+      v4i xin[kXChunks<FUSED>];
+      float ws;
+      load_codes<FUSED>(A, P, sb, ns, xin, ws);
+      prepare_codes<false, FUSED>(A, P, ns, xin, ws, lds, sh);
+    }
     __builtin_amdgcn_sched_barrier(0);
     constexpr int W = kWindow;
     static_assert(W % 4 == 0, "a ring slot always holds the same row tile");
@@ -606,14 +636,12 @@ __global__ __launch_bounds__(SPLIT ? 512 : 256) void decode_kernel(const DecodeA
   __shared__ Shared sh;
   if constexpr (SPLIT) {
     if (threadIdx.x == 0) {
-      sh.x_issued = 0;
       sh.amax_count = 0;
       sh.ready = 0;
     }
   }
   int wl;
   const DecodeProj P = select_proj(A.count, &wl);
-  if constexpr (SPLIT) __syncthreads();  // counters are zero before anyone posts
   switch (P.tww) {
     case 1: decode_tw<1, MODE, SPLIT>(A, P, wl, lds, sh); break;
     case 2: decode_tw<2, MODE, SPLIT>(A, P, wl, lds, sh); break;
