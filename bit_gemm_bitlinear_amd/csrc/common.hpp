@@ -113,6 +113,13 @@ __device__ __forceinline__ uint16_t dequant_bf16_fast(int32_t acc, float d, floa
   return f32_to_bf16(row_div_fast((float)acc, d, y));
 }
 
+// Two outputs converted together (one v_cvt_pk_bf16_f32): lo in bits 0-15.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2){lo, hi}, b2));
+}
+
 // Largest magnitude pattern of four bf16 values held in two dwords; the
 // bit pattern of |x| orders like |x| for finite values.
 __device__ __forceinline__ uint32_t absmax_bits4(uint32_t lo, uint32_t hi) {

@@ -296,6 +296,11 @@ __device__ __forceinline__ void issue_stage(const PrefillProj& P, int m0, int n0
   }
 }
 
+// Columns of a tile whose int32 sums are staged in LDS at once by the
+// epilogue (at most 256: 128 rows x 1040 bytes fit beside nothing else).
+template <int BNT>
+constexpr int kEpiCols = BNT < 256 ? BNT : 256;
+
 // WMI = 32-row tiles per wave.  With WMI = 4 each wave covers all 128 rows of
 // the tile and its own columns, so every weight column is expanded once per
 // workgroup; with WMI = 2 two waves share (and both expand) each column.
@@ -370,82 +375,114 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(const PrefillArgs A) {
       for (int h = 0; h < 2; ++h)
         b[f][h] = *reinterpret_cast<const v4i*>(bbuf + 16 * (j * 4 + ((2 * lg + h) ^ ((j >> 2) & 3))));
     }
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      v4i a[WMI];
+    // A fragments of step ks + 1 are read while step ks multiplies, so the
+    // LDS latency hides behind the matrix-core work
+    auto aload = [&](int ks, v4i (&a)[WMI]) {
 #pragma unroll
       for (int i = 0; i < WMI; ++i) {
         const int r = wm0 + 32 * i + lj;
         a[i] = *reinterpret_cast<const v4i*>(abuf + 16 * (r * 16 + ((8 * lg + ks) ^ (r & 15))));
       }
+    };
+    v4i a[2][WMI];
+    aload(0, a[0]);
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      if (ks < 7) aload(ks + 1, a[(ks + 1) & 1]);
 #pragma unroll
       for (int f = 0; f < WNF; ++f) {
         const v4i bq = decode16((uint32_t)b[f][ks >> 2][ks & 3]);
 #pragma unroll
-        for (int i = 0; i < WMI; ++i) acc[i][f] = mfma_32x32x32_i8(a[i], bq, acc[i][f]);
+        for (int i = 0; i < WMI; ++i) acc[i][f] = mfma_32x32x32_i8(a[ks & 1][i], bq, acc[i][f]);
       }
     }
   }
 
   // epilogue: lane holds C[8*(r/4) + 4*lg + r%4][lj] of each 32x32 tile.
-  // The finished values go through LDS (the stage buffers are free now) so
-  // that global stores are whole 16-byte pieces of output rows.
-  const int esz = bf ? 2 : 4;
-  const int orow = BNT * esz + 16;  // LDS bytes per output row (padded)
-  // one decision per workgroup instead of one per value: every divisor in
-  // the fast range (rows past M are clamped copies of the last row)
-  const int all_fast = __syncthreads_and(tid >= BM || s_rd[tid].fast);  // also: every wave
-                                                                         // is done with the stage buffers
-  auto put = [&](auto mode) {
-    constexpr int MODE_OUT = decltype(mode)::value;  // 0 bf16 fast, 1 bf16, 2 int32
+  // The raw sums go to LDS as int32 rows (the stage buffers are free once
+  // every wave is past the loop), kEpiCols columns per pass; then each
+  // thread takes one row: its code sum and divisor are read once, and 8
+  // consecutive outputs at a time are converted and stored as 16-byte
+  // (bf16) or 32-byte (int32) pieces.
+  constexpr int EC = kEpiCols<BNT>;
+  constexpr int orow = EC + 4;  // int32 words per staged row (16 bytes of padding)
+  static_assert(BNT % EC == 0 && EC % (32 * WNF) == 0, "a wave's columns lie in one pass");
+  int32_t* st = reinterpret_cast<int32_t*>(smem);
+  constexpr int TPR = kNT / BM;      // threads per row
+  constexpr int NPT = EC / 8 / TPR;  // 8-output pieces per thread and pass
+  static_assert(kNT % BM == 0 && (EC / 8) % TPR == 0, "rows split evenly over the threads");
+  const int rl = tid / TPR, m = m0 + rl;
+  const int c0 = tid % TPR;  // pieces c0, c0 + TPR, ...: a row's threads store adjacent pieces
+  const int32_t q = s_qs[rl];
+  const RowDiv d = s_rd[rl];
 #pragma unroll
-    for (int i = 0; i < WMI; ++i) {
+  for (int pass = 0; pass < BNT / EC; ++pass) {
+    __syncthreads();
+    if (wn0 / EC == pass) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int ml = wm0 + 32 * i + 8 * (r >> 2) + 4 * lg + (r & 3);
-        const int32_t q = s_qs[ml];
-        const RowDiv d = s_rd[ml];
+      for (int i = 0; i < WMI; ++i)
 #pragma unroll
-        for (int f = 0; f < WNF; ++f) {
-          const int nl = wn0 + 32 * f + lj;
-          const int32_t v = acc[i][f][r] - q;
-          if constexpr (MODE_OUT == 0)
-            *reinterpret_cast<uint16_t*>(smem + ml * orow + 2 * nl) = dequant_bf16_fast(v, d.d, d.y);
-          else if constexpr (MODE_OUT == 1)
-            *reinterpret_cast<uint16_t*>(smem + ml * orow + 2 * nl) = dequant_bf16_row(v, d);
-          else
-            *reinterpret_cast<int32_t*>(smem + ml * orow + 4 * nl) = v;
+        for (int r = 0; r < 16; ++r) {
+          const int ml = wm0 + 32 * i + 8 * (r >> 2) + 4 * lg + (r & 3);
+#pragma unroll
+          for (int f = 0; f < WNF; ++f)
+            st[ml * orow + wn0 - pass * EC + 32 * f + lj] = acc[i][f][r];
+        }
+    }
+    __syncthreads();
+    if (m >= A.m) continue;
+    const int32_t* srow = st + rl * orow + 8 * c0;
+    v4i raw[NPT][2];
+#pragma unroll
+    for (int j = 0; j < NPT; ++j) {
+      raw[j][0] = *reinterpret_cast<const v4i*>(srow + 8 * TPR * j);
+      raw[j][1] = *reinterpret_cast<const v4i*>(srow + 8 * TPR * j + 4);
+    }
+    const int nb = n0 + pass * EC + 8 * c0;  // first output column of piece 0
+    if (!bf) {
+      const bool wide = (P.n & 3) == 0;  // output rows are 16-byte aligned
+#pragma unroll
+      for (int j = 0; j < NPT; ++j) {
+        const int n = nb + 8 * TPR * j;
+        if (n >= P.n) continue;
+        const v4i lo = raw[j][0] - q, hi = raw[j][1] - q;
+        int32_t* dst = P.acc_out + (int64_t)m * P.n + n;
+        if (wide && n + 8 <= P.n) {
+          *G(reinterpret_cast<v4i*>(dst)) = lo;
+          *G(reinterpret_cast<v4i*>(dst + 4)) = hi;
+        } else {
+          const int32_t v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+          for (int e = 0; e < 8 && n + e < P.n; ++e) *G(dst + e) = v[e];
         }
       }
+      continue;
     }
-  };
-  if (!bf)
-    put(std::integral_constant<int, 2>{});
-  else if (all_fast)
-    put(std::integral_constant<int, 0>{});
-  else
-    put(std::integral_constant<int, 1>{});
-  __syncthreads();
-  const int chunks_row = BNT * esz / 16;  // 16-byte pieces per output row
-  const int per = 16 / esz;               // outputs per piece
-  const bool wide = (P.n % per) == 0;     // rows of the output are 16-byte aligned
-  int8_t* out = bf ? reinterpret_cast<int8_t*>(P.y) : reinterpret_cast<int8_t*>(P.acc_out);
-  for (int idx = tid; idx < BM * chunks_row; idx += kNT) {
-    const int ml = idx / chunks_row, c = idx - ml * chunks_row;
-    const int m = m0 + ml, n = n0 + c * per;
-    if (m >= A.m || n >= P.n) continue;
-    const int8_t* src = smem + ml * orow + c * 16;
-    int8_t* dst = out + ((int64_t)m * P.n + n) * esz;
-    if (wide && n + per <= P.n) {
-      *G(reinterpret_cast<v4i*>(dst)) = *reinterpret_cast<const v4i*>(src);
-    } else {
-      for (int e = 0; e < per && n + e < P.n; ++e) {
-        if (bf)
-          *G(reinterpret_cast<uint16_t*>(dst) + e) = reinterpret_cast<const uint16_t*>(src)[e];
-        else
-          *G(reinterpret_cast<int32_t*>(dst) + e) = reinterpret_cast<const int32_t*>(src)[e];
+    const bool wide = (P.n & 7) == 0;  // output rows are 16-byte aligned
+    auto emit = [&](auto fast) {
+#pragma unroll
+      for (int j = 0; j < NPT; ++j) {
+        const int n = nb + 8 * TPR * j;
+        if (n >= P.n) continue;
+        const int32_t v[8] = {raw[j][0].x - q, raw[j][0].y - q, raw[j][0].z - q, raw[j][0].w - q,
+                              raw[j][1].x - q, raw[j][1].y - q, raw[j][1].z - q, raw[j][1].w - q};
+        float yf[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          yf[e] = decltype(fast)::value ? row_div_fast((float)v[e], d.d, d.y) : (float)v[e] / d.d;
+        uint16_t* dst = P.y + (int64_t)m * P.n + n;
+        if (wide && n + 8 <= P.n) {
+          *G(reinterpret_cast<v4i*>(dst)) =
+              v4i{(int32_t)pack_bf16x2(yf[0], yf[1]), (int32_t)pack_bf16x2(yf[2], yf[3]),
+                  (int32_t)pack_bf16x2(yf[4], yf[5]), (int32_t)pack_bf16x2(yf[6], yf[7])};
+        } else {
+          for (int e = 0; e < 8 && n + e < P.n; ++e) *G(dst + e) = f32_to_bf16(yf[e]);
+        }
       }
-    }
+    };
+    if (d.fast)
+      emit(std::true_type{});
+    else
+      emit(std::false_type{});
   }
 }
 
@@ -467,7 +504,7 @@ hipError_t launch_prefill(const PrefillArgs& a, int total_tiles, hipStream_t s) 
     constexpr int BNT = BL_PREFILL_BN, NST = BL_PREFILL_NST, WMI = BL_PREFILL_WMI,
                   NW = BL_PREFILL_NW;
     constexpr size_t stages = (size_t)NST * Cfg<BNT, WMI, NW>::kStageBytes;
-    constexpr size_t out = (size_t)BM * (BNT * 4 + 16);  // int32 output staging
+    constexpr size_t out = (size_t)BM * (kEpiCols<BNT> * 4 + 16);  // int32 sums staged by rows
     constexpr size_t lds = stages > out ? stages : out;
     static const hipError_t attr = hipFuncSetAttribute(
         reinterpret_cast<const void*>(&prefill_kernel<BNT, NST, WMI, NW>),
