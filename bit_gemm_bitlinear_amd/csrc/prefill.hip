@@ -236,13 +236,17 @@ __global__ __launch_bounds__(kThreads) void prefill_reg_kernel(const PrefillArgs
 // per lane, lane L's bytes landing at dst + 16 L), through a ring of NST
 // slab buffers: while slab s is multiplied, slabs up to s+NST-1 are in
 // flight.  No staging registers, one barrier per slab.  The tile is BM=128
-// tokens x BNT outputs; four waves of 64 x BNT/2.
+// tokens x BNT outputs; a slab is BK codes deep (128 or 256).
 //
-// LDS image of a slab:
-//   A: 128 rows x 16 chunks of 16 B; chunk c of row r at r*16 + (c ^ (r & 15)).
-//   B: BNT columns x 4 chunks of 16 B (64 packed bytes = 256 codes); chunk c
-//      of column j at j*4 + (c ^ ((j >> 2) & 3)).
-// Both swizzles keep the lanes of one LDS read on distinct banks.
+// LDS image of a slab (KA = BK/16 chunks of 16 B per A row, KB = BK/64 per
+// B column):
+//   A: 128 rows x KA chunks; chunk c of row r at r*KA + (c ^ (r & (KA-1))).
+//   B: BNT columns x KB chunks (16 packed bytes = 64 codes each); chunk c of
+//      column j at j*KB + (c ^ ((j >> 2) & (KB-1))).
+// Both swizzles keep the lanes of one LDS read on distinct banks.  The two
+// halves of a wave (lanes 0-31, 32-63) take the two halves of the slab's K
+// range, so one matrix-core step pairs A chunks ks and KA/2 + ks with
+// packed B dword ks of the lane's B chunk.
 
 template <int N>
 __device__ __forceinline__ void wait_vm() {
@@ -255,11 +259,16 @@ __device__ __forceinline__ void dma16(const void* src, int8_t* lds_dst) {
                                    (__attribute__((address_space(3))) void*)lds_dst, 16, 0, 0);
 }
 
-template <int BNT, int WMI, int NW>
+template <int BNT, int WMI, int NW, int BK>
 struct Cfg {
+  static_assert(BK == 128 || BK == 256, "a slab is 128 or 256 codes deep");
   static constexpr int kNT = 64 * NW;  // threads
-  static constexpr int kAChunks = BM * 16;
-  static constexpr int kBChunks = BNT * 4;
+  static constexpr int kACh = BK / 16;  // 16-byte A chunks per row of a slab
+  static constexpr int kBCh = BK / 64;  // 16-byte B chunks per column of a slab
+  static constexpr int kBL = kBCh / 2;  // B chunks per lane (two lane halves split K)
+  static constexpr int kKS = BK / 32;   // matrix-core steps per slab
+  static constexpr int kAChunks = BM * kACh;
+  static constexpr int kBChunks = BNT * kBCh;
   static constexpr int kStageBytes = (kAChunks + kBChunks) * 16;
   static constexpr int kADma = kAChunks / kNT;
   static constexpr int kBDma = kBChunks / kNT;
@@ -271,17 +280,17 @@ struct Cfg {
   static_assert(kADma * kNT == kAChunks && kBDma * kNT == kBChunks, "whole DMA blocks");
 };
 
-template <int BNT, int WMI, int NW>
+template <int BNT, int WMI, int NW, int BK>
 __device__ __forceinline__ void issue_stage(const PrefillProj& P, int m0, int n0, int slab,
                                             int8_t* __restrict__ st) {
-  using K = Cfg<BNT, WMI, NW>;
+  using K = Cfg<BNT, WMI, NW, BK>;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
   for (int i = 0; i < K::kADma; ++i) {
     const int blk = wave * K::kADma + i;  // 64-chunk block written by this instruction
     const int pos = blk * 64 + lane;
-    const int r = pos >> 4, c = (pos & 15) ^ (r & 15);
-    dma16(P.q + (int64_t)(m0 + r) * P.ldq + slab * 256 + 16 * c, st + blk * 1024);
+    const int r = pos / K::kACh, c = (pos % K::kACh) ^ (r & (K::kACh - 1));
+    dma16(P.q + (int64_t)(m0 + r) * P.ldq + slab * BK + 16 * c, st + blk * 1024);
   }
   const int rowbytes = P.k >> 2;
   int8_t* bst = st + K::kAChunks * 16;
@@ -289,24 +298,22 @@ __device__ __forceinline__ void issue_stage(const PrefillProj& P, int m0, int n0
   for (int i = 0; i < K::kBDma; ++i) {
     const int blk = wave * K::kBDma + i;
     const int pos = blk * 64 + lane;
-    const int j = pos >> 2, c = (pos & 3) ^ ((j >> 2) & 3);
+    const int j = pos / K::kBCh, c = (pos % K::kBCh) ^ ((j >> 2) & (K::kBCh - 1));
     const int row = min(n0 + j, P.n - 1);
-    dma16(P.packed + (int64_t)row * rowbytes + min(slab * 64 + 16 * c, rowbytes - 16),
+    dma16(P.packed + (int64_t)row * rowbytes + min(slab * (BK / 4) + 16 * c, rowbytes - 16),
           bst + blk * 1024);
   }
 }
 
-// Columns of a tile whose int32 sums are staged in LDS at once by the
-// epilogue (at most 256: 128 rows x 1040 bytes fit beside nothing else).
-template <int BNT>
-constexpr int kEpiCols = BNT < 256 ? BNT : 256;
-
+// EC = columns of the tile whose int32 sums the epilogue stages in LDS at
+// once (128 rows x (4 EC + 16) bytes).
 // WMI = 32-row tiles per wave.  With WMI = 4 each wave covers all 128 rows of
 // the tile and its own columns, so every weight column is expanded once per
 // workgroup; with WMI = 2 two waves share (and both expand) each column.
-template <int BNT, int NST, int WMI, int NW>
-__global__ __launch_bounds__(64 * NW) void prefill_kernel(const PrefillArgs A) {
-  using K = Cfg<BNT, WMI, NW>;
+template <int BNT, int NST, int WMI, int NW, int BK, int EC>
+__global__ __launch_bounds__(64 * NW)
+__attribute__((amdgpu_waves_per_eu(NW == 4 ? 2 : 1))) void prefill_kernel(const PrefillArgs A) {
+  using K = Cfg<BNT, WMI, NW, BK>;
   constexpr int kNT = K::kNT;
   constexpr int WNF = K::WNF;
   extern __shared__ __align__(16) int8_t smem[];
@@ -325,7 +332,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(const PrefillArgs A) {
   const int n0 = tn * BNT;
   const int wm0 = (wave % K::kWavesM) * 32 * WMI;  // wave's rows within the tile
   const int wn0 = (wave / K::kWavesM) * 32 * WNF;  // wave's columns within the tile
-  const int S = (P.k + 255) >> 8;
+  const int S = (P.k + BK - 1) / BK;
   const bool bf = P.y != nullptr;
 
   // per-row code sums and divisors, fetched now (vector loads, retired in
@@ -347,7 +354,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(const PrefillArgs A) {
 
 #pragma unroll
   for (int p = 0; p < NST - 1; ++p)
-    if (p < S) issue_stage<BNT, WMI, NW>(P, m0, n0, p, smem + p * K::kStageBytes);
+    if (p < S) issue_stage<BNT, WMI, NW, BK>(P, m0, n0, p, smem + p * K::kStageBytes);
 
   for (int s = 0; s < S; ++s) {
     // wait for slab s: the slabs issued after it (at most NST-2) may still fly
@@ -363,17 +370,18 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(const PrefillArgs A) {
     __builtin_amdgcn_s_barrier();  // every wave's slab-s data is in LDS, and
                                    // every wave is done with slab s-1's buffer
     if (s + NST - 1 < S)
-      issue_stage<BNT, WMI, NW>(P, m0, n0, s + NST - 1, smem + ((s + NST - 1) % NST) * K::kStageBytes);
+      issue_stage<BNT, WMI, NW, BK>(P, m0, n0, s + NST - 1, smem + ((s + NST - 1) % NST) * K::kStageBytes);
     const int8_t* abuf = smem + (s % NST) * K::kStageBytes;
     const int8_t* bbuf = abuf + K::kAChunks * 16;
-    // weight chunks of this lane: column wn0 + 32f + lj, chunks 2lg and 2lg+1
-    v4i b[WNF][2];
+    // weight chunks of this lane: column wn0 + 32f + lj, chunks kBL * lg + h
+    v4i b[WNF][K::kBL];
 #pragma unroll
     for (int f = 0; f < WNF; ++f) {
       const int j = wn0 + 32 * f + lj;
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
-        b[f][h] = *reinterpret_cast<const v4i*>(bbuf + 16 * (j * 4 + ((2 * lg + h) ^ ((j >> 2) & 3))));
+      for (int h = 0; h < K::kBL; ++h)
+        b[f][h] = *reinterpret_cast<const v4i*>(
+            bbuf + 16 * (j * K::kBCh + ((K::kBL * lg + h) ^ ((j >> 2) & (K::kBCh - 1)))));
     }
     // A fragments of step ks + 1 are read while step ks multiplies, so the
     // LDS latency hides behind the matrix-core work
@@ -381,14 +389,15 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(const PrefillArgs A) {
 #pragma unroll
       for (int i = 0; i < WMI; ++i) {
         const int r = wm0 + 32 * i + lj;
-        a[i] = *reinterpret_cast<const v4i*>(abuf + 16 * (r * 16 + ((8 * lg + ks) ^ (r & 15))));
+        a[i] = *reinterpret_cast<const v4i*>(
+            abuf + 16 * (r * K::kACh + ((K::kKS * lg + ks) ^ (r & (K::kACh - 1)))));
       }
     };
     v4i a[2][WMI];
     aload(0, a[0]);
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      if (ks < 7) aload(ks + 1, a[(ks + 1) & 1]);
+    for (int ks = 0; ks < K::kKS; ++ks) {
+      if (ks < K::kKS - 1) aload(ks + 1, a[(ks + 1) & 1]);
 #pragma unroll
       for (int f = 0; f < WNF; ++f) {
         const v4i bq = decode16((uint32_t)b[f][ks >> 2][ks & 3]);
@@ -404,7 +413,6 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(const PrefillArgs A) {
   // thread takes one row: its code sum and divisor are read once, and 8
   // consecutive outputs at a time are converted and stored as 16-byte
   // (bf16) or 32-byte (int32) pieces.
-  constexpr int EC = kEpiCols<BNT>;
   constexpr int orow = EC + 4;  // int32 words per staged row (16 bytes of padding)
   static_assert(BNT % EC == 0 && EC % (32 * WNF) == 0, "a wave's columns lie in one pass");
   int32_t* st = reinterpret_cast<int32_t*>(smem);
@@ -486,7 +494,11 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(const PrefillArgs A) {
   }
 }
 
-// Slab buffers and wave layout of the main variant.
+// Slab buffers, wave layout, slab depth and epilogue pass width of the main
+// variant: 4 waves of 64 x 128 outputs, slabs of 128 codes, two buffers of
+// 24 KB and 128-column epilogue passes (67.6 KB) -- small enough that two
+// workgroups share a CU, so that one's epilogue (vector ALU work) overlaps
+// the other's matrix-core loop.
 #ifndef BL_PREFILL_NST
 #define BL_PREFILL_NST 2
 #endif
@@ -494,7 +506,13 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(const PrefillArgs A) {
 #define BL_PREFILL_WMI 2
 #endif
 #ifndef BL_PREFILL_NW
-#define BL_PREFILL_NW 8
+#define BL_PREFILL_NW 4
+#endif
+#ifndef BL_PREFILL_BK
+#define BL_PREFILL_BK 128
+#endif
+#ifndef BL_PREFILL_EC
+#define BL_PREFILL_EC 128
 #endif
 
 }  // namespace
@@ -502,15 +520,15 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(const PrefillArgs A) {
 hipError_t launch_prefill(const PrefillArgs& a, int total_tiles, hipStream_t s) {
   if (a.load_mode == 0) {
     constexpr int BNT = BL_PREFILL_BN, NST = BL_PREFILL_NST, WMI = BL_PREFILL_WMI,
-                  NW = BL_PREFILL_NW;
-    constexpr size_t stages = (size_t)NST * Cfg<BNT, WMI, NW>::kStageBytes;
-    constexpr size_t out = (size_t)BM * (kEpiCols<BNT> * 4 + 16);  // int32 sums staged by rows
+                  NW = BL_PREFILL_NW, BK = BL_PREFILL_BK, EC = BL_PREFILL_EC;
+    constexpr size_t stages = (size_t)NST * Cfg<BNT, WMI, NW, BK>::kStageBytes;
+    constexpr size_t out = (size_t)BM * (EC * 4 + 16);  // int32 sums staged by rows
     constexpr size_t lds = stages > out ? stages : out;
     static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&prefill_kernel<BNT, NST, WMI, NW>),
+        reinterpret_cast<const void*>(&prefill_kernel<BNT, NST, WMI, NW, BK, EC>),
         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (attr != hipSuccess) return attr;
-    prefill_kernel<BNT, NST, WMI, NW><<<(unsigned)total_tiles, 64 * NW, lds, s>>>(a);
+    prefill_kernel<BNT, NST, WMI, NW, BK, EC><<<(unsigned)total_tiles, 64 * NW, lds, s>>>(a);
   } else if (a.load_mode == 1) {
     prefill_reg_kernel<1><<<(unsigned)total_tiles, kThreads, 0, s>>>(a);
   } else {

@@ -149,6 +149,7 @@ ACC_SHAPES = [
     (4, 40, 14336 * 2), (16, 20, 8192 + 16),
     # prefill path (M > 16)
     (17, 16, 64), (33, 130, 260), (128, 128, 256), (200, 257, 516), (300, 64, 12), (129, 40, 2048),
+    (100, 257, 1088), (260, 520, 2112),  # K % 128 == 64: a last half-deep slab; ragged N and M
 ]
 
 
@@ -165,7 +166,8 @@ def test_forward_acc_parity(bl, m, n, k):
 # ------------------------------------------------------------------ forward (bf16)
 
 FWD_SHAPES = [(1, 16, 64), (1, 2048, 2048), (3, 50, 36), (8, 2048, 2048), (16, 96, 4096),
-              (16, 300, 9216), (17, 64, 256), (64, 200, 516), (256, 384, 2560), (40, 1000, 68)]
+              (16, 300, 9216), (17, 64, 256), (64, 200, 516), (256, 384, 2560), (40, 1000, 68),
+              (72, 250, 1088)]
 
 
 @pytest.mark.parametrize("m,n,k", FWD_SHAPES)
