@@ -240,10 +240,10 @@ __global__ __launch_bounds__(kThreads) void prefill_reg_kernel(const PrefillArgs
 //
 // LDS image of a slab (KA = BK/16 chunks of 16 B per A row, KB = BK/64 per
 // B column):
-//   A: 128 rows x KA chunks; chunk c of row r at r*KA + (c ^ (r & (KA-1))).
+//   A: 128 rows x KA chunks; chunk c of row r at r*KA + (c ^ ((r / (16/KA)) & (KA-1))).
 //   B: BNT columns x KB chunks (16 packed bytes = 64 codes each); chunk c of
-//      column j at j*KB + (c ^ ((j >> 2) & (KB-1))).
-// Both swizzles keep the lanes of one LDS read on distinct banks.  The two
+//      column j at j*KB + (c ^ ((j / (16/KB)) & (KB-1))).
+// Both swizzles keep the 16 lanes that LDS serves together on distinct banks.  The two
 // halves of a wave (lanes 0-31, 32-63) take the two halves of the slab's K
 // range, so one matrix-core step pairs A chunks ks and KA/2 + ks with
 // packed B dword ks of the lane's B chunk.
@@ -267,6 +267,17 @@ struct Cfg {
   static constexpr int kBCh = BK / 64;  // 16-byte B chunks per column of a slab
   static constexpr int kBL = kBCh / 2;  // B chunks per lane (two lane halves split K)
   static constexpr int kKS = BK / 32;   // matrix-core steps per slab
+  // LDS serves a 16-byte read 16 lanes at a time from 64 banks (256 bytes):
+  // the swizzles below give the 16 rows (A) or columns (B) that one such
+  // group reads 16 distinct 16-byte bank slots
+  static constexpr int kARowsPerSlot = 16 / kACh;  // rows sharing a swizzle value
+  static constexpr int kBColsPerSlot = 16 / kBCh;
+  static __device__ __forceinline__ int aswz(int r, int c) {
+    return c ^ ((r / kARowsPerSlot) & (kACh - 1));
+  }
+  static __device__ __forceinline__ int bswz(int j, int c) {
+    return c ^ ((j / kBColsPerSlot) & (kBCh - 1));
+  }
   static constexpr int kAChunks = BM * kACh;
   static constexpr int kBChunks = BNT * kBCh;
   static constexpr int kStageBytes = (kAChunks + kBChunks) * 16;
@@ -289,7 +300,7 @@ __device__ __forceinline__ void issue_stage(const PrefillProj& P, int m0, int n0
   for (int i = 0; i < K::kADma; ++i) {
     const int blk = wave * K::kADma + i;  // 64-chunk block written by this instruction
     const int pos = blk * 64 + lane;
-    const int r = pos / K::kACh, c = (pos % K::kACh) ^ (r & (K::kACh - 1));
+    const int r = pos / K::kACh, c = K::aswz(r, pos % K::kACh);
     dma16(P.q + (int64_t)(m0 + r) * P.ldq + slab * BK + 16 * c, st + blk * 1024);
   }
   const int rowbytes = P.k >> 2;
@@ -298,7 +309,7 @@ __device__ __forceinline__ void issue_stage(const PrefillProj& P, int m0, int n0
   for (int i = 0; i < K::kBDma; ++i) {
     const int blk = wave * K::kBDma + i;
     const int pos = blk * 64 + lane;
-    const int j = pos / K::kBCh, c = (pos % K::kBCh) ^ ((j >> 2) & (K::kBCh - 1));
+    const int j = pos / K::kBCh, c = K::bswz(j, pos % K::kBCh);
     const int row = min(n0 + j, P.n - 1);
     dma16(P.packed + (int64_t)row * rowbytes + min(slab * (BK / 4) + 16 * c, rowbytes - 16),
           bst + blk * 1024);
@@ -380,8 +391,7 @@ __attribute__((amdgpu_waves_per_eu(NW == 4 ? 2 : 1))) void prefill_kernel(const 
       const int j = wn0 + 32 * f + lj;
 #pragma unroll
       for (int h = 0; h < K::kBL; ++h)
-        b[f][h] = *reinterpret_cast<const v4i*>(
-            bbuf + 16 * (j * K::kBCh + ((K::kBL * lg + h) ^ ((j >> 2) & (K::kBCh - 1)))));
+        b[f][h] = *reinterpret_cast<const v4i*>(bbuf + 16 * (j * K::kBCh + K::bswz(j, K::kBL * lg + h)));
     }
     // A fragments of step ks + 1 are read while step ks multiplies, so the
     // LDS latency hides behind the matrix-core work
@@ -389,8 +399,7 @@ __attribute__((amdgpu_waves_per_eu(NW == 4 ? 2 : 1))) void prefill_kernel(const 
 #pragma unroll
       for (int i = 0; i < WMI; ++i) {
         const int r = wm0 + 32 * i + lj;
-        a[i] = *reinterpret_cast<const v4i*>(
-            abuf + 16 * (r * K::kACh + ((K::kKS * lg + ks) ^ (r & (K::kACh - 1)))));
+        a[i] = *reinterpret_cast<const v4i*>(abuf + 16 * (r * K::kACh + K::aswz(r, K::kKS * lg + ks)));
       }
     };
     v4i a[2][WMI];
@@ -398,6 +407,7 @@ __attribute__((amdgpu_waves_per_eu(NW == 4 ? 2 : 1))) void prefill_kernel(const 
 #pragma unroll
     for (int ks = 0; ks < K::kKS; ++ks) {
       if (ks < K::kKS - 1) aload(ks + 1, a[(ks + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);  // the reads go out ahead of this step's work
 #pragma unroll
       for (int f = 0; f < WNF; ++f) {
         const v4i bq = decode16((uint32_t)b[f][ks >> 2][ks & 3]);
