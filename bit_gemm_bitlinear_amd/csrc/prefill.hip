@@ -291,30 +291,54 @@ struct Cfg {
   static_assert(kADma * kNT == kAChunks && kBDma * kNT == kBChunks, "whole DMA blocks");
 };
 
+// The slab loads of one tile: each lane's global addresses are computed
+// once per tile, so issuing a slab is an add per load.  Weight rows whose
+// packed length is not a multiple of the slab's bytes have their last
+// slab's loads clamped to the row (the codes there meet zero activations).
 template <int BNT, int WMI, int NW, int BK>
-__device__ __forceinline__ void issue_stage(const PrefillProj& P, int m0, int n0, int slab,
-                                            int8_t* __restrict__ st) {
+struct Stager {
   using K = Cfg<BNT, WMI, NW, BK>;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int8_t* a[K::kADma];
+  const uint8_t* brow[K::kBDma];
+  int bc[K::kBDma];  // byte offset of the lane's chunk within a slab of a weight row
+  int rowbytes;
+
+  __device__ __forceinline__ Stager(const PrefillProj& P, int m0, int n0) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
-  for (int i = 0; i < K::kADma; ++i) {
-    const int blk = wave * K::kADma + i;  // 64-chunk block written by this instruction
-    const int pos = blk * 64 + lane;
-    const int r = pos / K::kACh, c = K::aswz(r, pos % K::kACh);
-    dma16(P.q + (int64_t)(m0 + r) * P.ldq + slab * BK + 16 * c, st + blk * 1024);
-  }
-  const int rowbytes = P.k >> 2;
-  int8_t* bst = st + K::kAChunks * 16;
+    for (int i = 0; i < K::kADma; ++i) {
+      const int pos = (wave * K::kADma + i) * 64 + lane;
+      const int r = pos / K::kACh, c = K::aswz(r, pos % K::kACh);
+      a[i] = P.q + (int64_t)(m0 + r) * P.ldq + 16 * c;
+    }
+    rowbytes = P.k >> 2;
 #pragma unroll
-  for (int i = 0; i < K::kBDma; ++i) {
-    const int blk = wave * K::kBDma + i;
-    const int pos = blk * 64 + lane;
-    const int j = pos / K::kBCh, c = K::bswz(j, pos % K::kBCh);
-    const int row = min(n0 + j, P.n - 1);
-    dma16(P.packed + (int64_t)row * rowbytes + min(slab * (BK / 4) + 16 * c, rowbytes - 16),
-          bst + blk * 1024);
+    for (int i = 0; i < K::kBDma; ++i) {
+      const int pos = (wave * K::kBDma + i) * 64 + lane;
+      const int j = pos / K::kBCh, c = K::bswz(j, pos % K::kBCh);
+      brow[i] = P.packed + (int64_t)min(n0 + j, P.n - 1) * rowbytes;
+      bc[i] = 16 * c;
+    }
   }
-}
+
+  // Slab `slab` into the stage buffer st (each instruction fills 1 KB of
+  // LDS: lane L's 16 bytes land at st + 1024 * block + 16 L).
+  __device__ __forceinline__ void issue(int slab, int8_t* __restrict__ st) const {
+    const int wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int i = 0; i < K::kADma; ++i) dma16(a[i] + slab * BK, st + (wave * K::kADma + i) * 1024);
+    int8_t* bst = st + K::kAChunks * 16;
+    const int b0 = slab * (BK / 4);
+    if (b0 + BK / 4 <= rowbytes) {
+#pragma unroll
+      for (int i = 0; i < K::kBDma; ++i) dma16(brow[i] + b0 + bc[i], bst + (wave * K::kBDma + i) * 1024);
+    } else {
+#pragma unroll
+      for (int i = 0; i < K::kBDma; ++i)
+        dma16(brow[i] + min(b0 + bc[i], rowbytes - 16), bst + (wave * K::kBDma + i) * 1024);
+    }
+  }
+};
 
 // EC = columns of the tile whose int32 sums the epilogue stages in LDS at
 // once (128 rows x (4 EC + 16) bytes).
@@ -363,9 +387,10 @@ __attribute__((amdgpu_waves_per_eu(NW == 4 ? 2 : 1))) void prefill_kernel(const 
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][f][r] = 0;
 
+  const Stager<BNT, WMI, NW, BK> stager(P, m0, n0);
 #pragma unroll
   for (int p = 0; p < NST - 1; ++p)
-    if (p < S) issue_stage<BNT, WMI, NW, BK>(P, m0, n0, p, smem + p * K::kStageBytes);
+    if (p < S) stager.issue(p, smem + p * K::kStageBytes);
 
   for (int s = 0; s < S; ++s) {
     // wait for slab s: the slabs issued after it (at most NST-2) may still fly
@@ -381,7 +406,7 @@ __attribute__((amdgpu_waves_per_eu(NW == 4 ? 2 : 1))) void prefill_kernel(const 
     __builtin_amdgcn_s_barrier();  // every wave's slab-s data is in LDS, and
                                    // every wave is done with slab s-1's buffer
     if (s + NST - 1 < S)
-      issue_stage<BNT, WMI, NW, BK>(P, m0, n0, s + NST - 1, smem + ((s + NST - 1) % NST) * K::kStageBytes);
+      stager.issue(s + NST - 1, smem + ((s + NST - 1) % NST) * K::kStageBytes);
     const int8_t* abuf = smem + (s % NST) * K::kStageBytes;
     const int8_t* bbuf = abuf + K::kAChunks * 16;
     // weight chunks of this lane: column wn0 + 32f + lj, chunks kBL * lg + h
