@@ -250,6 +250,100 @@ __device__ __forceinline__ void quant_row_internal_fast(const uint16_t* __restri
   }
 }
 
+// One wave per row, for launches whose rows all come from bf16 input with
+// k % 8 == 0 and at most 64 * NBW groups of 16 codes: no barriers and no
+// LDS.  Lane l owns groups l + 64 b, two 16-byte loads each, all issued
+// before any is used; the absmax and the code sum are wave reductions.
+// q = rint(x * s) with |x * s| <= 127 * (1 + 2^-24) (s = RN(127 / amax)), so
+// the clamp to [-128, 127] never binds; adding 1.5 * 2^23 to t = RN(x * s)
+// rounds to an integer with ties to even and leaves q in two's complement in
+// the low byte of the sum's bits, which byte permutes gather into the
+// internal order (dword a, byte b = code 4b + a).
+template <int NBW>
+__device__ __forceinline__ void quant_row_wave(const uint16_t* __restrict__ xr, int k, int ngroups,
+                                               v4i* __restrict__ qv, int32_t* qsum,
+                                               float* x_scale) {
+  const int lane = threadIdx.x & 63;
+  const int kg = k >> 4;  // groups holding data (a last half group: k % 16 == 8)
+  v4i lo[NBW], hi[NBW];
+#pragma unroll
+  for (int b = 0; b < NBW; ++b) {
+    const int g = lane + 64 * b;
+    lo[b] = hi[b] = v4i{0, 0, 0, 0};
+    if (16 * g < k) {
+      lo[b] = *reinterpret_cast<const v4i*>(xr + 16 * g);
+      if (16 * g + 8 < k) hi[b] = *reinterpret_cast<const v4i*>(xr + 16 * g + 8);
+    }
+  }
+  uint32_t amax = 0;
+#pragma unroll
+  for (int b = 0; b < NBW; ++b)
+    amax = max(amax, max(max(absmax_bits4((uint32_t)lo[b].x, (uint32_t)lo[b].y),
+                             absmax_bits4((uint32_t)lo[b].z, (uint32_t)lo[b].w)),
+                         max(absmax_bits4((uint32_t)hi[b].x, (uint32_t)hi[b].y),
+                             absmax_bits4((uint32_t)hi[b].z, (uint32_t)hi[b].w))));
+  amax = wave_reduce(amax, [](uint32_t x, uint32_t y) { return max(x, y); });
+  const float s = act_scale(bf16_to_f32(amax));
+  int32_t sum = 0;
+#pragma unroll
+  for (int b = 0; b < NBW; ++b) {
+    const int g = lane + 64 * b;
+    if (g >= ngroups) continue;
+    if (g > kg || (g == kg && 16 * g >= k)) {  // padding group: zero codes
+      qv[g] = v4i{0, 0, 0, 0};
+      continue;
+    }
+    const uint32_t w[8] = {(uint32_t)lo[b].x, (uint32_t)lo[b].y, (uint32_t)lo[b].z,
+                           (uint32_t)lo[b].w, (uint32_t)hi[b].x, (uint32_t)hi[b].y,
+                           (uint32_t)hi[b].z, (uint32_t)hi[b].w};
+    uint32_t r[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const uint32_t bits = (e & 1) ? (w[e >> 1] & 0xFFFF0000u) : (w[e >> 1] << 16);
+      r[e] = __float_as_uint(__uint_as_float(bits) * s + 12582912.0f);
+    }
+    v4i o;
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const uint32_t l2 = __builtin_amdgcn_perm(r[a + 4], r[a], 0x0c0c0400u);
+      const uint32_t h2 = __builtin_amdgcn_perm(r[a + 12], r[a + 8], 0x0c0c0400u);
+      o[a] = (int32_t)__builtin_amdgcn_perm(h2, l2, 0x05040100u);
+      sum = __builtin_amdgcn_sdot4(o[a], 0x01010101, sum, false);
+    }
+    qv[g] = o;
+  }
+  sum = (int32_t)wave_reduce((uint32_t)sum, [](uint32_t x, uint32_t y) { return x + y; });
+  if (lane == 0) {
+    *qsum = sum;
+    *x_scale = s;
+  }
+}
+
+template <int NBW>
+__global__ __launch_bounds__(kThreads) void act_quant_rows_kernel(const ActQuantArgs a) {
+  constexpr int kRowsPerBlock = kThreads / 64;
+  const int b = blockIdx.x;
+  if (b >= a.zero_blocks_begin) {
+    const int64_t nzb = (int64_t)(gridDim.x - a.zero_blocks_begin);
+    for (int64_t i = (int64_t)(b - a.zero_blocks_begin) * kThreads + threadIdx.x; i < a.zero_words;
+         i += nzb * kThreads)
+      a.zero[i] = 0;
+    return;
+  }
+  const int row = b * kRowsPerBlock + (int)(threadIdx.x >> 6);
+  int ji = 0;
+  while (ji + 1 < a.count && row >= a.j[ji + 1].row_begin) ++ji;
+  const ActQuantJob& J = a.j[ji];
+  const int m = row - J.row_begin;
+  if (m >= J.m_pad) return;  // past the last job's rows
+  v4i* qv = reinterpret_cast<v4i*>(J.q + (int64_t)m * J.ldq);
+  if (m >= J.m) {  // padding row: zero codes
+    for (int g = threadIdx.x & 63; g < J.ldq / 16; g += 64) qv[g] = v4i{0, 0, 0, 0};
+    return;
+  }
+  quant_row_wave<NBW>(J.x + (int64_t)m * J.k, J.k, J.ldq / 16, qv, J.qsum + m, J.x_scale + m);
+}
+
 __global__ __launch_bounds__(kThreads) void act_quant_internal_kernel(const ActQuantArgs a) {
   __shared__ uint32_t red[4];
   const int b = blockIdx.x;
@@ -317,6 +411,27 @@ hipError_t launch_act_quant_internal(const ActQuantArgs& a, int total_rows, hipS
     int64_t per = (int64_t)kThreads * 16;
     int64_t zb = (args.zero_words + per - 1) / per;
     zero_blocks = (int)(zb > 1024 ? 1024 : zb);
+  }
+  // one wave per row when every job is bf16 input with 16-byte rows that
+  // fit the lanes' registers
+  int groups = 0;
+  bool rows_ok = args.count > 0;
+  for (int i = 0; i < args.count; ++i) {
+    const ActQuantJob& J = args.j[i];
+    rows_ok = rows_ok && J.x != nullptr && (J.k & 7) == 0;
+    groups = groups > J.ldq / 16 ? groups : J.ldq / 16;
+  }
+  if (rows_ok && groups <= 64 * 16) {
+    const int row_blocks = (total_rows + kThreads / 64 - 1) / (kThreads / 64);
+    args.zero_blocks_begin = row_blocks;
+    const dim3 grid((unsigned)(row_blocks + zero_blocks));
+    if (groups <= 64 * 4)
+      act_quant_rows_kernel<4><<<grid, kThreads, 0, s>>>(args);
+    else if (groups <= 64 * 8)
+      act_quant_rows_kernel<8><<<grid, kThreads, 0, s>>>(args);
+    else
+      act_quant_rows_kernel<16><<<grid, kThreads, 0, s>>>(args);
+    return hipGetLastError();
   }
   args.zero_blocks_begin = total_rows;
   act_quant_internal_kernel<<<(unsigned)(total_rows + zero_blocks), kThreads, 0, s>>>(args);

@@ -11,6 +11,10 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+// Every product and sum is rounded on its own (the quantization and
+// division steps depend on it), whatever contraction the build would allow.
+#pragma clang fp contract(off)
+
 namespace bl {
 
 typedef int32_t v4i __attribute__((ext_vector_type(4)));

@@ -167,7 +167,10 @@ def test_forward_acc_parity(bl, m, n, k):
 
 FWD_SHAPES = [(1, 16, 64), (1, 2048, 2048), (3, 50, 36), (8, 2048, 2048), (16, 96, 4096),
               (16, 300, 9216), (17, 64, 256), (64, 200, 516), (256, 384, 2560), (40, 1000, 68),
-              (72, 250, 1088)]
+              (72, 250, 1088),
+              # activation quantization of the prefill path: a half group (K % 16 == 8),
+              # the 16-group-per-lane variant, and rows too long for it
+              (48, 96, 1048), (20, 64, 14336), (18, 32, 16400)]
 
 
 @pytest.mark.parametrize("m,n,k", FWD_SHAPES)
