@@ -63,11 +63,15 @@ void make_layout(int32_t count, const int64_t* ns, const int64_t* ks, int64_t m,
   L.decode = m <= kDecodeMaxM;
   L.load_mode = load_mode_for(count, ks);
   L.m_pad = L.decode ? (int32_t)m : (int32_t)round_up(m, kPrefillBM);
+  // decode: a layer that one workgroup per CU can cover takes the split
+  // plan; otherwise each projection is planned on its own
+  const bool split =
+      L.decode && plan_decode_split(m, count, ns, ks, L.load_mode, device_cu_count(), L.plan);
   size_t off = 0;
   for (int i = 0; i < count; ++i) {
     L.q_off[i] = L.xs_off[i] = L.qs_off[i] = 0;
     if (L.decode) {
-      L.plan[i] = plan_decode(m, ns[i], ks[i], L.load_mode);
+      if (!split) L.plan[i] = plan_decode(m, ns[i], ks[i], L.load_mode);
       L.plan[i].fused = L.plan[i].fused && have_x;
       if (L.plan[i].fused) continue;
     }
@@ -91,6 +95,16 @@ void make_layout(int32_t count, const int64_t* ns, const int64_t* ks, int64_t m,
     }
   }
   L.zero_bytes = off - L.zero_off;
+  // the size does not depend on which plan the device's CU count picks:
+  // room for the per-projection plans' split-K partials is always counted
+  size_t ring = L.zero_off;
+  for (int i = 0; L.decode && i < count; ++i) {
+    const DecodePlan p = plan_decode(m, ns[i], ks[i], L.load_mode);
+    if (p.ksplit > 1)
+      ring = align256(align256(ring + sizeof(int32_t) * (size_t)(m * ns[i])) +
+                      sizeof(uint32_t) * (size_t)p.ngroups);
+  }
+  off = std::max(off, ring);
   L.total = off > 0 ? off : 256;
 }
 

@@ -18,6 +18,7 @@ namespace bl {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kWaveRowsMin = 1024;  // rows from which one wave per row pays
 
 __device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t* red) {
 #pragma unroll
@@ -413,7 +414,8 @@ hipError_t launch_act_quant_internal(const ActQuantArgs& a, int total_rows, hipS
     zero_blocks = (int)(zb > 1024 ? 1024 : zb);
   }
   // one wave per row when every job is bf16 input with 16-byte rows that
-  // fit the lanes' registers
+  // fit the lanes' registers, and there are rows enough to fill the chip
+  // (a few long decode rows are faster with a workgroup each)
   int groups = 0;
   bool rows_ok = args.count > 0;
   for (int i = 0; i < args.count; ++i) {
@@ -421,7 +423,7 @@ hipError_t launch_act_quant_internal(const ActQuantArgs& a, int total_rows, hipS
     rows_ok = rows_ok && J.x != nullptr && (J.k & 7) == 0;
     groups = groups > J.ldq / 16 ? groups : J.ldq / 16;
   }
-  if (rows_ok && groups <= 64 * 16) {
+  if (rows_ok && groups <= 64 * 16 && total_rows >= kWaveRowsMin) {
     const int row_blocks = (total_rows + kThreads / 64 - 1) / (kThreads / 64);
     args.zero_blocks_begin = row_blocks;
     const dim3 grid((unsigned)(row_blocks + zero_blocks));

@@ -40,8 +40,9 @@ namespace {
 static_assert(BL_DECODE_WINDOW % 4 == 0, "ring slots hold whole tile rounds");
 
 constexpr int kWindow = BL_DECODE_WINDOW;  // 16-byte weight chunks in flight per lane
-constexpr int kWaveChunks = 16;            // target chunks streamed per wave
-constexpr int kWaveMaxChunks = 24;         // most chunks one wave streams
+constexpr int kWaveChunks = 24;            // target chunks streamed per wave (ring shape)
+constexpr int kWaveMaxChunks = 24;         // most chunks one wave streams (ring shape)
+constexpr int kSplitRing = 16;             // load ring per lane of the split shape
 constexpr int kStageUnits = kDecodeLdsA / 16 / 256;  // 16-byte code units per activation thread
 
 // 16 bytes of a packed row at byte offset `off` (a multiple of 16).  Parts
@@ -465,25 +466,34 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& A, const DecodePro
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");  // counters are zero
       prepare_codes<true, FUSED>(A, P, ns, xin, ws, lds, sh);
     } else {
-      constexpr int NC = kWaveChunks;
+      // a ring of NC chunks per lane: every slot is refilled with the chunk
+      // NC ahead right after it is read, so NC loads stay in flight until
+      // the last round (which refills nothing)
+      constexpr int NC = TWW == 3 ? 24 : kSplitRing;
+      static_assert(NC % TWW == 0, "a ring slot always holds the same row tile");
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");  // counters zeroed
       __builtin_amdgcn_s_barrier();
-      for (int base = 0; base < max(NI, 1); base += NC) {
-        v4i ring[NC];
+      v4i ring[NC];
 #pragma unroll
-        for (int d = 0; d < NC; ++d) ring[d] = wload(base + d);
-        __builtin_amdgcn_sched_barrier(0);
-        if (base == 0) lds_wait(&sh.ready, 4);
-        v4i a[4];
+      for (int d = 0; d < NC; ++d) ring[d] = wload(d);
+      __builtin_amdgcn_sched_barrier(0);
+      lds_wait(&sh.ready, 4);
+      v4i a[4];
+      auto round = [&](int base, auto refill) {
         static_for<NC>([&](auto dc) {
           constexpr int d = decltype(dc)::value;
-          constexpr int t = d % TWW;
+          constexpr int t = d % TWW;  // base is a multiple of NC, NC of TWW
+          const v4i b = ring[d];
+          if constexpr (decltype(refill)::value) ring[d] = wload(base + NC + d);
           if (base + d < NI) {
             if constexpr (t == 0) afrag((base + d) / TWW, a);
-            mma_chunk(acc[t], acc4[t], a, ring[d]);
+            mma_chunk(acc[t], acc4[t], a, b);
           }
         });
-      }
+      };
+      const int rounds = max((NI + NC - 1) / NC, 1);
+      for (int r = 0; r + 1 < rounds; ++r) round(r * NC, std::true_type{});
+      round((rounds - 1) * NC, std::false_type{});
     }
   } else {
     // all four waves prepare the codes, then stream through a ring of
@@ -645,6 +655,9 @@ __global__ __launch_bounds__(SPLIT ? 512 : 256) void decode_kernel(const DecodeA
   switch (P.tww) {
     case 1: decode_tw<1, MODE, SPLIT>(A, P, wl, lds, sh); break;
     case 2: decode_tw<2, MODE, SPLIT>(A, P, wl, lds, sh); break;
+    case 3:  // split-shape plans only, with the K range unsplit (wk = 1)
+      if constexpr (SPLIT) decode_tw<3, MODE, SPLIT>(A, P, wl, lds, sh);
+      break;
     default: decode_tw<4, MODE, SPLIT>(A, P, wl, lds, sh); break;
   }
 }
@@ -680,12 +693,62 @@ DecodePlan plan_decode(int64_t m, int64_t n, int64_t k, int mode) {
   return p;
 }
 
-size_t decode_lds_bytes(int64_t m, int lds_row) {
-  return (size_t)m * lds_row + (size_t)4 * kDecodeMaxTww * m * 16 * 4;
+// Split-shape plan for a whole layer: one workgroup per CU at most, each
+// streaming wave's share as small as possible.  Per projection the choice is
+// the K split over the 4 streaming waves (wk) and the 16-row tiles per wave
+// (tww, 1-4); a wave then streams tww * ceil(S / wk) 16-byte chunks per lane
+// (S = 256-code slabs per row).  The smallest bound X on that count for which
+// the fewest workgroups each projection needs add up to at most `cus` wins.
+// K is never split across workgroups here, so every row's codes fit LDS.
+bool plan_decode_split(int64_t m, int32_t count, const int64_t* ns, const int64_t* ks, int mode,
+                       int cus, DecodePlan* plans) {
+  constexpr int kMaxChunks = 96;  // per lane: at most six rounds of the ring
+  constexpr int kSplitPlanMinChunks = 48;
+  if (mode != 0 || count < 1 || count > kMaxProj) return false;
+  int S[kMaxProj];
+  int64_t tiles[kMaxProj];
+  for (int i = 0; i < count; ++i) {
+    S[i] = (int)((ks[i] + 255) / 256);
+    tiles[i] = (ns[i] + 15) / 16;
+    if (m * (S[i] * 256 + 16) > kDecodeLdsA) return false;
+  }
+  // (wk, tww) pairs: three tiles per wave only with the K range unsplit
+  // (the in-LDS partial sums index rows by shifts)
+  const int wks[10] = {1, 1, 1, 1, 2, 2, 2, 4, 4, 4};
+  const int twws[10] = {1, 2, 3, 4, 1, 2, 4, 1, 2, 4};
+  for (int x = 1; x <= kMaxChunks; ++x) {
+    int64_t total = 0;
+    bool ok = true;
+    for (int i = 0; i < count && ok; ++i) {
+      int64_t best = -1;
+      for (int o = 0; o < 10; ++o) {
+        const int wk = wks[o], tww = twws[o];
+        if (tww * ((S[i] + wk - 1) / wk) > x) continue;
+        const int64_t per = (int64_t)(4 / wk) * tww;  // 16-row tiles per workgroup
+        const int64_t wgs = (tiles[i] + per - 1) / per;
+        if (best < 0 || wgs < best) {
+          best = wgs;
+          DecodePlan& p = plans[i];
+          p.wk = wk;
+          p.tww = tww;
+          p.kspw = S[i];
+          p.ksplit = 1;
+          p.ngroups = (int)wgs;
+          p.fused = m <= kFusedMaxM && ks[i] % 16 == 0 && m * ks[i] <= kFusedMaxElems;
+        }
+      }
+      if (best < 0) ok = false;
+      total += best;
+    }
+    // Shorter streams are left to the per-projection plans: measured on
+    // the 3B-class layer (36 chunks per wave here) the many-workgroup ring
+    // shape was faster, on the 8B-class layer (64) this plan was.
+    if (ok && total <= cus) return x >= kSplitPlanMinChunks;
+  }
+  return false;
 }
 
-hipError_t launch_decode(const DecodeArgs& a, int total_wgs, size_t lds_bytes, hipStream_t s) {
-  // CUs of the current device (cached per device id)
+int device_cu_count() {
   static int cus[64] = {0};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
@@ -694,7 +757,15 @@ hipError_t launch_decode(const DecodeArgs& a, int total_wgs, size_t lds_bytes, h
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) n = 1;
     cus[dev] = n > 0 ? n : 1;
   }
-  const bool split = a.load_mode == 0 && total_wgs <= cus[dev];
+  return cus[dev];
+}
+
+size_t decode_lds_bytes(int64_t m, int lds_row) {
+  return (size_t)m * lds_row + (size_t)4 * kDecodeMaxTww * m * 16 * 4;
+}
+
+hipError_t launch_decode(const DecodeArgs& a, int total_wgs, size_t lds_bytes, hipStream_t s) {
+  const bool split = a.load_mode == 0 && total_wgs <= device_cu_count();
   const dim3 grid((unsigned)total_wgs);
   if (split)
     decode_kernel<0, true><<<grid, 512, lds_bytes, s>>>(a);

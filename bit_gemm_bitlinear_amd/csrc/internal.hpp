@@ -86,6 +86,9 @@ struct DecodePlan {
   bool fused;
 };
 DecodePlan plan_decode(int64_t m, int64_t n, int64_t k, int mode);
+bool plan_decode_split(int64_t m, int32_t count, const int64_t* ns, const int64_t* ks, int mode,
+                       int cus, DecodePlan* plans);
+int device_cu_count();  // compute units of the current device (cached per device)
 size_t decode_lds_bytes(int64_t m, int lds_row);
 hipError_t launch_decode(const DecodeArgs& a, int total_wgs, size_t lds_bytes, hipStream_t s);
 

@@ -202,6 +202,26 @@ def test_forward_deterministic_and_grouped_equals_single(bl):
         assert_bf16_close(host_bits(y), r)
 
 
+@pytest.mark.parametrize("m", [1, 3, 16])
+def test_grouped_ragged_layer(bl, m):
+    """A layer whose row counts are not multiples of the workgroup's rows and
+    whose K ranges differ: the layer-level plan (one workgroup per CU, rows
+    and K split over the waves, 1-4 row tiles per wave) must cover every
+    output exactly once."""
+    shapes = [(1000, 2048), (3001, 3072), (70, 4352), (4100, 1024), (17, 8192), (2500, 2560)]
+    xs, ps, ss, refs = [], [], [], []
+    for i, (n, k) in enumerate(shapes):
+        x, w = wls.random_case(60 + 7 * m + i, m, n, k)
+        p, s = bl.pack_weights(torch.from_numpy(w).to(DEV))
+        xs.append(dev_bf16(x))
+        ps.append(p)
+        ss.append(s)
+        refs.append(oracle.forward(x, *oracle.pack_weights(w)))
+    ys = bl.forward_grouped(xs, ps, ss)
+    for (n, k), y, r in zip(shapes, ys, refs):
+        assert_bf16_close(host_bits(y), r, f"grouped ragged {m}x{n}x{k}")
+
+
 def test_golden_cases(bl):
     path = os.path.join(os.path.dirname(__file__), "golden", "oracle_small_cases.json")
     for c in json.load(open(path))["cases"]:
