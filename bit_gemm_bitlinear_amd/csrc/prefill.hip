@@ -340,6 +340,11 @@ struct Stager {
   }
 };
 
+#ifndef BL_PREFILL_WGS_PER_CU
+#define BL_PREFILL_WGS_PER_CU 2
+#endif
+constexpr int kPrefillWgsPerCu = BL_PREFILL_WGS_PER_CU;  // workgroups the LDS and registers allow per CU
+
 // EC = columns of the tile whose int32 sums the epilogue stages in LDS at
 // once (128 rows x (4 EC + 16) bytes).
 // WMI = 32-row tiles per wave.  With WMI = 4 each wave covers all 128 rows of
@@ -347,7 +352,7 @@ struct Stager {
 // workgroup; with WMI = 2 two waves share (and both expand) each column.
 template <int BNT, int NST, int WMI, int NW, int BK, int EC>
 __global__ __launch_bounds__(64 * NW)
-__attribute__((amdgpu_waves_per_eu(NW == 4 ? 2 : 1))) void prefill_kernel(const PrefillArgs A) {
+__attribute__((amdgpu_waves_per_eu(NW * kPrefillWgsPerCu / 4))) void prefill_kernel(const PrefillArgs A) {
   using K = Cfg<BNT, WMI, NW, BK>;
   constexpr int kNT = K::kNT;
   constexpr int WNF = K::WNF;
