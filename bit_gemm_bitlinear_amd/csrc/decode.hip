@@ -6,22 +6,27 @@
 //
 // This is bound by HBM bandwidth on the packed weights (2 bits per weight),
 // so the kernel is organised around streaming them once:
-//  * work unit: a workgroup (4 waves) owns 16*TW consecutive weight rows and
-//    a range of K (all of it unless K is split for LDS space); every lane
-//    issues all of its 16-byte weight loads up front, so a whole decoder
-//    layer is in flight at once;
+//  * work unit: a workgroup owns 16*TW consecutive weight rows per group of
+//    streaming waves and a range of K (all of it unless K is split for LDS
+//    space).  Split shape (one workgroup per CU): waves 0-3 stream through a
+//    16-deep load ring per lane while waves 4-7 prepare the activation codes;
+//    ring shape (several workgroups per CU): four waves prepare the codes,
+//    then stream through an 8-deep ring;
 //  * activations: for small M*K the workgroup quantizes the bf16 rows itself
 //    (activation_norm_quant: exact integer absmax over the bf16 magnitude
-//    bits, one fp32 division, one multiply and round per code) straight into
-//    LDS -- no separate launch; otherwise it stages codes prepared by
-//    act_quant.hip.  Either way activation loads are issued before the weight
-//    loads, because the memory counter retires loads in order;
+//    bits, one fp32 division, one multiply and one rounding add per code)
+//    straight into LDS -- no separate launch; otherwise it stages codes
+//    prepared by act_quant.hip.  Either way the activation loads reach the
+//    memory pipeline before the weight loads (a barrier orders them in the
+//    split shape): behind a full weight stream they would arrive microseconds
+//    later;
 //  * each 16 packed bytes hold 64 weights = four K-steps of one row for the
-//    16x16x64 int8 matrix-core op; they are expanded in registers to codes
-//    c = u + 1 with one shift and one mask per dword (common.hpp), and
-//    sum q*u = sum q*c - sum q is restored with the per-row code sum;
-//  * token rows m >= M of the 16-row A operand are zeros (no LDS reads);
-//  * the four waves split K, and their partial sums meet in LDS.
+//    16x16x64 int8 matrix-core op; they are expanded in registers with five
+//    bit operations per packed dword (mma_chunk), and sum q*u = sum q*c - sum q
+//    restores the ternary weights u = c - 1 from the codes c;
+//  * token rows m >= M of the 16-row A operand repeat row 0 (rows of the
+//    product do not mix; output rows m >= M are never stored);
+//  * the streaming waves may split K, and their partial sums meet in LDS.
 // Loads past the end of a row or past the last row are clamped to valid
 // addresses instead of masked: the activation codes there are zero (rows of
 // codes are zero-padded) and output columns of rows >= N are never stored.

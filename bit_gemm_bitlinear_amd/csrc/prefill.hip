@@ -6,14 +6,20 @@
 //
 // A dense contraction, so it runs on v_mfma_i32_32x32x32_i8 (half the
 // operand bytes and half the weight-expansion work per multiply of the
-// 16x16x64 form).  A workgroup computes a 128 (tokens) x 256 (outputs) tile
-// with four waves of 64 x 128 (2 x 4 matrix-core tiles of 32 x 32).
+// 16x16x64 form).  Two variants:
+//  * the main one (prefill_kernel, "Main variant" below) for weight rows that
+//    are 16-byte aligned (K % 64 == 0): both operands go from global memory
+//    straight into LDS, slabs of 128 codes, two workgroups per CU;
+//  * the register-staged one (prefill_reg_kernel, next) for other K.
 //
+// Register-staged variant: a workgroup computes a 128 (tokens) x 256
+// (outputs) tile with four waves of 64 x 128 (2 x 4 matrix-core tiles of
+// 32 x 32).
 //  * K advances by slabs of 256 codes.  The activation-code tile of a slab
 //    (128 rows x 256 B, internal layout from act_quant.hip) is staged in LDS,
 //    double-buffered: slab s+1 is fetched into registers while slab s is
 //    consumed, then written to the other buffer.  16-byte chunk c of row r is
-//    stored at chunk c ^ (r & 15), which spreads the 32 rows one A fragment
+//    stored at chunk c ^ (r & 15), which spreads the rows one A fragment
 //    reads over all banks.
 //  * Packed weights are small (2 bits each) and each wave needs its own 128
 //    columns, so they go straight from global memory to registers, one slab
