@@ -171,6 +171,14 @@ __device__ __forceinline__ void lds_wait(const int32_t* c, int target) {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Workgroup barrier ordering LDS only: weight loads in flight are not waited
+// for (a full __syncthreads fence could wait for them).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Publishes this wave's LDS writes, then adds one to *c.
 __device__ __forceinline__ void lds_post(int32_t* c) {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
@@ -314,7 +322,7 @@ __device__ __forceinline__ void prepare_codes(const DecodeArgs& A, const DecodeP
     if constexpr (SPLIT)
       lds_wait(&sh.amax_count, 4);
     else
-      __syncthreads();
+      lds_barrier();
     float s[kFusedMaxM];
 #pragma unroll
     for (int r = 0; r < kFusedMaxM; ++r) {
@@ -379,7 +387,7 @@ __device__ __forceinline__ void prepare_codes(const DecodeArgs& A, const DecodeP
   if constexpr (SPLIT)
     lds_post(&sh.ready);
   else
-    __syncthreads();
+    lds_barrier();
 }
 
 // Consumes one 16-byte weight chunk (64 weights of one row, four K-steps of
@@ -406,7 +414,9 @@ __device__ __forceinline__ void mma_chunk(v4i& acc1, v4i& acc4, const v4i (&a)[4
   }
 }
 
-template <int TWW, int MODE, bool FUSED, bool SPLIT>
+// EARLY (ring shape, several token rows): the first weight loads go out
+// before the code preparation instead of after it.
+template <int TWW, int MODE, bool FUSED, bool SPLIT, bool EARLY = false>
 __device__ __forceinline__ void decode_body(const DecodeArgs& A, const DecodeProj& P, int wl,
                                             int8_t* __restrict__ lds, Shared& sh) {
   constexpr int NT = SPLIT ? 512 : 256;
@@ -505,18 +515,28 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& A, const DecodePro
     // kWindow chunks (one round consumes slots 0..W-1; with REFILL each slot
     // is reloaded one round ahead right after it is read; rounds are nested
     // so every executed path is straight-line code)
+    // With several token rows (EARLY) the first W weight loads go out right
+    // behind the activation loads, so the longer code preparation overlaps
+    // them; with one row it is short, and the activation loads fare better
+    // alone.
+    constexpr int W = kWindow;
+    static_assert(W % 4 == 0, "a ring slot always holds the same row tile");
+    v4i ring[W];
+    auto fill = [&]() {
+#pragma unroll
+      for (int d = 0; d < W; ++d) ring[d] = wload(d);
+      __builtin_amdgcn_sched_barrier(0);
+    };
     {
       v4i xin[kXChunks<FUSED>];
       float ws;
       load_codes<FUSED>(A, P, sb, ns, xin, ws);
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (EARLY) fill();
       prepare_codes<false, FUSED>(A, P, ns, xin, ws, lds, sh);
     }
     __builtin_amdgcn_sched_barrier(0);
-    constexpr int W = kWindow;
-    static_assert(W % 4 == 0, "a ring slot always holds the same row tile");
-    v4i ring[W];
-#pragma unroll
-    for (int d = 0; d < W; ++d) ring[d] = wload(d);
+    if constexpr (!EARLY) fill();
     v4i a[4];
     auto round = [&](int base, auto refill) {
       static_for<W>([&](auto dc) {
@@ -630,22 +650,22 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& A, const DecodePro
   }
 }
 
-template <int TWW, int MODE, bool SPLIT>
+template <int TWW, int MODE, bool SPLIT, bool EARLY>
 __device__ __forceinline__ void decode_tw(const DecodeArgs& A, const DecodeProj& P, int wl,
                                           int8_t* lds, Shared& sh) {
   if constexpr (MODE == 0) {
     if (P.x) {
-      decode_body<TWW, MODE, true, SPLIT>(A, P, wl, lds, sh);
+      decode_body<TWW, MODE, true, SPLIT, EARLY>(A, P, wl, lds, sh);
       return;
     }
   }
-  decode_body<TWW, MODE, false, SPLIT>(A, P, wl, lds, sh);
+  decode_body<TWW, MODE, false, SPLIT, EARLY>(A, P, wl, lds, sh);
 }
 
 // SPLIT: 8 waves, for launches that fit on the chip in one wave of WGs (the
 // activation work of a WG then overlaps its weight stream instead of
 // preceding it); otherwise 4 waves, so that several WGs share a CU.
-template <int MODE, bool SPLIT>
+template <int MODE, bool SPLIT, bool EARLY = false>
 __global__ __launch_bounds__(SPLIT ? 512 : 256) void decode_kernel(const DecodeArgs A) {
   extern __shared__ __align__(16) int8_t lds[];
   __shared__ Shared sh;
@@ -658,12 +678,12 @@ __global__ __launch_bounds__(SPLIT ? 512 : 256) void decode_kernel(const DecodeA
   int wl;
   const DecodeProj P = select_proj(A.count, &wl);
   switch (P.tww) {
-    case 1: decode_tw<1, MODE, SPLIT>(A, P, wl, lds, sh); break;
-    case 2: decode_tw<2, MODE, SPLIT>(A, P, wl, lds, sh); break;
+    case 1: decode_tw<1, MODE, SPLIT, EARLY>(A, P, wl, lds, sh); break;
+    case 2: decode_tw<2, MODE, SPLIT, EARLY>(A, P, wl, lds, sh); break;
     case 3:  // split-shape plans only, with the K range unsplit (wk = 1)
-      if constexpr (SPLIT) decode_tw<3, MODE, SPLIT>(A, P, wl, lds, sh);
+      if constexpr (SPLIT) decode_tw<3, MODE, SPLIT, EARLY>(A, P, wl, lds, sh);
       break;
-    default: decode_tw<4, MODE, SPLIT>(A, P, wl, lds, sh); break;
+    default: decode_tw<4, MODE, SPLIT, EARLY>(A, P, wl, lds, sh); break;
   }
 }
 
@@ -774,6 +794,8 @@ hipError_t launch_decode(const DecodeArgs& a, int total_wgs, size_t lds_bytes, h
   const dim3 grid((unsigned)total_wgs);
   if (split)
     decode_kernel<0, true><<<grid, 512, lds_bytes, s>>>(a);
+  else if (a.load_mode == 0 && a.m > 1)
+    decode_kernel<0, false, true><<<grid, 256, lds_bytes, s>>>(a);
   else if (a.load_mode == 0)
     decode_kernel<0, false><<<grid, 256, lds_bytes, s>>>(a);
   else if (a.load_mode == 1)
