@@ -624,7 +624,9 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& A, const DecodePro
   // thread has seen its own acknowledged (memory counter at zero) and the
   // workgroup has met, the counter increment is ordered after all of them,
   // and the last WG reads the sums back with atomics as well.  No cache
-  // write-back fence is needed for data that only atomics touch.
+  // write-back fence is needed for data that only atomics touch.  (Plain
+  // device-coherent stores into per-part slices, read back with coherent
+  // loads, were measured slower than these atomics.)
   if constexpr (FUSED) return;  // fused quantization never splits K across WGs
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
@@ -789,19 +791,38 @@ size_t decode_lds_bytes(int64_t m, int lds_row) {
   return (size_t)m * lds_row + (size_t)4 * kDecodeMaxTww * m * 16 * 4;
 }
 
+// Lets kernel K use up to `bytes` of dynamic LDS (needed above 64 KB); once
+// per instantiation.
+template <auto Kern>
+hipError_t allow_lds(size_t bytes) {
+  if (bytes <= 64 * 1024) return hipSuccess;
+  static const hipError_t e = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(Kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+      (int)decode_lds_bytes(kDecodeMaxM, kDecodeLdsA / kDecodeMaxM + 16));
+  return e;
+}
+
 hipError_t launch_decode(const DecodeArgs& a, int total_wgs, size_t lds_bytes, hipStream_t s) {
   const bool split = a.load_mode == 0 && total_wgs <= device_cu_count();
   const dim3 grid((unsigned)total_wgs);
-  if (split)
-    decode_kernel<0, true><<<grid, 512, lds_bytes, s>>>(a);
-  else if (a.load_mode == 0 && a.m > 1)
-    decode_kernel<0, false, true><<<grid, 256, lds_bytes, s>>>(a);
-  else if (a.load_mode == 0)
-    decode_kernel<0, false><<<grid, 256, lds_bytes, s>>>(a);
-  else if (a.load_mode == 1)
-    decode_kernel<1, false><<<grid, 256, lds_bytes, s>>>(a);
-  else
-    decode_kernel<2, false><<<grid, 256, lds_bytes, s>>>(a);
+  hipError_t e = hipSuccess;
+  if (split) {
+    e = allow_lds<&decode_kernel<0, true>>(lds_bytes);
+    if (e == hipSuccess) decode_kernel<0, true><<<grid, 512, lds_bytes, s>>>(a);
+  } else if (a.load_mode == 0 && a.m > 1) {
+    e = allow_lds<&decode_kernel<0, false, true>>(lds_bytes);
+    if (e == hipSuccess) decode_kernel<0, false, true><<<grid, 256, lds_bytes, s>>>(a);
+  } else if (a.load_mode == 0) {
+    e = allow_lds<&decode_kernel<0, false>>(lds_bytes);
+    if (e == hipSuccess) decode_kernel<0, false><<<grid, 256, lds_bytes, s>>>(a);
+  } else if (a.load_mode == 1) {
+    e = allow_lds<&decode_kernel<1, false>>(lds_bytes);
+    if (e == hipSuccess) decode_kernel<1, false><<<grid, 256, lds_bytes, s>>>(a);
+  } else {
+    e = allow_lds<&decode_kernel<2, false>>(lds_bytes);
+    if (e == hipSuccess) decode_kernel<2, false><<<grid, 256, lds_bytes, s>>>(a);
+  }
+  if (e != hipSuccess) return e;
   return hipGetLastError();
 }
 

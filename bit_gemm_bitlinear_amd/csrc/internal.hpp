@@ -12,7 +12,10 @@ constexpr int kMaxProj = 16;
 // Decode path (M <= 16) limits.
 constexpr int kDecodeMaxM = 16;
 constexpr int kDecodeMaxTww = 4;      // 16-row tiles per wave
-constexpr int kDecodeLdsA = 48 * 1024;
+#ifndef BL_DECODE_LDS_A
+#define BL_DECODE_LDS_A (48 * 1024)
+#endif
+constexpr int kDecodeLdsA = BL_DECODE_LDS_A;  // LDS for a workgroup's activation codes
 
 // Activation codes for the contraction kernels are kept in an internal
 // layout: rows padded to a multiple of 256 codes (zero filled), and inside
