@@ -161,6 +161,7 @@ bl_status run_forward(int32_t count, const ProjIO* io, int64_t m, void* workspac
     J.m = (int32_t)m;
     J.m_pad = L.m_pad;
     J.row_begin = rows;
+    J.paired = L.decode ? 1 : 0;
     rows += L.m_pad;
   }
   qa.count = jobs;

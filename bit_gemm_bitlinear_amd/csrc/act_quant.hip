@@ -149,6 +149,22 @@ __device__ __forceinline__ v4i transpose16(const int32_t (&q)[16]) {
   return o;
 }
 
+// Stores the 16 codes of group g of a row (dword a, byte b = code 4b + a).
+// GEMM order: the group's 16 bytes as they are.  Decode order: within each
+// 32-code block (groups 2i, 2i+1), dwords 0 and 2 of group 2i, dwords 0 and
+// 2 of group 2i+1, then dwords 1 and 3 of each -- the order in which the
+// decode kernel's paired matrix-core ops take them.
+__device__ __forceinline__ void put_group(v4i* __restrict__ qv, int g, v4i v, bool paired) {
+  if (!paired) {
+    qv[g] = v;
+    return;
+  }
+  typedef int32_t v2i __attribute__((ext_vector_type(2)));
+  int8_t* blk = reinterpret_cast<int8_t*>(qv) + 32 * (g >> 1) + 8 * (g & 1);
+  *reinterpret_cast<v2i*>(blk) = v2i{v.x, v.z};
+  *reinterpret_cast<v2i*>(blk + 16) = v2i{v.y, v.w};
+}
+
 __global__ __launch_bounds__(kThreads) void act_quant_public_kernel(
     const uint16_t* __restrict__ x, int k, int8_t* __restrict__ q, float* __restrict__ x_scale) {
   __shared__ uint32_t red[4];
@@ -192,7 +208,7 @@ __device__ __forceinline__ uint32_t wave_reduce(uint32_t v, Op op) {
 __device__ __forceinline__ void quant_row_internal_fast(const uint16_t* __restrict__ xr, int k,
                                                         int ngroups, v4i* __restrict__ qv,
                                                         uint32_t* red, int32_t* qsum,
-                                                        float* x_scale) {
+                                                        float* x_scale, bool paired) {
   constexpr int NB = kBatch;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   v4i lo[NB], hi[NB];
@@ -236,8 +252,10 @@ __device__ __forceinline__ void quant_row_internal_fast(const uint16_t* __restri
 #pragma unroll
       for (int a = 0; a < 4; ++a) usum = __builtin_amdgcn_sad_u8(d[a], 0u, usum);
       ++ng;
-      qv[g] = v4i{(int32_t)(d[0] ^ 0x80808080u), (int32_t)(d[1] ^ 0x80808080u),
-                  (int32_t)(d[2] ^ 0x80808080u), (int32_t)(d[3] ^ 0x80808080u)};
+      put_group(qv, g,
+                v4i{(int32_t)(d[0] ^ 0x80808080u), (int32_t)(d[1] ^ 0x80808080u),
+                    (int32_t)(d[2] ^ 0x80808080u), (int32_t)(d[3] ^ 0x80808080u)},
+                paired);
     }
   }
   int32_t sum = (int32_t)usum - 128 * 16 * ng;
@@ -370,7 +388,7 @@ __global__ __launch_bounds__(kThreads) void act_quant_internal_kernel(const ActQ
   float s = 0.0f;
   if (J.x && (J.k & 7) == 0 && J.ldq / 16 <= kThreads * kBatch) {
     quant_row_internal_fast(J.x + (int64_t)m * J.k, J.k, J.ldq / 16, qv, red, J.qsum + m,
-                            J.x_scale + m);
+                            J.x_scale + m, J.paired != 0);
     return;
   }
   if (J.x) {
@@ -378,7 +396,7 @@ __global__ __launch_bounds__(kThreads) void act_quant_internal_kernel(const ActQ
                   [&](int g, const int32_t(&c)[16]) {
 #pragma unroll
                     for (int i = 0; i < 16; ++i) sum += c[i];
-                    qv[g] = transpose16(c);
+                    put_group(qv, g, transpose16(c), J.paired != 0);
                   });
   } else {
     const int8_t* qin = J.q_in + (int64_t)m * J.k;
@@ -387,7 +405,7 @@ __global__ __launch_bounds__(kThreads) void act_quant_internal_kernel(const ActQ
       load16_codes(qin, J.k, 16 * g, c);
 #pragma unroll
       for (int i = 0; i < 16; ++i) sum += c[i];
-      qv[g] = transpose16(c);
+      put_group(qv, g, transpose16(c), J.paired != 0);
     }
   }
   sum = block_sum_i32(sum, reinterpret_cast<int32_t*>(red));
@@ -420,7 +438,7 @@ hipError_t launch_act_quant_internal(const ActQuantArgs& a, int total_rows, hipS
   bool rows_ok = args.count > 0;
   for (int i = 0; i < args.count; ++i) {
     const ActQuantJob& J = args.j[i];
-    rows_ok = rows_ok && J.x != nullptr && (J.k & 7) == 0;
+    rows_ok = rows_ok && J.x != nullptr && (J.k & 7) == 0 && !J.paired;
     groups = groups > J.ldq / 16 ? groups : J.ldq / 16;
   }
   if (rows_ok && groups <= 64 * 16 && total_rows >= kWaveRowsMin) {

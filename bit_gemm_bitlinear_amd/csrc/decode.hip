@@ -275,9 +275,9 @@ __device__ __forceinline__ void prepare_codes(const DecodeArgs& A, const DecodeP
 #pragma unroll
     for (int i = 0; i < NX; ++i) {
       const int u = xt + NA * i;
-      if (u < units) {
+      if (u < units) {  // already in the decode order (act_quant.hip)
         const int m = u / upr, c = u - m * upr;
-        put_group(lds + m * lrow, c, xin[i]);
+        *reinterpret_cast<v4i*>(lds + m * lrow + 16 * c) = xin[i];
       }
     }
   } else {

@@ -20,6 +20,8 @@ constexpr int kDecodeLdsA = BL_DECODE_LDS_A;  // LDS for a workgroup's activatio
 // Activation codes for the contraction kernels are kept in an internal
 // layout: rows padded to a multiple of 256 codes (zero filled), and inside
 // every group of 16 codes the 4x4 byte transpose described in common.hpp.
+// For the decode kernel the four dwords of each group are further placed in
+// the order its paired matrix-core ops read (see put_group in act_quant.hip).
 constexpr int kKPad = 256;
 
 inline int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
@@ -34,6 +36,7 @@ struct ActQuantJob {
   int32_t* qsum;       // [m] row sums of the codes (written)
   int32_t k, ldq, m, m_pad;
   int32_t row_begin;   // first block of this job in the launch
+  int32_t paired;      // 1: the decode kernel's order (put_group in act_quant.hip), 0: the GEMM's
 };
 
 struct ActQuantArgs {
