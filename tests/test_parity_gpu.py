@@ -147,6 +147,8 @@ ACC_SHAPES = [
     (1, 16, 64), (1, 1, 4), (2, 17, 12), (3, 33, 68), (4, 100, 260), (5, 48, 516),
     (8, 300, 1024), (15, 129, 2048 + 64), (16, 64, 256), (16, 3072, 9216), (1, 200, 16384 + 4),
     (4, 40, 14336 * 2), (16, 20, 8192 + 16),
+    # long rows: a workgroup streams all of K (several ring rounds, codes read from memory)
+    (16, 300, 12288), (8, 100, 65536), (2, 48, 49152 + 64),
     # prefill path (M > 16)
     (17, 16, 64), (33, 130, 260), (128, 128, 256), (200, 257, 516), (300, 64, 12), (129, 40, 2048),
     (100, 257, 1088), (260, 520, 2112),  # K % 128 == 64: a last half-deep slab; ragged N and M
