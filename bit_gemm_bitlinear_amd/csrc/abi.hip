@@ -9,6 +9,7 @@
 #include <algorithm>
 
 #include "internal.hpp"
+#include "prefill_plan.hpp"
 
 using namespace bl;
 
@@ -217,7 +218,6 @@ bl_status run_forward(int32_t count, const ProjIO* io, int64_t m, void* workspac
     int order[kMaxProj];
     for (int i = 0; i < count; ++i) order[i] = i;
     std::stable_sort(order, order + count, [&](int a, int b) { return ks[a] > ks[b]; });
-    int64_t tiles = 0;
     for (int o = 0; o < count; ++o) {
       const int i = order[o];
       PrefillProj& P = pa.p[o];
@@ -232,10 +232,47 @@ bl_status run_forward(int32_t count, const ProjIO* io, int64_t m, void* workspac
       P.k = (int32_t)ks[i];
       P.ldq = (int32_t)round_up(ks[i], kKPad);
       P.tiles_n = (int32_t)((ns[i] + prefill_bn(load_mode) - 1) / prefill_bn(load_mode));
-      pa.tile_begin[o] = (int32_t)tiles;
-      tiles += round_up((int64_t)pa.tiles_m * P.tiles_n, 8);  // XCD-aligned ranges
+      P.ldy = (int32_t)ns[i];
+      P.narrow = 0;
     }
-    for (int o = count; o < kMaxProj; ++o) pa.tile_begin[o] = (int32_t)tiles;
+    // The last tile columns of the last projection become narrow tiles when
+    // that evens out the launch's last round of workgroups.
+    int entries = count;
+    if (load_mode == 0 && count < kMaxProj) {
+      int64_t slabs[kMaxProj], cols[kMaxProj];
+      for (int o = 0; o < count; ++o) {
+        slabs[o] = (pa.p[o].k + 127) / 128;
+        cols[o] = pa.p[o].n;
+      }
+      const int c = plan_narrow_columns<kPrefillBN, kPrefillNarrowBN>(
+          count, slabs, cols, pa.tiles_m, (int64_t)kPrefillWgsPerCu * device_cu_count());
+      if (c > 0) {
+        PrefillProj& W = pa.p[count - 1];
+        const int32_t keep = (W.tiles_n - c) * kPrefillBN;  // columns that stay in wide tiles
+        PrefillProj T = W;
+        T.packed = W.packed + (int64_t)keep * (W.k / 4);
+        T.y = W.y ? W.y + keep : nullptr;
+        T.acc_out = W.acc_out ? W.acc_out + keep : nullptr;
+        T.n = W.n - keep;
+        T.tiles_n = (T.n + kPrefillNarrowBN - 1) / kPrefillNarrowBN;
+        T.narrow = 1;
+        if (keep == 0) {
+          W = T;
+        } else {
+          W.n = keep;
+          W.tiles_n -= c;
+          pa.p[count] = T;
+          entries = count + 1;
+        }
+      }
+    }
+    pa.count = entries;
+    int64_t tiles = 0;
+    for (int o = 0; o < entries; ++o) {
+      pa.tile_begin[o] = (int32_t)tiles;
+      tiles += round_up((int64_t)pa.tiles_m * pa.p[o].tiles_n, 8);  // XCD-aligned ranges
+    }
+    for (int o = entries; o < kMaxProj; ++o) pa.tile_begin[o] = (int32_t)tiles;
     if (tiles >= (int64_t(1) << 31)) return BL_ESHAPE;
     if (launch_prefill(pa, (int)tiles, stream) != hipSuccess) return BL_EHIP;
   }

@@ -104,8 +104,14 @@ constexpr int kPrefillBM = 128;  // token rows per tile
 #define BL_PREFILL_BN 256
 #endif
 constexpr int kPrefillBN = BL_PREFILL_BN;  // output columns per tile, 16-byte aligned weight rows
+constexpr int kPrefillNarrowBN = 128;  // the same, narrow tiles (the last round of a launch)
 constexpr int kPrefillRegBN = 256;  // output columns per tile, other weight rows
 inline int prefill_bn(int load_mode) { return load_mode == 0 ? kPrefillBN : kPrefillRegBN; }
+#ifndef BL_PREFILL_WGS_PER_CU
+#define BL_PREFILL_WGS_PER_CU 2
+#endif
+// Workgroups of the main prefill kernel that the LDS and registers allow per CU.
+constexpr int kPrefillWgsPerCu = BL_PREFILL_WGS_PER_CU;
 
 struct PrefillProj {
   const uint8_t* packed;
@@ -115,8 +121,10 @@ struct PrefillProj {
   const int8_t* q;      // internal layout [m_pad][ldq]
   const float* x_scale;
   const int32_t* qsum;
-  int32_t n, k, ldq;
-  int32_t tiles_n;      // ceil(n / BN)
+  int32_t n, k, ldq;    // n: output columns of this entry
+  int32_t tiles_n;      // ceil(n / tile width)
+  int32_t ldy;          // output row stride (elements of y or acc_out)
+  int32_t narrow;       // 1: tiles of kPrefillNarrowBN columns (main variant only)
 };
 
 struct PrefillArgs {

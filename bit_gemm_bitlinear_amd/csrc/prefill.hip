@@ -228,9 +228,9 @@ __global__ __launch_bounds__(kThreads) void prefill_reg_kernel(const PrefillArgs
         if (n >= P.n) continue;
         const int32_t v = acc[i][f][r] - qs;
         if (P.y)
-          *G(P.y + (int64_t)m * P.n + n) = dequant_bf16_row(v, rd);
+          *G(P.y + (int64_t)m * P.ldy + n) = dequant_bf16_row(v, rd);
         else
-          *G(P.acc_out + (int64_t)m * P.n + n) = v;
+          *G(P.acc_out + (int64_t)m * P.ldy + n) = v;
       }
     }
   }
@@ -346,31 +346,16 @@ struct Stager {
   }
 };
 
-#ifndef BL_PREFILL_WGS_PER_CU
-#define BL_PREFILL_WGS_PER_CU 2
-#endif
-constexpr int kPrefillWgsPerCu = BL_PREFILL_WGS_PER_CU;  // workgroups the LDS and registers allow per CU
-
-// EC = columns of the tile whose int32 sums the epilogue stages in LDS at
-// once (128 rows x (4 EC + 16) bytes).
 // WMI = 32-row tiles per wave.  With WMI = 4 each wave covers all 128 rows of
 // the tile and its own columns, so every weight column is expanded once per
 // workgroup; with WMI = 2 two waves share (and both expand) each column.
-template <int BNT, int NST, int WMI, int NW, int BK, int EC>
-__global__ __launch_bounds__(64 * NW)
-__attribute__((amdgpu_waves_per_eu(NW * kPrefillWgsPerCu / 4))) void prefill_kernel(const PrefillArgs A) {
+// One output tile (BM rows x BNT columns) of projection P.
+template <int BNT, int NST, int WMI, int NW, int BK>
+__device__ __forceinline__ void prefill_tile(const PrefillArgs& A, const PrefillProj& P, int tm, int tn,
+                                             int8_t* __restrict__ smem) {
   using K = Cfg<BNT, WMI, NW, BK>;
   constexpr int kNT = K::kNT;
   constexpr int WNF = K::WNF;
-  extern __shared__ __align__(16) int8_t smem[];
-  __shared__ int32_t s_qs[BM];
-  __shared__ RowDiv s_rd[BM];
-  int pi = 0;
-#pragma unroll
-  for (int i = 1; i < kMaxProj; ++i) pi += (i < A.count && (int)blockIdx.x >= A.tile_begin[i]);
-  const PrefillProj& P = A.p[pi];
-  int tm, tn;
-  if (!tile_of((int)blockIdx.x - A.tile_begin[pi], A.tiles_m, P.tiles_n, &tm, &tn)) return;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int lj = lane & 31, lg = lane >> 5;
@@ -381,22 +366,22 @@ __attribute__((amdgpu_waves_per_eu(NW * kPrefillWgsPerCu / 4))) void prefill_ker
   const int S = (P.k + BK - 1) / BK;
   const bool bf = P.y != nullptr;
 
-  // per-row code sums and divisors, fetched now (vector loads, retired in
-  // order ahead of the slab loads) and published by the loop's barriers
-  if (tid < BM) {
-    const int m = min(m0 + tid, A.m - 1);
-    const float ws = bf ? load_f32_vmem(P.w_scale) : 0.0f;
-    s_qs[tid] = *G(P.qsum + m);
-    s_rd[tid] = row_div_setup(bf ? *G(P.x_scale + m) * ws : 1.0f);
-  }
-
+  // This lane's token rows, one per 32-row subtile: m0 + wm0 + 32 i + lj.
+  // The accumulators start from minus the row's code sum (the contraction
+  // with codes c = u + 1 then ends at the sum over q * u).
+  const float ws = bf ? load_f32_vmem(P.w_scale) : 0.0f;
+  float xs[WMI];
   v16i acc[WMI][WNF];
 #pragma unroll
-  for (int i = 0; i < WMI; ++i)
+  for (int i = 0; i < WMI; ++i) {
+    const int m = min(m0 + wm0 + 32 * i + lj, A.m - 1);
+    const int32_t q0 = -*G(P.qsum + m);
+    xs[i] = bf ? *G(P.x_scale + m) : 1.0f;
 #pragma unroll
     for (int f = 0; f < WNF; ++f)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][f][r] = 0;
+      for (int r = 0; r < 16; ++r) acc[i][f][r] = q0;
+  }
 
   const Stager<BNT, WMI, NW, BK> stager(P, m0, n0);
 #pragma unroll
@@ -448,103 +433,108 @@ __attribute__((amdgpu_waves_per_eu(NW * kPrefillWgsPerCu / 4))) void prefill_ker
       for (int f = 0; f < WNF; ++f) {
         const v4i bq = decode16((uint32_t)b[f][ks >> 2][ks & 3]);
 #pragma unroll
-        for (int i = 0; i < WMI; ++i) acc[i][f] = mfma_32x32x32_i8(a[ks & 1][i], bq, acc[i][f]);
+        for (int i = 0; i < WMI; ++i) acc[i][f] = mfma_32x32x32_i8(bq, a[ks & 1][i], acc[i][f]);
       }
     }
   }
 
-  // epilogue: lane holds C[8*(r/4) + 4*lg + r%4][lj] of each 32x32 tile.
-  // The raw sums go to LDS as int32 rows (the stage buffers are free once
-  // every wave is past the loop), kEpiCols columns per pass; then each
-  // thread takes one row: its code sum and divisor are read once, and 8
-  // consecutive outputs at a time are converted and stored as 16-byte
-  // (bf16) or 32-byte (int32) pieces.
-  constexpr int orow = EC + 4;  // int32 words per staged row (16 bytes of padding)
-  static_assert(BNT % EC == 0 && EC % (32 * WNF) == 0, "a wave's columns lie in one pass");
-  int32_t* st = reinterpret_cast<int32_t*>(smem);
-  constexpr int TPR = kNT / BM;      // threads per row
-  constexpr int NPT = EC / 8 / TPR;  // 8-output pieces per thread and pass
-  static_assert(kNT % BM == 0 && (EC / 8) % TPR == 0, "rows split evenly over the threads");
-  const int rl = tid / TPR, m = m0 + rl;
-  const int c0 = tid % TPR;  // pieces c0, c0 + TPR, ...: a row's threads store adjacent pieces
-  const int32_t q = s_qs[rl];
-  const RowDiv d = s_rd[rl];
+  // Epilogue.  The weights are the matrix core's first operand, so lane
+  // (lj, lg) holds, for subtiles i and f, token row m0 + wm0 + 32 i + lj at
+  // columns wn0 + 32 f + 8 a + 4 lg + b in acc[i][f][4 a + b] (a, b = 0..3):
+  // runs of 4 columns of one row.  No LDS and no barrier: each lane divides
+  // by its row's divisor, and for bf16 output one swap with the lane 32 away
+  // turns two runs of 4 into 8 consecutive columns (a 16-byte store).
 #pragma unroll
-  for (int pass = 0; pass < BNT / EC; ++pass) {
-    __syncthreads();
-    if (wn0 / EC == pass) {
-#pragma unroll
-      for (int i = 0; i < WMI; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int ml = wm0 + 32 * i + 8 * (r >> 2) + 4 * lg + (r & 3);
-#pragma unroll
-          for (int f = 0; f < WNF; ++f)
-            st[ml * orow + wn0 - pass * EC + 32 * f + lj] = acc[i][f][r];
-        }
-    }
-    __syncthreads();
-    if (m >= A.m) continue;
-    const int32_t* srow = st + rl * orow + 8 * c0;
-    v4i raw[NPT][2];
-#pragma unroll
-    for (int j = 0; j < NPT; ++j) {
-      raw[j][0] = *reinterpret_cast<const v4i*>(srow + 8 * TPR * j);
-      raw[j][1] = *reinterpret_cast<const v4i*>(srow + 8 * TPR * j + 4);
-    }
-    const int nb = n0 + pass * EC + 8 * c0;  // first output column of piece 0
+  for (int i = 0; i < WMI; ++i) {
+    const int m = m0 + wm0 + 32 * i + lj;
+    const bool row_ok = m < A.m;
     if (!bf) {
-      const bool wide = (P.n & 3) == 0;  // output rows are 16-byte aligned
+      const bool wide = (P.ldy & 3) == 0;  // output rows are 16-byte aligned
+      int32_t* yrow = P.acc_out + (int64_t)m * P.ldy;
 #pragma unroll
-      for (int j = 0; j < NPT; ++j) {
-        const int n = nb + 8 * TPR * j;
-        if (n >= P.n) continue;
-        const v4i lo = raw[j][0] - q, hi = raw[j][1] - q;
-        int32_t* dst = P.acc_out + (int64_t)m * P.n + n;
-        if (wide && n + 8 <= P.n) {
-          *G(reinterpret_cast<v4i*>(dst)) = lo;
-          *G(reinterpret_cast<v4i*>(dst + 4)) = hi;
-        } else {
-          const int32_t v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-          for (int e = 0; e < 8 && n + e < P.n; ++e) *G(dst + e) = v[e];
+      for (int f = 0; f < WNF; ++f)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const int n = n0 + wn0 + 32 * f + 8 * a + 4 * lg;
+          if (!row_ok || n >= P.n) continue;
+          const v4i v = {acc[i][f][4 * a], acc[i][f][4 * a + 1], acc[i][f][4 * a + 2], acc[i][f][4 * a + 3]};
+          if (wide && n + 4 <= P.n) {
+            *G(reinterpret_cast<v4i*>(yrow + n)) = v;
+          } else {
+            for (int e = 0; e < 4 && n + e < P.n; ++e) *G(yrow + n + e) = v[e];
+          }
         }
-      }
       continue;
     }
-    const bool wide = (P.n & 7) == 0;  // output rows are 16-byte aligned
-    auto emit = [&](auto fast) {
+    const RowDiv d = row_div_setup(xs[i] * ws);
+    const bool wide = (P.ldy & 7) == 0;  // output rows are 16-byte aligned
+    uint16_t* yrow = P.y + (int64_t)m * P.ldy;
 #pragma unroll
-      for (int j = 0; j < NPT; ++j) {
-        const int n = nb + 8 * TPR * j;
-        if (n >= P.n) continue;
-        const int32_t v[8] = {raw[j][0].x - q, raw[j][0].y - q, raw[j][0].z - q, raw[j][0].w - q,
-                              raw[j][1].x - q, raw[j][1].y - q, raw[j][1].z - q, raw[j][1].w - q};
-        float yf[8];
+    for (int f = 0; f < WNF; ++f) {
+      float yf[16];
+      if (d.fast) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          yf[e] = decltype(fast)::value ? row_div_fast((float)v[e], d.d, d.y) : (float)v[e] / d.d;
-        uint16_t* dst = P.y + (int64_t)m * P.n + n;
-        if (wide && n + 8 <= P.n) {
-          *G(reinterpret_cast<v4i*>(dst)) =
-              v4i{(int32_t)pack_bf16x2(yf[0], yf[1]), (int32_t)pack_bf16x2(yf[2], yf[3]),
-                  (int32_t)pack_bf16x2(yf[4], yf[5]), (int32_t)pack_bf16x2(yf[6], yf[7])};
-        } else {
-          for (int e = 0; e < 8 && n + e < P.n; ++e) *G(dst + e) = f32_to_bf16(yf[e]);
+        for (int r = 0; r < 16; ++r) yf[r] = row_div_fast((float)acc[i][f][r], d.d, d.y);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) yf[r] = (float)acc[i][f][r] / d.d;
+      }
+      // pk[2a], pk[2a+1]: columns 8a + 4lg + 0..3 as bf16 pairs
+      uint32_t pk[8];
+#pragma unroll
+      for (int h = 0; h < 8; ++h) pk[h] = pack_bf16x2(yf[2 * h], yf[2 * h + 1]);
+      // Swap lanes 32-63 of the first register with lanes 0-31 of the
+      // second: lanes 0-31 then hold columns 0-7 (pk[0..3]) and 16-23
+      // (pk[4..7]) of the 32-column subtile, lanes 32-63 columns 8-15 and
+      // 24-31.
+#pragma unroll
+      for (int h = 0; h < 8; h += 4) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const auto sw = __builtin_amdgcn_permlane32_swap(pk[h + t], pk[h + 2 + t], false, false);
+          pk[h + t] = sw[0];
+          pk[h + 2 + t] = sw[1];
         }
       }
-    };
-    if (d.fast)
-      emit(std::true_type{});
-    else
-      emit(std::false_type{});
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int n = n0 + wn0 + 32 * f + 16 * h + 8 * lg;
+        if (!row_ok || n >= P.n) continue;
+        const uint32_t* w = pk + 4 * h;
+        if (wide && n + 8 <= P.n) {
+          *G(reinterpret_cast<v4i*>(yrow + n)) = v4i{(int32_t)w[0], (int32_t)w[1], (int32_t)w[2], (int32_t)w[3]};
+        } else {
+          for (int e = 0; e < 8 && n + e < P.n; ++e) *G(yrow + n + e) = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+        }
+      }
+    }
   }
 }
 
-// Slab buffers, wave layout, slab depth and epilogue pass width of the main
-// variant: 4 waves of 64 x 128 outputs, slabs of 128 codes, two buffers of
-// 24 KB and 128-column epilogue passes (67.6 KB) -- small enough that two
-// workgroups share a CU, so that one's epilogue (vector ALU work) overlaps
-// the other's matrix-core loop.
+// Tiles are BNT = kPrefillBN columns wide, or kPrefillNarrowBN for the
+// entries marked narrow: the host gives the tiles that would otherwise run
+// in a last, partly filled round of workgroups that width, so that the
+// round fills the chip and ends sooner.
+template <int NST, int WMI, int NW, int BK>
+__global__ __launch_bounds__(64 * NW)
+__attribute__((amdgpu_waves_per_eu(NW * kPrefillWgsPerCu / 4))) void prefill_kernel(const PrefillArgs A) {
+  extern __shared__ __align__(16) int8_t smem[];
+  int pi = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxProj; ++i) pi += (i < A.count && (int)blockIdx.x >= A.tile_begin[i]);
+  const PrefillProj& P = A.p[pi];
+  int tm, tn;
+  if (!tile_of((int)blockIdx.x - A.tile_begin[pi], A.tiles_m, P.tiles_n, &tm, &tn)) return;
+  if (P.narrow)
+    prefill_tile<kPrefillNarrowBN, NST, WMI, NW, BK>(A, P, tm, tn, smem);
+  else
+    prefill_tile<kPrefillBN, NST, WMI, NW, BK>(A, P, tm, tn, smem);
+}
+
+// Slab buffers, wave layout and slab depth of the main variant: 4 waves of
+// 64 x 128 outputs, slabs of 128 codes, two buffers of 24 KB -- small enough
+// that two workgroups share a CU, so that one's epilogue (vector ALU work)
+// overlaps the other's matrix-core loop.
 #ifndef BL_PREFILL_NST
 #define BL_PREFILL_NST 2
 #endif
@@ -557,24 +547,20 @@ __attribute__((amdgpu_waves_per_eu(NW * kPrefillWgsPerCu / 4))) void prefill_ker
 #ifndef BL_PREFILL_BK
 #define BL_PREFILL_BK 128
 #endif
-#ifndef BL_PREFILL_EC
-#define BL_PREFILL_EC 128
-#endif
 
 }  // namespace
 
 hipError_t launch_prefill(const PrefillArgs& a, int total_tiles, hipStream_t s) {
   if (a.load_mode == 0) {
     constexpr int BNT = BL_PREFILL_BN, NST = BL_PREFILL_NST, WMI = BL_PREFILL_WMI,
-                  NW = BL_PREFILL_NW, BK = BL_PREFILL_BK, EC = BL_PREFILL_EC;
-    constexpr size_t stages = (size_t)NST * Cfg<BNT, WMI, NW, BK>::kStageBytes;
-    constexpr size_t out = (size_t)BM * (EC * 4 + 16);  // int32 sums staged by rows
-    constexpr size_t lds = stages > out ? stages : out;
+                  NW = BL_PREFILL_NW, BK = BL_PREFILL_BK;
+    static_assert(BNT >= kPrefillNarrowBN, "the wide tiles' slab buffers hold the narrow ones'");
+    constexpr size_t lds = (size_t)NST * Cfg<BNT, WMI, NW, BK>::kStageBytes;
     static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&prefill_kernel<BNT, NST, WMI, NW, BK, EC>),
+        reinterpret_cast<const void*>(&prefill_kernel<NST, WMI, NW, BK>),
         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (attr != hipSuccess) return attr;
-    prefill_kernel<BNT, NST, WMI, NW, BK, EC><<<(unsigned)total_tiles, 64 * NW, lds, s>>>(a);
+    prefill_kernel<NST, WMI, NW, BK><<<(unsigned)total_tiles, 64 * NW, lds, s>>>(a);
   } else if (a.load_mode == 1) {
     prefill_reg_kernel<1><<<(unsigned)total_tiles, kThreads, 0, s>>>(a);
   } else {

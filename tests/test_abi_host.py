@@ -285,3 +285,66 @@ def test_row_division_matches_ieee_division(tmp_path):
     assert bad == 0
     # the correction step matters: a bare multiply by the reciprocal is off often
     assert corrected > 1000
+
+
+# ------------------------------------------------------------------ prefill launch plan
+
+PLAN_SRC = r'''
+#include "prefill_plan.hpp"
+#include <cstdio>
+#include <queue>
+#include <random>
+#include <functional>
+
+// every tile on its own: a min-heap of slot free times
+static double brute_end(const bl::TileClass* c, int n, long slots) {
+  std::priority_queue<double, std::vector<double>, std::greater<double>> h;
+  for (long i = 0; i < slots; ++i) h.push(0.0);
+  double end = 0;
+  for (int k = 0; k < n; ++k)
+    for (long t = 0; t < c[k].count; ++t) {
+      double s = h.top(); h.pop(); h.push(s + c[k].us); if (s + c[k].us > end) end = s + c[k].us;
+    }
+  return end;
+}
+
+int main() {
+  std::mt19937 g(7);
+  int mismatches = 0;
+  for (int trial = 0; trial < 300; ++trial) {
+    int n = 1 + g() % 5;
+    long slots = 1 + g() % 600;
+    bl::TileClass c[5];
+    for (int k = 0; k < n; ++k) c[k] = bl::TileClass{(int64_t)(g() % 900), (double)(1 + g() % 80)};
+    double a = bl::list_schedule_end(c, n, slots), b = brute_end(c, n, slots);
+    if (a != b) ++mismatches;
+  }
+  // FFN of a d=2560 / ffn=6912 layer at 2048 tokens, launch order down, gate, up
+  const int64_t slabs[3] = {54, 20, 20}, cols[3] = {2560, 6912, 6912};
+  int ffn = bl::plan_narrow_columns<256, 128>(3, slabs, cols, 16, 512);
+  // the same layer at 256 tokens: 2 x 64 tiles fit one round
+  int small = bl::plan_narrow_columns<256, 128>(3, slabs, cols, 2, 512);
+  // four whole rounds of equal tiles: nothing to even out
+  const int64_t s1[1] = {20}, c1[1] = {256 * 128};
+  int whole = bl::plan_narrow_columns<256, 128>(1, s1, c1, 16, 512);
+  printf("%d %d %d %d\n", mismatches, ffn, small, whole);
+  return 0;
+}
+'''
+
+
+def test_prefill_plan(tmp_path):
+    """The grouped list-scheduling model equals a per-tile simulation, and
+    the plan narrows the tiles of the FFN's partly filled last round (160
+    tiles = 10 tile columns of the up projection) and nothing in launches
+    that fill whole rounds."""
+    src = tmp_path / "plan_check.cpp"
+    exe = tmp_path / "plan_check"
+    src.write_text(PLAN_SRC)
+    subprocess.run(["g++", "-O2", "-std=c++17", "-I", CSRC, str(src), "-o", str(exe)], check=True)
+    mismatches, ffn, small, whole = map(int, subprocess.run(
+        [str(exe)], capture_output=True, text=True, check=True).stdout.split())
+    assert mismatches == 0
+    assert ffn == 10
+    assert small == 0
+    assert whole == 0

@@ -152,6 +152,9 @@ ACC_SHAPES = [
     # prefill path (M > 16)
     (17, 16, 64), (33, 130, 260), (128, 128, 256), (200, 257, 516), (300, 64, 12), (129, 40, 2048),
     (100, 257, 1088), (260, 520, 2112),  # K % 128 == 64: a last half-deep slab; ragged N and M
+    # more tiles than one round of workgroups on 256 CUs: the last tile column
+    # runs as narrow tiles (ragged, and with output rows not 16-byte aligned)
+    (2048, 8400, 256), (2048, 8401, 256),
 ]
 
 
@@ -235,6 +238,33 @@ def test_golden_cases(bl):
         assert host_bits(y).tolist() == c["y_bits"]
         acc = bl.forward_acc(torch.tensor(c["q"], dtype=torch.int8, device=DEV), packed)
         assert acc.cpu().numpy().tolist() == c["acc"]
+
+
+# Grouped prefill launches with more tiles than one round of workgroups
+# (2 per CU on 256 CUs), shaped so that the launch plan runs the last tile
+# columns of the last projection as narrow tiles: 4 of 12 columns (narrow
+# part 953 columns, ragged), 1 of 2 (44 columns), and the whole projection
+# (200 columns, 25 row tiles).
+NARROW_LAYERS = [
+    (2000, [(7000, 2048), (3001, 1088)]),
+    (3000, [(5000, 2048), (300, 1024)]),
+    (3200, [(5000, 2048), (200, 1024)]),
+]
+
+
+@pytest.mark.parametrize("m,shapes", NARROW_LAYERS)
+def test_grouped_prefill_narrow_tail(bl, m, shapes):
+    xs, ps, ss, refs = [], [], [], []
+    for i, (n, k) in enumerate(shapes):
+        x, w = wls.random_case(90 + m + i, m, n, k)
+        p, s = bl.pack_weights(torch.from_numpy(w).to(DEV))
+        xs.append(dev_bf16(x))
+        ps.append(p)
+        ss.append(s)
+        refs.append(oracle.forward(x, *oracle.pack_weights(w)))
+    ys = bl.forward_grouped(xs, ps, ss)
+    for (n, k), y, r in zip(shapes, ys, refs):
+        assert_bf16_close(host_bits(y), r, f"grouped prefill {m}x{n}x{k}")
 
 
 # ------------------------------------------------------------------ full-size workloads
