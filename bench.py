@@ -21,7 +21,8 @@ Profiling helpers (the summaries under profiles/ are written by these):
 
     python bench.py --pmc-probe ...            eager steps + a copy kernel of known size
     python bench.py --summarize-stats DIR      text summary of a rocprofv3 --stats run
-    python bench.py --summarize-pmc FDIR WDIR  HBM traffic per dispatch from FETCH_SIZE /
+    python bench.py --summarize-pmc FDIR WDIR [--pmc-kernel decode|prefill]
+                                               HBM traffic per dispatch from FETCH_SIZE /
                                                WRITE_SIZE runs, scaled by the copy kernel
 """
 
@@ -45,10 +46,22 @@ METRIC = "BitLinear decode GB/s of packed weights (% HBM peak); prefill int8 TOP
 HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, published
 MFMA_I8_PEAK_TOPS = 5000.0  # MI355X dense int8 matrix peak, published
 
-# Sources the decode kernel is built from; a traffic figure measured on other
-# sources is stale and is not reported.
-DECODE_SOURCES = ["decode.hip", "common.hpp", "row_div.hpp", "internal.hpp"]
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_kernel_decode_1b_m1_traffic.txt")
+# Per kernel: the name rocprofv3 reports, the sources it is built from (a
+# traffic figure measured on other sources is stale and is not reported) and
+# the committed summary of its HBM traffic.
+PMC_KERNELS = {
+    "decode": {
+        "name": "decode_kernel",
+        "sources": ["decode.hip", "common.hpp", "row_div.hpp", "internal.hpp"],
+        "file": os.path.join(ROOT, "profiles", "decode_kernel_decode_1b_m1_traffic.txt"),
+    },
+    "prefill": {
+        "name": "prefill_kernel",
+        "sources": ["prefill.hip", "prefill_plan.hpp", "abi.hip", "common.hpp", "row_div.hpp",
+                    "internal.hpp"],
+        "file": os.path.join(ROOT, "profiles", "prefill_kernel_prefill_2b_m2048_traffic.txt"),
+    },
+}
 COPY_PROBE_MIB = 512
 
 
@@ -70,15 +83,17 @@ def parse():
                     help="eager steps of the workload, then a copy kernel of known size")
     ap.add_argument("--summarize-stats", metavar="DIR")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--pmc-kernel", choices=sorted(PMC_KERNELS), default="decode",
+                    help="kernel whose traffic --summarize-pmc reports")
     ap.add_argument("--command", default="", help="command line recorded in a summary")
     ap.add_argument("--curve", action="store_true",
                     help="decode GB/s against weight bytes for one projection (1 MiB .. 1 GiB)")
     return ap.parse_args()
 
 
-def decode_sources_sha256() -> str:
+def sources_sha256(kind: str) -> str:
     h = hashlib.sha256()
-    for name in DECODE_SOURCES:
+    for name in PMC_KERNELS[kind]["sources"]:
         with open(os.path.join(ROOT, "bit_gemm_bitlinear_amd", "csrc", name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()
@@ -228,7 +243,8 @@ def prefill_measure(torch, bl, wls, dev, steps):
                                   "vendor GEMM library) on the same three shapes",
         "ms_per_step": ev_s / n * 1e3, "ops_per_step": wl.ops(m), "steps": n,
         "roofline": {"bound": "mfma", "achieved": tops, "peak": MFMA_I8_PEAK_TOPS,
-                     "unit": "TFLOP/s", "frac": tops / MFMA_I8_PEAK_TOPS, "traffic": None},
+                     "unit": "TFLOP/s", "frac": tops / MFMA_I8_PEAK_TOPS,
+                     "traffic": read_traffic("prefill")},
     }
 
 
@@ -296,11 +312,11 @@ def _per_kernel_counter(d, counter):
     return by_name
 
 
-def summarize_pmc(fdir, wdir, command):
+def summarize_pmc(fdir, wdir, command, kind):
     fetch = _per_kernel_counter(fdir, "FETCH_SIZE")
     write = _per_kernel_counter(wdir, "WRITE_SIZE")
     copy_name = next((n for n in fetch if "neg" in n.lower()), None)
-    dec_name = next((n for n in fetch if "decode_kernel" in n), None)
+    dec_name = next((n for n in fetch if PMC_KERNELS[kind]["name"] in n), None)
     if copy_name is None or dec_name is None:
         sys.exit(f"kernels not found: {list(fetch)[:8]}")
     copy_bytes = COPY_PROBE_MIB * (1 << 20)
@@ -311,9 +327,9 @@ def summarize_pmc(fdir, wdir, command):
     dw = float(np.mean(write[dec_name]))
     traffic = df * 1024 * f_fac + dw * 1024 * w_fac
     lines = [
-        "# HBM traffic of the decode kernel (rocprofv3 PMC, one counter per run)",
+        f"# HBM traffic of the {kind} kernel (rocprofv3 PMC, one counter per run)",
         f"command: {command}",
-        f"decode_sources_sha256: {decode_sources_sha256()}",
+        f"sources_sha256: {sources_sha256(kind)}",
         f"kernel: {dec_name[:140]}",
         f"dispatches: {len(fetch[dec_name])} (FETCH_SIZE run), {len(write.get(dec_name, []))} (WRITE_SIZE run)",
         f"FETCH_SIZE_KiB_per_dispatch: {df:.1f}",
@@ -330,15 +346,15 @@ def summarize_pmc(fdir, wdir, command):
     print("\n".join(lines))
 
 
-def read_traffic():
-    """Traffic figure of the committed PMC summary, or None if it is missing or
-    was measured on other decode-kernel sources."""
+def read_traffic(kind):
+    """Traffic figure of the committed PMC summary of a kernel, or None if it
+    is missing or was measured on other sources of that kernel."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(PMC_KERNELS[kind]["file"]) as f:
             kv = dict(l.split(": ", 1) for l in f.read().splitlines() if ": " in l)
     except OSError:
         return None
-    if kv.get("decode_sources_sha256") != decode_sources_sha256():
+    if kv.get("sources_sha256") != sources_sha256(kind):
         return None
     try:
         return float(kv["traffic_bytes_per_dispatch"])
@@ -353,14 +369,20 @@ def pmc_probe(torch, bl, wls, args):
     copies = max(1, int(np.ceil(args.rotate_bytes / wl.packed_bytes)))
     calls = prepare(torch, bl, wls, wl, m, copies, dev)
     time_steps(torch, calls, args.steps, 0, eager=True)
+    del calls
+    # the prefill workload, a few eager steps (one weight copy, as timed)
+    pwl = wls.WORKLOADS["prefill_2b_m2048"]
+    pcalls = prepare(torch, bl, wls, pwl, pwl.ms[0], 1, dev)
+    time_steps(torch, pcalls, 8, 0, eager=True)
+    del pcalls
     n = COPY_PROBE_MIB * (1 << 20) // 4
     a = torch.ones(n, dtype=torch.float32, device=dev)
     b = torch.empty_like(a)
     for _ in range(3):
         torch.neg(a, out=b)
     torch.cuda.synchronize()
-    print(f"pmc probe: {args.steps} eager steps of {wl.name}, 3 copies of {COPY_PROBE_MIB} MiB",
-          flush=True)
+    print(f"pmc probe: {args.steps} eager steps of {wl.name}, 8 of prefill_2b_m2048, "
+          f"3 copies of {COPY_PROBE_MIB} MiB", flush=True)
 
 
 def bandwidth_curve(torch, bl, dev, k=4096, sizes_mib=(1, 4, 16, 64, 256, 1024)):
@@ -389,7 +411,7 @@ def main():
     if args.summarize_stats:
         return summarize_stats(args.summarize_stats, args.command)
     if args.summarize_pmc:
-        return summarize_pmc(*args.summarize_pmc, args.command)
+        return summarize_pmc(*args.summarize_pmc, args.command, args.pmc_kernel)
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
               "(see the sharding notes in DESIGN.md); run with --gpus 1", file=sys.stderr)
@@ -414,7 +436,7 @@ def main():
     host_s, ev_s, n = time_steps(torch, calls, args.steps, args.warmup, args.eager)
     per_step = ev_s / n
     gbs = wl.packed_bytes / per_step / 1e9
-    traffic = read_traffic() if (args.workload == "decode_1b_m1" and m == 1) else None
+    traffic = read_traffic("decode") if (args.workload == "decode_1b_m1" and m == 1) else None
 
     out = {
         "metric": METRIC,
