@@ -242,7 +242,10 @@ __global__ __launch_bounds__(kThreads) void prefill_reg_kernel(const PrefillArgs
 // per lane, lane L's bytes landing at dst + 16 L), through a ring of NST
 // slab buffers: while slab s is multiplied, slabs up to s+NST-1 are in
 // flight.  No staging registers, one barrier per slab.  The tile is BM=128
-// tokens x BNT outputs; a slab is BK codes deep (128 or 256).
+// tokens x BNT outputs (256, or 128 for the entries the host marks narrow); a
+// slab is BK codes deep (128 or 256).  The expanded weights are the matrix
+// core's first operand and the activation codes its second, so each lane's
+// sums belong to one token row (see the epilogue).
 //
 // LDS image of a slab (KA = BK/16 chunks of 16 B per A row, KB = BK/64 per
 // B column):
