@@ -447,6 +447,8 @@ hipError_t launch_act_quant_internal(const ActQuantArgs& a, int total_rows, hipS
     const dim3 grid((unsigned)(row_blocks + zero_blocks));
     if (groups <= 64 * 4)
       act_quant_rows_kernel<4><<<grid, kThreads, 0, s>>>(args);
+    else if (groups <= 64 * 7)
+      act_quant_rows_kernel<7><<<grid, kThreads, 0, s>>>(args);
     else if (groups <= 64 * 8)
       act_quant_rows_kernel<8><<<grid, kThreads, 0, s>>>(args);
     else
