@@ -187,6 +187,44 @@ def copy_bandwidth(torch, dev, mib=1024, reps=10):
     return 2 * mib * (1 << 20) / s / 1e9
 
 
+def measured_ceilings(torch, dev, reps=10):
+    """The GPU's achievable ceilings from the probe kernels
+    (include/bitlinear_probes.h): a streaming read of 1 GiB, and the int8
+    matrix-core loop with prefill-like operands (random activation bytes and
+    weight codes, changing every operation) and with constant operands."""
+    from bit_gemm_bitlinear_amd import probes
+
+    def timed(fn, n):
+        fn()
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        for _ in range(n):
+            fn()
+        ev1.record()
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) / 1e3 / n
+
+    nbytes = 1 << 30
+    buf = torch.randint(-128, 128, (nbytes,), dtype=torch.int8, device=dev)
+    sink = torch.zeros(probes.SINK_WORDS, dtype=torch.int32, device=dev)
+    read_s = timed(lambda: probes.stream_read(buf, sink), reps)
+    del buf
+    wgs = torch.cuda.get_device_properties(dev).multi_processor_count * 4
+    msink = torch.empty(wgs * 256, dtype=torch.int32, device=dev)
+    iters = 2048
+    ops = probes.OPS_PER_ROUND_PER_WG * iters * wgs
+    rand_s = timed(lambda: probes.mfma_i8(wgs, iters, 1, msink), reps)
+    const_s = timed(lambda: probes.mfma_i8(wgs, iters, 0, msink), reps)
+    return {
+        "stream_read_GBs": nbytes / read_s / 1e9,
+        "mfma_i8_loop_TOPS": ops / rand_s / 1e12,
+        "mfma_i8_loop_const_TOPS": ops / const_s / 1e12,
+        "note": "probe kernels: 16-byte streaming read of 1 GiB; v_mfma_i32_32x32x32_i8 loop "
+                "from registers, prefill-like operands (and constant operands)",
+    }
+
+
 def cpu_baseline(wls, wl, m, budget_s):
     """The oracle as it stands, on host cores, over whole passes of the layer
     (all projections at token count m) until about `budget_s` seconds."""
@@ -478,6 +516,12 @@ def main():
         del calls
     if not args.no_prefill:
         out["prefill"] = prefill_measure(torch, bl, wls, dev, args.steps)
+    if not args.no_context:
+        peaks = measured_ceilings(torch, dev)
+        peaks["decode_frac_of_stream_read"] = gbs / peaks["stream_read_GBs"]
+        if "prefill" in out:
+            peaks["prefill_frac_of_mfma_loop"] = out["prefill"]["value"] / peaks["mfma_i8_loop_TOPS"]
+        out["measured_peaks"] = peaks
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wls, wl, m, args.cpu_seconds)
     print(json.dumps(out), flush=True)

@@ -21,6 +21,9 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libbitlinear.so")
 SOURCES = ["abi.hip", "act_quant.hip", "decode.hip", "prefill.hip", "pack.hip"]
+# measurement kernels (include/bitlinear_probes.h), a library of their own
+PROBE_LIB = os.path.join(PKG, "libbitlinear_probes.so")
+PROBE_SOURCES = ["probes.hip"]
 ARCH = "gfx950"
 
 CFLAGS = [
@@ -47,7 +50,8 @@ def _run(cmd):
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every HIP source and link libbitlinear.so; returns its path."""
+    """Compile every HIP source and link libbitlinear.so and
+    libbitlinear_probes.so; returns the path of libbitlinear.so."""
     os.makedirs(BUILD, exist_ok=True)
     cc = hipcc()
 
@@ -56,13 +60,14 @@ def build(verbose: bool = False) -> str:
         _run([cc, *CFLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
         return obj
 
-    with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(compile_one, SOURCES))
-    tmp = LIB + ".tmp"
-    _run([cc, "-shared", f"--offload-arch={ARCH}", "-o", tmp, *objs])
-    os.replace(tmp, LIB)
-    if verbose:
-        print(f"built {LIB}")
+    with ThreadPoolExecutor(max_workers=min(8, len(SOURCES) + len(PROBE_SOURCES))) as ex:
+        objs = list(ex.map(compile_one, SOURCES + PROBE_SOURCES))
+    for lib, n0, n1 in ((LIB, 0, len(SOURCES)), (PROBE_LIB, len(SOURCES), len(objs))):
+        tmp = lib + ".tmp"
+        _run([cc, "-shared", f"--offload-arch={ARCH}", "-o", tmp, *objs[n0:n1]])
+        os.replace(tmp, lib)
+        if verbose:
+            print(f"built {lib}")
     return LIB
 
 

@@ -55,6 +55,37 @@ def test_exports_every_declared_function(bl):
     assert set(names) <= exported
 
 
+def test_probe_library_exports_and_validation():
+    """libbitlinear_probes.so exports what include/bitlinear_probes.h declares
+    and rejects bad arguments on the host (nothing is launched)."""
+    from bit_gemm_bitlinear_amd import build as b
+
+    if not os.path.exists(b.PROBE_LIB):
+        b.build()
+    from bit_gemm_bitlinear_amd import probes
+
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "bitlinear_probes.h")).read(),
+                  flags=re.S)
+    names = sorted(set(re.findall(r"\b(blprobe_\w+)\s*\(", text)))
+    assert names == ["blprobe_mfma_i8", "blprobe_stream_read"]
+    out = subprocess.run(["nm", "-D", "--defined-only", probes.LIB_PATH], capture_output=True,
+                         text=True).stdout
+    assert set(names) <= set(re.findall(r"\bT (blprobe_\w+)", out))
+    lib = probes.lib()
+    buf, sink = ctypes.c_void_p(0x10000), ctypes.c_void_p(0x20000)  # never dereferenced
+    assert lib.blprobe_stream_read(None, 1024, sink, None) == 1
+    assert lib.blprobe_stream_read(buf, 1024, None, None) == 1
+    assert lib.blprobe_stream_read(buf, 0, sink, None) == 1
+    assert lib.blprobe_stream_read(buf, 1000, sink, None) == 1  # not a multiple of 16
+    assert lib.blprobe_stream_read(ctypes.c_void_p(0x10004), 1024, sink, None) == 1
+    assert lib.blprobe_mfma_i8(0, 1, 0, sink, None) == 1
+    assert lib.blprobe_mfma_i8((1 << 20) + 1, 1, 0, sink, None) == 1
+    assert lib.blprobe_mfma_i8(1, 0, 0, sink, None) == 1
+    assert lib.blprobe_mfma_i8(1, (1 << 16) + 1, 0, sink, None) == 1
+    assert lib.blprobe_mfma_i8(1, 1, 2, sink, None) == 1
+    assert lib.blprobe_mfma_i8(1, 1, 0, None, None) == 1
+
+
 def test_status_strings_and_version(bl):
     lib = bl.lib()
     assert lib.bitlinear_abi_version() == 1
