@@ -149,6 +149,9 @@ ACC_SHAPES = [
     (4, 40, 14336 * 2), (16, 20, 8192 + 16),
     # long rows: a workgroup streams all of K (several ring rounds, codes read from memory)
     (16, 300, 12288), (8, 100, 65536), (2, 48, 49152 + 64),
+    # K split across workgroups with the staged codes close to the LDS code
+    # budget (13 rows x 15 slabs per workgroup, 11 x 17, 5 x 40)
+    (13, 77, 30720), (11, 50, 20480 + 64), (5, 33, 40960),
     # prefill path (M > 16)
     (17, 16, 64), (33, 130, 260), (128, 128, 256), (200, 257, 516), (300, 64, 12), (129, 40, 2048),
     (100, 257, 1088), (260, 520, 2112),  # K % 128 == 64: a last half-deep slab; ragged N and M
@@ -175,7 +178,9 @@ FWD_SHAPES = [(1, 16, 64), (1, 2048, 2048), (3, 50, 36), (8, 2048, 2048), (16, 9
               (72, 250, 1088),
               # activation quantization of the prefill path: a half group (K % 16 == 8),
               # the 16-group-per-lane variant, and rows too long for it
-              (48, 96, 1048), (20, 64, 14336), (18, 32, 16400)]
+              (48, 96, 1048), (20, 64, 14336), (18, 32, 16400),
+              # decode with K split across workgroups near the LDS code budget
+              (13, 64, 30720)]
 
 
 @pytest.mark.parametrize("m,n,k", FWD_SHAPES)
