@@ -86,12 +86,16 @@ inline int plan_narrow_columns(int count, const int64_t* slabs, const int64_t* n
     tiles += cls[i].count;
   }
   if (tiles <= slots) return 0;  // one round: nothing waits for a slot
+  // past 16 rounds the last round's idle slots cost little; skip the plan
+  if (tiles > 16 * slots) return 0;
   const int last = count - 1;
   const int64_t wide_cols = (ncols[last] + kWideBN - 1) / kWideBN;
+  // narrowing more than about one round of tiles cannot even it out further
+  const int64_t max_c = std::min<int64_t>(wide_cols, (slots + tiles_m - 1) / tiles_m + 1);
   const double narrow_us = kNarrowTileFixedUs + kNarrowTileSlabUs * (double)slabs[last];
   double best = list_schedule_end(cls.data(), count, slots);
   int best_c = 0;
-  for (int64_t c = 1; c <= wide_cols; ++c) {
+  for (int64_t c = 1; c <= max_c; ++c) {
     const int64_t keep = wide_cols - c;  // wide tile columns left in front
     const int64_t narrow_n = ncols[last] - keep * kWideBN;
     cls[last] = TileClass{tiles_m * keep, kWideTileFixedUs + kWideTileSlabUs * (double)slabs[last]};

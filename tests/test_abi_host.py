@@ -358,24 +358,51 @@ int main() {
   // four whole rounds of equal tiles: nothing to even out
   const int64_t s1[1] = {20}, c1[1] = {256 * 128};
   int whole = bl::plan_narrow_columns<256, 128>(1, s1, c1, 16, 512);
-  printf("%d %d %d %d\n", mismatches, ffn, small, whole);
+  // the bounded search is as good as trying every column count
+  int worse = 0;
+  for (int trial = 0; trial < 200; ++trial) {
+    const int n = 1 + g() % 4;
+    int64_t sl[4], nc[4];
+    for (int i = 0; i < n; ++i) { sl[i] = 1 + g() % 60; nc[i] = 64 + g() % 30000; }
+    const int64_t tm = 1 + g() % 40, slots = 64 + g() % 600;
+    int64_t tiles = 0;
+    for (int i = 0; i < n; ++i) tiles += tm * ((nc[i] + 255) / 256);
+    if (tiles <= slots || tiles > 16 * slots) continue;
+    auto end_of = [&](int64_t c) {
+      std::vector<bl::TileClass> cl(n + 1);
+      for (int i = 0; i < n; ++i)
+        cl[i] = bl::TileClass{tm * ((nc[i] + 255) / 256), bl::kWideTileFixedUs + bl::kWideTileSlabUs * sl[i]};
+      const int64_t cols = (nc[n - 1] + 255) / 256, keep = cols - c;
+      cl[n - 1].count = tm * keep;
+      cl[n] = bl::TileClass{tm * ((nc[n - 1] - keep * 256 + 127) / 128),
+                            bl::kNarrowTileFixedUs + bl::kNarrowTileSlabUs * sl[n - 1]};
+      return bl::list_schedule_end(cl.data(), n + 1, slots);
+    };
+    double best = end_of(0);
+    for (int64_t c = 1; c <= (nc[n - 1] + 255) / 256; ++c) best = std::min(best, end_of(c));
+    const int c = bl::plan_narrow_columns<256, 128>(n, sl, nc, tm, slots);
+    if (end_of(c) > best * 1.0101) ++worse;
+  }
+  printf("%d %d %d %d %d\n", mismatches, ffn, small, whole, worse);
   return 0;
 }
 '''
 
 
 def test_prefill_plan(tmp_path):
-    """The grouped list-scheduling model equals a per-tile simulation, and
-    the plan narrows the tiles of the FFN's partly filled last round (160
-    tiles = 10 tile columns of the up projection) and nothing in launches
-    that fill whole rounds."""
+    """The grouped list-scheduling model equals a per-tile simulation; the
+    plan narrows the tiles of the FFN's partly filled last round (160 tiles =
+    10 tile columns of the up projection) and nothing in launches that fill
+    whole rounds; its bounded search does as well as trying every column
+    count (within its 1% threshold)."""
     src = tmp_path / "plan_check.cpp"
     exe = tmp_path / "plan_check"
     src.write_text(PLAN_SRC)
     subprocess.run(["g++", "-O2", "-std=c++17", "-I", CSRC, str(src), "-o", str(exe)], check=True)
-    mismatches, ffn, small, whole = map(int, subprocess.run(
+    mismatches, ffn, small, whole, worse = map(int, subprocess.run(
         [str(exe)], capture_output=True, text=True, check=True).stdout.split())
     assert mismatches == 0
+    assert worse == 0
     assert ffn == 10
     assert small == 0
     assert whole == 0
