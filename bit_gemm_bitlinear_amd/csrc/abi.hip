@@ -46,6 +46,9 @@ struct Layout {
   size_t q_off[kMaxProj], xs_off[kMaxProj], qs_off[kMaxProj];
   size_t part_off[kMaxProj], cnt_off[kMaxProj];
   DecodePlan plan[kMaxProj];
+  // prefill (main variant): K parts per projection and their int32 partial sums
+  int32_t pf_ksplit[kMaxProj], pf_kspw[kMaxProj];
+  size_t pf_part_off[kMaxProj];
   size_t zero_off, zero_bytes;
   size_t total;
 };
@@ -96,6 +99,27 @@ void make_layout(int32_t count, const int64_t* ns, const int64_t* ks, int64_t m,
     }
   }
   L.zero_bytes = off - L.zero_off;
+  // prefill: split the K of projections whose tiles would outlast the rest of
+  // the launch (a plan from the shapes alone, so the size queries agree)
+  for (int i = 0; i < count; ++i) {
+    L.pf_ksplit[i] = 1;
+    L.pf_kspw[i] = (int32_t)((ks[i] + kPrefillSlab - 1) / kPrefillSlab);
+    L.pf_part_off[i] = 0;
+  }
+  if (!L.decode && L.load_mode == 0) {
+    int64_t slabs[kMaxProj], tiles[kMaxProj];
+    for (int i = 0; i < count; ++i) {
+      slabs[i] = L.pf_kspw[i];
+      tiles[i] = (int64_t)(L.m_pad / kPrefillBM) * ((ns[i] + kPrefillBN - 1) / kPrefillBN);
+    }
+    plan_ksplit(count, slabs, tiles, kPrefillPlanSlots, kPrefillMinPartSlabs, kPrefillMaxSplit,
+                L.pf_ksplit, L.pf_kspw);
+    for (int i = 0; i < count; ++i) {
+      if (L.pf_ksplit[i] == 1) continue;
+      L.pf_part_off[i] = off;
+      off = align256(off + sizeof(int32_t) * (size_t)L.pf_ksplit[i] * (size_t)m * (size_t)ns[i]);
+    }
+  }
   // the size does not depend on which plan the device's CU count picks:
   // room for the per-projection plans' split-K partials is always counted
   size_t ring = L.zero_off;
@@ -217,7 +241,8 @@ bl_status run_forward(int32_t count, const ProjIO* io, int64_t m, void* workspac
     // so the costliest tiles start first and the short ones fill in.
     int order[kMaxProj];
     for (int i = 0; i < count; ++i) order[i] = i;
-    std::stable_sort(order, order + count, [&](int a, int b) { return ks[a] > ks[b]; });
+    std::stable_sort(order, order + count,
+                     [&](int a, int b) { return L.pf_kspw[a] > L.pf_kspw[b]; });  // slabs per tile
     for (int o = 0; o < count; ++o) {
       const int i = order[o];
       PrefillProj& P = pa.p[o];
@@ -234,18 +259,23 @@ bl_status run_forward(int32_t count, const ProjIO* io, int64_t m, void* workspac
       P.tiles_n = (int32_t)((ns[i] + prefill_bn(load_mode) - 1) / prefill_bn(load_mode));
       P.ldy = (int32_t)ns[i];
       P.narrow = 0;
+      P.ksplit = L.pf_ksplit[i];
+      P.kspw = L.pf_kspw[i];
+      P.part = P.ksplit > 1 ? reinterpret_cast<int32_t*>(ws + L.pf_part_off[i]) : nullptr;
     }
     // The last tile columns of the last projection become narrow tiles when
     // that evens out the launch's last round of workgroups.
     int entries = count;
     if (load_mode == 0 && count < kMaxProj) {
       int64_t slabs[kMaxProj], cols[kMaxProj];
+      int parts[kMaxProj];
       for (int o = 0; o < count; ++o) {
-        slabs[o] = (pa.p[o].k + 127) / 128;
+        slabs[o] = pa.p[o].kspw;
         cols[o] = pa.p[o].n;
+        parts[o] = pa.p[o].ksplit;
       }
       const int c = plan_narrow_columns<kPrefillBN, kPrefillNarrowBN>(
-          count, slabs, cols, pa.tiles_m, (int64_t)kPrefillWgsPerCu * device_cu_count());
+          count, slabs, cols, pa.tiles_m, (int64_t)kPrefillWgsPerCu * device_cu_count(), parts);
       if (c > 0) {
         PrefillProj& W = pa.p[count - 1];
         const int32_t keep = (W.tiles_n - c) * kPrefillBN;  // columns that stay in wide tiles
@@ -267,14 +297,21 @@ bl_status run_forward(int32_t count, const ProjIO* io, int64_t m, void* workspac
       }
     }
     pa.count = entries;
-    int64_t tiles = 0;
+    int64_t tiles = 0, pieces = 0;
     for (int o = 0; o < entries; ++o) {
+      const PrefillProj& P = pa.p[o];
       pa.tile_begin[o] = (int32_t)tiles;
-      tiles += round_up((int64_t)pa.tiles_m * pa.p[o].tiles_n, 8);  // XCD-aligned ranges
+      tiles += round_up((int64_t)pa.tiles_m * P.tiles_n * P.ksplit, 8);  // XCD-aligned ranges
+      pa.fin_begin[o] = (int32_t)pieces;
+      if (P.ksplit > 1) pieces += m * ((P.n + 7) / 8);  // 8 outputs of one row each
     }
-    for (int o = entries; o < kMaxProj; ++o) pa.tile_begin[o] = (int32_t)tiles;
-    if (tiles >= (int64_t(1) << 31)) return BL_ESHAPE;
+    for (int o = entries; o < kMaxProj; ++o) {
+      pa.tile_begin[o] = (int32_t)tiles;
+      pa.fin_begin[o] = (int32_t)pieces;
+    }
+    if (tiles >= (int64_t(1) << 31) || pieces >= (int64_t(1) << 31)) return BL_ESHAPE;
     if (launch_prefill(pa, (int)tiles, stream) != hipSuccess) return BL_EHIP;
+    if (launch_prefill_finish(pa, (int)pieces, stream) != hipSuccess) return BL_EHIP;
   }
   return BL_OK;
 }

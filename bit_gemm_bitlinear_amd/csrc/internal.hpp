@@ -130,10 +130,16 @@ struct PrefillProj {
   int32_t tiles_n;      // ceil(n / tile width)
   int32_t ldy;          // output row stride (elements of y or acc_out)
   int32_t narrow;       // 1: tiles of kPrefillNarrowBN columns (main variant only)
+  // K split across workgroups (main variant only): part kp of a tile covers
+  // slabs [kp * kspw, (kp + 1) * kspw) and writes its int32 sums to
+  // part[kp][m][n] (row stride n); prefill_finish_kernel adds the parts.
+  int32_t ksplit, kspw;
+  int32_t* part;
 };
 
 struct PrefillArgs {
   int32_t tile_begin[kMaxProj];  // first tile of each projection in the launch
+  int32_t fin_begin[kMaxProj];   // first 8-output piece of each projection (finish)
   PrefillProj p[kMaxProj];
   int32_t count;
   int32_t m;
@@ -141,7 +147,18 @@ struct PrefillArgs {
   int32_t load_mode;
 };
 
+// MI355X workgroup slots for the K-split plan of the prefill launch (256 CUs,
+// two workgroups each): fixed, so that workspace sizes depend on shapes only.
+constexpr int kPrefillPlanSlots = 512;
+constexpr int kPrefillSlab = 128;  // codes per K slab of the main variant
+// Slabs (128 codes) per K part: at least this many, and the plan splits a
+// projection only when its K is over twice the launch's average load per slot.
+constexpr int kPrefillMinPartSlabs = 16;
+constexpr int kPrefillMaxSplit = 16;
+
 hipError_t launch_prefill(const PrefillArgs& a, int total_tiles, hipStream_t s);
+// Adds the K parts of the split projections and writes their outputs.
+hipError_t launch_prefill_finish(const PrefillArgs& a, int total_pieces, hipStream_t s);
 
 // ---- weight preparation (pack.hip) ----
 hipError_t launch_pack(const float* w, int64_t n, int64_t k, uint8_t* packed, float* w_scale,

@@ -355,9 +355,8 @@ struct Stager {
 // One output tile (BM rows x BNT columns) of projection P.
 template <int BNT, int NST, int WMI, int NW, int BK>
 __device__ __forceinline__ void prefill_tile(const PrefillArgs& A, const PrefillProj& P, int tm, int tn,
-                                             int8_t* __restrict__ smem) {
+                                             int kp, int8_t* __restrict__ smem) {
   using K = Cfg<BNT, WMI, NW, BK>;
-  constexpr int kNT = K::kNT;
   constexpr int WNF = K::WNF;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -367,6 +366,8 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& A, const Prefill
   const int wm0 = (wave % K::kWavesM) * 32 * WMI;  // wave's rows within the tile
   const int wn0 = (wave / K::kWavesM) * 32 * WNF;  // wave's columns within the tile
   const int S = (P.k + BK - 1) / BK;
+  const int s0 = kp * P.kspw;           // first slab of this K part
+  const int nsl = min(S - s0, P.kspw);  // its slabs (all of K when unsplit)
   const bool bf = P.y != nullptr;
 
   // This lane's token rows, one per 32-row subtile: m0 + wm0 + 32 i + lj.
@@ -378,7 +379,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& A, const Prefill
 #pragma unroll
   for (int i = 0; i < WMI; ++i) {
     const int m = min(m0 + wm0 + 32 * i + lj, A.m - 1);
-    const int32_t q0 = -*G(P.qsum + m);
+    const int32_t q0 = kp == 0 ? -*G(P.qsum + m) : 0;  // once per output
     xs[i] = bf ? *G(P.x_scale + m) : 1.0f;
 #pragma unroll
     for (int f = 0; f < WNF; ++f)
@@ -389,11 +390,11 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& A, const Prefill
   const Stager<BNT, WMI, NW, BK> stager(P, m0, n0);
 #pragma unroll
   for (int p = 0; p < NST - 1; ++p)
-    if (p < S) stager.issue(p, smem + p * K::kStageBytes);
+    if (p < nsl) stager.issue(s0 + p, smem + p * K::kStageBytes);
 
-  for (int s = 0; s < S; ++s) {
+  for (int s = 0; s < nsl; ++s) {
     // wait for slab s: the slabs issued after it (at most NST-2) may still fly
-    const int ahead = min(S - 1 - s, NST - 2);
+    const int ahead = min(nsl - 1 - s, NST - 2);
     if constexpr (NST == 3) {
       if (ahead >= 1)
         wait_vm<K::kDma>();
@@ -404,8 +405,8 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& A, const Prefill
     }
     __builtin_amdgcn_s_barrier();  // every wave's slab-s data is in LDS, and
                                    // every wave is done with slab s-1's buffer
-    if (s + NST - 1 < S)
-      stager.issue(s + NST - 1, smem + ((s + NST - 1) % NST) * K::kStageBytes);
+    if (s + NST - 1 < nsl)
+      stager.issue(s0 + s + NST - 1, smem + ((s + NST - 1) % NST) * K::kStageBytes);
     const int8_t* abuf = smem + (s % NST) * K::kStageBytes;
     const int8_t* bbuf = abuf + K::kAChunks * 16;
     // weight chunks of this lane: column wn0 + 32f + lj, chunks kBL * lg + h
@@ -451,9 +452,10 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& A, const Prefill
   for (int i = 0; i < WMI; ++i) {
     const int m = m0 + wm0 + 32 * i + lj;
     const bool row_ok = m < A.m;
-    if (!bf) {
-      const bool wide = (P.ldy & 3) == 0;  // output rows are 16-byte aligned
-      int32_t* yrow = P.acc_out + (int64_t)m * P.ldy;
+    if (!bf || P.ksplit > 1) {  // int32 sums: the output, or a K part's partial sums
+      const int ld = P.ksplit > 1 ? P.n : P.ldy;
+      const bool wide = (ld & 3) == 0;  // rows are 16-byte aligned
+      int32_t* yrow = (P.ksplit > 1 ? P.part + (int64_t)kp * A.m * P.n : P.acc_out) + (int64_t)m * ld;
 #pragma unroll
       for (int f = 0; f < WNF; ++f)
 #pragma unroll
@@ -527,11 +529,71 @@ __attribute__((amdgpu_waves_per_eu(NW * kPrefillWgsPerCu / 4))) void prefill_ker
   for (int i = 1; i < kMaxProj; ++i) pi += (i < A.count && (int)blockIdx.x >= A.tile_begin[i]);
   const PrefillProj& P = A.p[pi];
   int tm, tn;
-  if (!tile_of((int)blockIdx.x - A.tile_begin[pi], A.tiles_m, P.tiles_n, &tm, &tn)) return;
+  // the K parts of a split projection are further column tiles
+  if (!tile_of((int)blockIdx.x - A.tile_begin[pi], A.tiles_m, P.tiles_n * P.ksplit, &tm, &tn)) return;
+  const int kp = tn / P.tiles_n;
+  tn -= kp * P.tiles_n;
   if (P.narrow)
-    prefill_tile<kPrefillNarrowBN, NST, WMI, NW, BK>(A, P, tm, tn, smem);
+    prefill_tile<kPrefillNarrowBN, NST, WMI, NW, BK>(A, P, tm, tn, kp, smem);
   else
-    prefill_tile<kPrefillBN, NST, WMI, NW, BK>(A, P, tm, tn, smem);
+    prefill_tile<kPrefillBN, NST, WMI, NW, BK>(A, P, tm, tn, kp, smem);
+}
+
+// Adds the K parts of the split projections.  Piece i of a projection is 8
+// consecutive outputs of one token row: the parts' int32 sums (part 0
+// includes minus the row's code sum), then the same division and bf16
+// rounding as the unsplit epilogue, or the int32 sum.
+__global__ __launch_bounds__(kThreads) void prefill_finish_kernel(const PrefillArgs A) {
+  const int idx = (int)blockIdx.x * kThreads + (int)threadIdx.x;
+  int pi = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxProj; ++i) pi += (i < A.count && idx >= A.fin_begin[i]);
+  const PrefillProj& P = A.p[pi];
+  if (P.ksplit <= 1) return;
+  const int cpr = (P.n + 7) >> 3;  // pieces per row
+  const int local = idx - A.fin_begin[pi];
+  if (local < 0 || local >= A.m * cpr) return;
+  const int m = local / cpr, n = 8 * (local - m * cpr);
+  const int64_t slice = (int64_t)A.m * P.n;
+  const int32_t* src = P.part + (int64_t)m * P.n + n;
+  const bool whole = n + 8 <= P.n;
+  int32_t v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  if ((P.n & 3) == 0 && whole) {
+    for (int kp = 0; kp < P.ksplit; ++kp) {
+      const v4i lo = *G(reinterpret_cast<const v4i*>(src + kp * slice));
+      const v4i hi = *G(reinterpret_cast<const v4i*>(src + kp * slice + 4));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[e] += lo[e];
+        v[4 + e] += hi[e];
+      }
+    }
+  } else {
+    for (int kp = 0; kp < P.ksplit; ++kp)
+      for (int e = 0; e < 8 && n + e < P.n; ++e) v[e] += *G(src + kp * slice + e);
+  }
+  if (!P.y) {
+    int32_t* dst = P.acc_out + (int64_t)m * P.ldy + n;
+    if ((P.ldy & 3) == 0 && whole) {
+      *G(reinterpret_cast<v4i*>(dst)) = v4i{v[0], v[1], v[2], v[3]};
+      *G(reinterpret_cast<v4i*>(dst + 4)) = v4i{v[4], v[5], v[6], v[7]};
+    } else {
+      for (int e = 0; e < 8 && n + e < P.n; ++e) *G(dst + e) = v[e];
+    }
+    return;
+  }
+  const RowDiv d = row_div_setup(*G(P.x_scale + m) * *G(P.w_scale));
+  float yf[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) yf[e] = d.fast ? row_div_fast((float)v[e], d.d, d.y) : (float)v[e] / d.d;
+  uint16_t* dst = P.y + (int64_t)m * P.ldy + n;
+  if ((P.ldy & 7) == 0 && whole) {
+    *G(reinterpret_cast<v4i*>(dst)) =
+        v4i{(int32_t)pack_bf16x2(yf[0], yf[1]), (int32_t)pack_bf16x2(yf[2], yf[3]),
+            (int32_t)pack_bf16x2(yf[4], yf[5]), (int32_t)pack_bf16x2(yf[6], yf[7])};
+  } else {
+    for (int e = 0; e < 8 && n + e < P.n; ++e) *G(dst + e) = f32_to_bf16(yf[e]);
+  }
 }
 
 // Slab buffers, wave layout and slab depth of the main variant: 4 waves of
@@ -550,6 +612,7 @@ __attribute__((amdgpu_waves_per_eu(NW * kPrefillWgsPerCu / 4))) void prefill_ker
 #ifndef BL_PREFILL_BK
 #define BL_PREFILL_BK 128
 #endif
+static_assert(BL_PREFILL_BK == kPrefillSlab, "the host plans K parts in slabs of this size");
 
 }  // namespace
 
@@ -569,6 +632,12 @@ hipError_t launch_prefill(const PrefillArgs& a, int total_tiles, hipStream_t s) 
   } else {
     prefill_reg_kernel<2><<<(unsigned)total_tiles, kThreads, 0, s>>>(a);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_finish(const PrefillArgs& a, int total_pieces, hipStream_t s) {
+  if (total_pieces <= 0) return hipSuccess;
+  prefill_finish_kernel<<<(unsigned)((total_pieces + kThreads - 1) / kThreads), kThreads, 0, s>>>(a);
   return hipGetLastError();
 }
 

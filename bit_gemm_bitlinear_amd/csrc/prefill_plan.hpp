@@ -67,22 +67,51 @@ inline double list_schedule_end(const TileClass* cls, int n, int64_t slots) {
   return end;
 }
 
+// K parts of each projection.  A projection whose K (in slabs of 128
+// codes) is more than twice the launch's average load per slot would keep
+// its workgroups busy long after the rest of the launch: it is split into
+// parts of about that average (at least min_part slabs, at most max_split
+// parts), whose int32 sums are added afterwards.
+//   slabs[i]: K slabs of projection i;  tiles[i]: its output tiles
+//   ksplit[i], kspw[i] (out): parts, and slabs per part (the last may be shorter)
+inline void plan_ksplit(int count, const int64_t* slabs, const int64_t* tiles, int64_t slots,
+                        int64_t min_part, int max_split, int* ksplit, int* kspw) {
+  double work = 0.0;
+  for (int i = 0; i < count; ++i) work += (double)tiles[i] * (double)slabs[i];
+  int64_t target = (int64_t)(work / (double)std::max<int64_t>(slots, 1)) + 1;
+  target = std::max<int64_t>(target, min_part);
+  for (int i = 0; i < count; ++i) {
+    ksplit[i] = 1;
+    kspw[i] = (int)slabs[i];
+    if (slabs[i] <= 2 * target) continue;
+    int64_t parts = std::min<int64_t>(max_split, (slabs[i] + target - 1) / target);
+    const int64_t per = (slabs[i] + parts - 1) / parts;
+    parts = (slabs[i] + per - 1) / per;  // no empty part
+    ksplit[i] = (int)parts;
+    kspw[i] = (int)per;
+  }
+}
+
 // Tile columns (of kWideBN outputs) at the end of the last projection to run
 // as narrow tiles (kNarrowBN outputs); 0 keeps every tile wide.
 //   count:     projections in launch order
-//   slabs[i]:  K slabs (of 128 codes) of projection i
+//   slabs[i]:  K slabs (of 128 codes) of one tile of projection i (one K part)
 //   ncols[i]:  output columns of projection i
+//   parts[i]:  K parts of projection i (null: 1 each); the last projection
+//              is narrowed only when it has one
 //   tiles_m:   tiles along the token rows
 //   slots:     workgroups that run at once on the device
 template <int kWideBN, int kNarrowBN>
 inline int plan_narrow_columns(int count, const int64_t* slabs, const int64_t* ncols, int64_t tiles_m,
-                               int64_t slots) {
+                               int64_t slots, const int* parts = nullptr) {
   if (count < 1 || tiles_m < 1 || slots < 1) return 0;
+  if (parts && parts[count - 1] != 1) return 0;
   std::vector<TileClass> cls(count + 1);
   int64_t tiles = 0;
   for (int i = 0; i < count; ++i) {
     const int64_t tn = (ncols[i] + kWideBN - 1) / kWideBN;
-    cls[i] = TileClass{tiles_m * tn, kWideTileFixedUs + kWideTileSlabUs * (double)slabs[i]};
+    cls[i] = TileClass{tiles_m * tn * (parts ? parts[i] : 1),
+                       kWideTileFixedUs + kWideTileSlabUs * (double)slabs[i]};
     tiles += cls[i].count;
   }
   if (tiles <= slots) return 0;  // one round: nothing waits for a slot

@@ -158,6 +158,10 @@ ACC_SHAPES = [
     # more tiles than one round of workgroups on 256 CUs: the last tile column
     # runs as narrow tiles (ragged, and with output rows not 16-byte aligned)
     (2048, 8400, 256), (2048, 8401, 256),
+    # few tiles with long K: K split across workgroups (8 and 5 parts), the
+    # parts added by the finishing pass (rows of partial sums not 16-byte
+    # aligned; a half-deep last slab; ragged M)
+    (256, 301, 16384), (200, 300, 8256),
 ]
 
 
@@ -180,7 +184,9 @@ FWD_SHAPES = [(1, 16, 64), (1, 2048, 2048), (3, 50, 36), (8, 2048, 2048), (16, 9
               # the 16-group-per-lane variant, and rows too long for it
               (48, 96, 1048), (20, 64, 14336), (18, 32, 16400),
               # decode with K split across workgroups near the LDS code budget
-              (13, 64, 30720)]
+              (13, 64, 30720),
+              # prefill with K split across workgroups (ragged output rows)
+              (300, 201, 16448), (130, 256, 12288)]
 
 
 @pytest.mark.parametrize("m,n,k", FWD_SHAPES)
