@@ -389,6 +389,56 @@ int main() {
 '''
 
 
+KSPLIT_SRC = r'''
+#include "prefill_plan.hpp"
+#include <cstdio>
+#include <random>
+
+int main() {
+  int ks[8], kw[8];
+  { const int64_t sl[3] = {54, 20, 20}, t[3] = {160, 432, 432};  // 2B FFN, M = 2048
+    bl::plan_ksplit(3, sl, t, 512, 16, 16, ks, kw);
+    printf("%d %d %d ", ks[0], ks[1], ks[2]); }
+  { const int64_t sl[7] = {32, 32, 32, 32, 32, 32, 112}, t[7] = {64, 16, 16, 64, 224, 224, 64};  // 8B, M = 512
+    bl::plan_ksplit(7, sl, t, 512, 16, 16, ks, kw);
+    printf("%d %d %d ", ks[0], ks[6], kw[6]); }
+  { const int64_t sl[1] = {128}, t[1] = {4};
+    bl::plan_ksplit(1, sl, t, 512, 16, 16, ks, kw);
+    printf("%d %d ", ks[0], kw[0]); }
+  // every split covers K exactly with no empty part, within the bounds
+  std::mt19937 g(3);
+  int bad = 0;
+  for (int trial = 0; trial < 2000; ++trial) {
+    const int n = 1 + g() % 8;
+    int64_t sl[8], t[8];
+    for (int i = 0; i < n; ++i) { sl[i] = 1 + g() % 400; t[i] = 1 + g() % 300; }
+    bl::plan_ksplit(n, sl, t, 512, 16, 16, ks, kw);
+    for (int i = 0; i < n; ++i) {
+      if (ks[i] < 1 || ks[i] > 16 || kw[i] < 1) ++bad;
+      if ((int64_t)ks[i] * kw[i] < sl[i] || (int64_t)(ks[i] - 1) * kw[i] >= sl[i]) ++bad;
+      if (ks[i] == 1 && kw[i] != sl[i]) ++bad;
+    }
+  }
+  printf("%d\n", bad);
+  return 0;
+}
+'''
+
+
+def test_prefill_ksplit_plan(tmp_path):
+    """The K-split plan leaves the 2B FFN whole, splits the 8B-class layer's
+    down projection at M = 512 (112 slabs) into 3 parts of 38 and a lone
+    128-slab projection into 8 of 16, and every split covers K with no empty
+    part and at most 16 parts."""
+    src = tmp_path / "ksplit_check.cpp"
+    exe = tmp_path / "ksplit_check"
+    src.write_text(KSPLIT_SRC)
+    subprocess.run(["g++", "-O2", "-std=c++17", "-I", CSRC, str(src), "-o", str(exe)], check=True)
+    out = list(map(int, subprocess.run([str(exe)], capture_output=True, text=True,
+                                       check=True).stdout.split()))
+    assert out == [1, 1, 1, 1, 3, 38, 8, 16, 0]
+
+
 def test_prefill_plan(tmp_path):
     """The grouped list-scheduling model equals a per-tile simulation; the
     plan narrows the tiles of the FFN's partly filled last round (160 tiles =
