@@ -17,7 +17,9 @@ from .bitlinear_oracle import (  # noqa: F401
     pack,
     pack_weights,
     ternarize,
+    tile,
     unpack,
+    untile,
     weight_quant,
     weight_scale,
 )

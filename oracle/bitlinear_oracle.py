@@ -60,6 +60,10 @@ R6  The contraction is exact integer arithmetic (int32 result), not a
 R7  Dequantization divides fp32(acc) by the fp32 product
     fp32(input_scale * weight_scale) (one correctly rounded division),
     then rounds to bfloat16 with round-to-nearest-even.
+R11 (a storage choice of this project, not a reading of the pages) The
+    optional tiled layout (``tile`` / ``untile``) permutes the R5 bytes
+    inside each block of 16 rows (N % 16 == 0, K % 256 == 0); it changes
+    no result.
 
 Parity status: every function here is pinned by tests that do not call it
 to compute their expectation (hand derivations, exact rational arithmetic,
@@ -223,6 +227,47 @@ def unpack(packed: np.ndarray) -> np.ndarray:
     for j in range(4):
         out[:, :, j] = ((packed >> np.uint8(2 * j)) & np.uint8(3)).astype(np.int8) - 1
     return out.reshape(n, kb * 4)
+
+
+def _tiled_position(row: int, o: int, rowbytes: int) -> int:
+    """R11: where the 16 R5 bytes at byte o (a multiple of 16) of weight row
+    `row` start in the tiled layout.  Rows 16b..16b+15 keep their block of
+    16 * rowbytes bytes; it is cut along K into 1 KB tiles (64 bytes of each of
+    the 16 rows), and inside a tile the 16-byte piece g = (o // 16) % 4 of row
+    r = row % 16 comes at 256 * g + 16 * r."""
+    block, r = divmod(row, 16)
+    tile_no, g = divmod(o // 16, 4)
+    return block * 16 * rowbytes + 1024 * tile_no + 256 * g + 16 * r
+
+
+def tile(packed: np.ndarray) -> np.ndarray:
+    """R5 bytes [N, K/4] -> the tiled layout (R11), as [N/16, 4K] bytes."""
+    packed = np.asarray(packed, dtype=np.uint8)
+    n, rowbytes = packed.shape
+    if n % 16 or rowbytes % 64:
+        raise ValueError("the tiled layout needs N % 16 == 0 and K % 256 == 0")
+    out = np.empty(n * rowbytes, dtype=np.uint8)
+    for row in range(n):
+        for o in range(0, rowbytes, 16):
+            at = _tiled_position(row, o, rowbytes)
+            out[at:at + 16] = packed[row, o:o + 16]
+    return out.reshape(n // 16, 16 * rowbytes)
+
+
+def untile(tiled: np.ndarray) -> np.ndarray:
+    """The inverse of ``tile``: [N/16, 4K] bytes -> R5 bytes [N, K/4]."""
+    tiled = np.asarray(tiled, dtype=np.uint8)
+    nb, width = tiled.shape
+    n, rowbytes = 16 * nb, width // 16
+    if width % 1024:
+        raise ValueError("the tiled layout needs K % 256 == 0")
+    flat = tiled.reshape(-1)
+    out = np.empty((n, rowbytes), dtype=np.uint8)
+    for row in range(n):
+        for o in range(0, rowbytes, 16):
+            at = _tiled_position(row, o, rowbytes)
+            out[row, o:o + 16] = flat[at:at + 16]
+    return out
 
 
 # --------------------------------------------------------------------------

@@ -284,6 +284,61 @@ def test_unpack_roundtrip_and_code3():
     assert np.array_equal(oracle.pack(oracle.unpack(valid.reshape(1, -1))), valid.reshape(1, -1))
 
 
+# ---------------------------------------------------------------- tiled layout
+
+def test_tile_matches_transpose_formulation():
+    """The tiled layout as one numpy reshape/transpose of the row-major bytes:
+    [block, row r, tile t, chunk g, byte j] -> [block, t, g, r, j]."""
+    rng = np.random.default_rng(11)
+    for n, k in [(16, 256), (32, 512), (48, 1024)]:
+        packed = rng.integers(0, 256, size=(n, k // 4), dtype=np.uint8)
+        expect = packed.reshape(n // 16, 16, k // 256, 4, 16).transpose(0, 2, 3, 1, 4)
+        got = oracle.tile(packed)
+        assert got.shape == (n // 16, 4 * k)
+        assert np.array_equal(got.reshape(-1), expect.reshape(-1))
+
+
+def test_tile_hand_positions_and_inverse():
+    """Single marked bytes land where the layout's rule puts them, block by
+    block, and untile restores the rows."""
+    n, k = 32, 512
+    rb = k // 4
+    for row, o in [(0, 0), (0, 16), (1, 0), (15, 63), (5, 64), (16, 0), (31, 127), (17, 80)]:
+        packed = np.zeros((n, rb), np.uint8)
+        packed[row, o] = 0xA5
+        flat = oracle.tile(packed).reshape(-1)
+        assert int(np.count_nonzero(flat)) == 1
+        # worked by hand: block row // 16 starts at (row // 16) * 16 * rb; within
+        # it tile o // 64 starts at 1024 * (o // 64); chunk (o % 64) // 16 of the
+        # tile's 64-byte row piece at 256 * ((o % 64) // 16); row row % 16 at
+        # 16 * (row % 16); byte o % 16 inside the chunk
+        at = (row // 16) * 16 * rb + 1024 * (o // 64) + 256 * ((o % 64) // 16) + 16 * (row % 16) + o % 16
+        assert flat[at] == 0xA5
+    rng = np.random.default_rng(12)
+    packed = rng.integers(0, 256, size=(n, rb), dtype=np.uint8)
+    tiled = oracle.tile(packed)
+    assert np.array_equal(oracle.untile(tiled), packed)
+    # every block of 16 rows keeps its bytes in place (a permutation inside it)
+    flat = tiled.reshape(-1)
+    for b in range(n // 16):
+        blk = slice(b * 16 * rb, (b + 1) * 16 * rb)
+        assert np.array_equal(np.sort(flat[blk]), np.sort(packed[16 * b:16 * b + 16].reshape(-1)))
+    with pytest.raises(ValueError):
+        oracle.tile(np.zeros((8, 64), np.uint8))
+    with pytest.raises(ValueError):
+        oracle.tile(np.zeros((16, 32), np.uint8))
+
+
+def test_tile_first_tile_is_the_16x16x64_operand_order():
+    """Lane 16 g + r of a 64-lane read of the first 1 KB gets row r, bytes
+    16 g .. 16 g + 15: the rows of the matrix-core operand, by brute force."""
+    packed = np.random.default_rng(13).integers(0, 256, size=(16, 64), dtype=np.uint8)
+    flat = oracle.tile(packed).reshape(-1)
+    for lane in range(64):
+        g, r = divmod(lane, 16)
+        assert flat[16 * lane:16 * lane + 16].tolist() == packed[r, 16 * g:16 * g + 16].tolist()
+
+
 # ---------------------------------------------------------------- contraction
 
 @pytest.mark.parametrize("shape", [(1, 1, 4), (3, 5, 8), (4, 7, 33), (2, 9, 64)])
