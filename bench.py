@@ -86,6 +86,8 @@ def parse():
     ap.add_argument("--pmc-kernel", choices=sorted(PMC_KERNELS), default="decode",
                     help="kernel whose traffic --summarize-pmc reports")
     ap.add_argument("--command", default="", help="command line recorded in a summary")
+    ap.add_argument("--layout", choices=["tiled", "rows"], default="tiled",
+                    help="weight layout: the 16-row tiled layout, or row-major [N][K/4]")
     ap.add_argument("--curve", action="store_true",
                     help="decode GB/s against weight bytes for one projection (1 MiB .. 1 GiB)")
     return ap.parse_args()
@@ -103,14 +105,17 @@ def dev_bf16(torch, bits, dev):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
 
 
-def prepare(torch, bl, wls, wl, m, copies, dev):
-    """Packed weights (packed on the GPU by the library), R rotated copies,
-    activations, and one prepared grouped call per copy."""
+def prepare(torch, bl, wls, wl, m, copies, dev, tiled=True):
+    """Packed weights (packed on the GPU by the library, then put in the
+    16-row tiled layout), R rotated copies, activations, and one prepared
+    grouped call per copy."""
     xs, packed, scales = [], [], []
     for pi in range(len(wl.projections)):
         w = torch.from_numpy(wls.weights(wl, pi)).to(dev)
         p, s = bl.pack_weights(w)
         del w
+        if tiled:
+            p = bl.tile_weights(p)
         packed.append(p)
         scales.append(s)
         xs.append(dev_bf16(torch, wls.activations(wl, pi, m), dev))
@@ -264,18 +269,19 @@ def cpu_baseline(wls, wl, m, budget_s):
     }
 
 
-def prefill_measure(torch, bl, wls, dev, steps):
+def prefill_measure(torch, bl, wls, dev, steps, tiled=True):
     wl = wls.WORKLOADS["prefill_2b_m2048"]
     m = wl.ms[0]
     # one weight copy (6.5 MB of packed weights stay cached, as in a model
     # whose prefill is compute bound); 8 steps per captured graph so the
     # replay launches do not show between steps
-    calls = prepare(torch, bl, wls, wl, m, 1, dev) * 8
+    calls = prepare(torch, bl, wls, wl, m, 1, dev, tiled) * 8
     host_s, ev_s, n = time_steps(torch, calls, max(64, steps // 8), 16, eager=False)
     tops = wl.ops(m) * n / ev_s / 1e12
     return {
         "workload": wl.name, "m": m, "value": tops, "unit": "TOPS",
         "note": "end to end: activation quantization pass + MFMA GEMM, 3 projections",
+        "weight_layout": "tiled" if tiled else "rows",
         "library_int8_gemm_TOPS": library_int8_gemm(torch, wl, m, dev),
         "library_int8_gemm_note": "context: torch._int_mm (dense int8 x int8 -> int32, "
                                   "vendor GEMM library) on the same three shapes",
@@ -405,12 +411,13 @@ def pmc_probe(torch, bl, wls, args):
     wl = wls.WORKLOADS[args.workload]
     m = args.m if args.m is not None else wl.ms[0]
     copies = max(1, int(np.ceil(args.rotate_bytes / wl.packed_bytes)))
-    calls = prepare(torch, bl, wls, wl, m, copies, dev)
+    tiled = args.layout == "tiled"
+    calls = prepare(torch, bl, wls, wl, m, copies, dev, tiled)
     time_steps(torch, calls, args.steps, 0, eager=True)
     del calls
     # the prefill workload, a few eager steps (one weight copy, as timed)
     pwl = wls.WORKLOADS["prefill_2b_m2048"]
-    pcalls = prepare(torch, bl, wls, pwl, pwl.ms[0], 1, dev)
+    pcalls = prepare(torch, bl, wls, pwl, pwl.ms[0], 1, dev, tiled)
     time_steps(torch, pcalls, 8, 0, eager=True)
     del pcalls
     n = COPY_PROBE_MIB * (1 << 20) // 4
@@ -423,7 +430,7 @@ def pmc_probe(torch, bl, wls, args):
           f"3 copies of {COPY_PROBE_MIB} MiB", flush=True)
 
 
-def bandwidth_curve(torch, bl, dev, k=4096, sizes_mib=(1, 4, 16, 64, 256, 1024)):
+def bandwidth_curve(torch, bl, dev, layout, k=4096, sizes_mib=(1, 4, 16, 64, 256, 1024)):
     """Decode (M=1) on a single N x K projection of random packed bytes (code 3
     included: timing only), cold: rotated over copies spanning >= 1 GiB."""
     rows = []
@@ -434,11 +441,14 @@ def bandwidth_curve(torch, bl, dev, k=4096, sizes_mib=(1, 4, 16, 64, 256, 1024))
         n = mib * (1 << 20) * 4 // k
         copies = max(1, (1 << 30) // (mib << 20)) if mib < 1024 else 2
         base = torch.randint(0, 256, (n, k // 4), dtype=torch.uint8, device=dev)
+        if layout == "tiled":
+            base = bl.tile_weights(base)
         calls = [bl.GroupedCall([x], [base if c == 0 else base.clone()], [ws]) for c in range(copies)]
         steps = max(64, min(4096, 256 * copies // max(1, mib // 16)))
         _, ev_s, nrun = time_steps(torch, calls, steps, min(64, steps), False)
         us = ev_s / nrun * 1e6
-        rows.append({"MiB": mib, "n": n, "k": k, "us": us, "GBs": (mib << 20) / (us * 1e-6) / 1e9})
+        rows.append({"MiB": mib, "n": n, "k": k, "layout": layout, "us": us,
+                     "GBs": (mib << 20) / (us * 1e-6) / 1e9})
         del calls, base
         torch.cuda.empty_cache()
     return rows
@@ -451,8 +461,8 @@ def main():
     if args.summarize_pmc:
         return summarize_pmc(*args.summarize_pmc, args.command, args.pmc_kernel)
     if args.gpus != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
-              "(see the sharding notes in DESIGN.md); run with --gpus 1", file=sys.stderr)
+        print("bench.py runs on one GPU only: the library has no multi-GPU path; "
+              "run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     import torch
 
@@ -462,7 +472,7 @@ def main():
     if args.pmc_probe:
         return pmc_probe(torch, bl, wls, args)
     if args.curve:
-        for r in bandwidth_curve(torch, bl, torch.device("cuda:0")):
+        for r in bandwidth_curve(torch, bl, torch.device("cuda:0"), args.layout):
             print(json.dumps(r), flush=True)
         return
 
@@ -470,11 +480,13 @@ def main():
     wl = wls.WORKLOADS[args.workload]
     m = args.m if args.m is not None else wl.ms[0]
     copies = max(1, int(np.ceil(args.rotate_bytes / wl.packed_bytes)))
-    calls = prepare(torch, bl, wls, wl, m, copies, dev)
+    tiled = args.layout == "tiled"
+    calls = prepare(torch, bl, wls, wl, m, copies, dev, tiled)
     host_s, ev_s, n = time_steps(torch, calls, args.steps, args.warmup, args.eager)
     per_step = ev_s / n
     gbs = wl.packed_bytes / per_step / 1e9
-    traffic = read_traffic("decode") if (args.workload == "decode_1b_m1" and m == 1) else None
+    traffic = (read_traffic("decode") if (args.workload == "decode_1b_m1" and m == 1 and tiled)
+               else None)
 
     out = {
         "metric": METRIC,
@@ -493,6 +505,7 @@ def main():
             "workload": wl.name, "m": m,
             "projections": [[p.name, p.n, p.k] for p in wl.projections],
             "packed_bytes_per_step": wl.packed_bytes,
+            "weight_layout": args.layout,
             "kernel_launches_per_step": 1,
             "rotated_weight_copies": copies,
             "launch": "eager" if args.eager else "hip-graph",
@@ -512,10 +525,16 @@ def main():
             "copy_GBs": copy_bandwidth(torch, dev),
             "copy_note": "plain device copy of 1 GiB (read + write bytes / time), torch elementwise kernel",
         }
+        # the same step on the other weight layout
+        o_calls = prepare(torch, bl, wls, wl, m, copies, dev, not tiled)
+        _, o_s, o_n = time_steps(torch, o_calls, args.steps, args.warmup, args.eager)
+        del o_calls
+        out["context"]["other_layout"] = "rows" if tiled else "tiled"
+        out["context"]["other_layout_GBs"] = wl.packed_bytes / (o_s / o_n) / 1e9
     else:
         del calls
     if not args.no_prefill:
-        out["prefill"] = prefill_measure(torch, bl, wls, dev, args.steps)
+        out["prefill"] = prefill_measure(torch, bl, wls, dev, args.steps, tiled)
     if not args.no_context:
         peaks = measured_ceilings(torch, dev)
         peaks["decode_frac_of_stream_read"] = gbs / peaks["stream_read_GBs"]

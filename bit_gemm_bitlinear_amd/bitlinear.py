@@ -30,7 +30,11 @@ _i64, _i32, _sz, _vp = ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t, ctypes.c
 class Projection(ctypes.Structure):
     """bl_projection: one projection of a grouped forward call."""
     _fields_ = [("x", _vp), ("packed", _vp), ("w_scale", _vp), ("y", _vp),
-                ("n", _i64), ("k", _i64)]
+                ("n", _i64), ("k", _i64), ("layout", _i32), ("reserved", _i32)]
+
+
+LAYOUT_ROWS = 0   # BL_LAYOUT_ROWS: packed uint8 [N, K/4]
+LAYOUT_TILED = 1  # BL_LAYOUT_TILED: uint8 [N/16, 4*K], one row per block of 16 weight rows
 
 
 _SIGS = {
@@ -39,13 +43,19 @@ _SIGS = {
     "bitlinear_pack_workspace_bytes": (_sz, [_i64, _i64]),
     "bitlinear_pack_weights": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp, _vp, _sz, _vp]),
     "bitlinear_unpack_weights": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp]),
+    "bitlinear_tile_weights": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp]),
+    "bitlinear_untile_weights": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp]),
     "bitlinear_act_quant": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp, _vp]),
     "bitlinear_forward_workspace_bytes": (_sz, [_i64, _i64, _i64]),
     "bitlinear_forward": (ctypes.c_int, [_i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "bitlinear_forward_tiled": (ctypes.c_int, [_i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _sz,
+                                               _vp]),
     "bitlinear_forward_grouped_workspace_bytes": (_sz, [_i32, ctypes.POINTER(Projection), _i64]),
     "bitlinear_forward_grouped": (ctypes.c_int, [_i32, ctypes.POINTER(Projection), _i64, _vp,
                                                  _sz, _vp]),
     "bitlinear_forward_acc": (ctypes.c_int, [_i64, _i64, _i64, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "bitlinear_forward_acc_tiled": (ctypes.c_int, [_i64, _i64, _i64, _vp, _vp, _vp, _vp, _sz,
+                                                   _vp]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -122,6 +132,39 @@ def unpack_weights(packed: torch.Tensor) -> torch.Tensor:
     return u
 
 
+def tile_weights(packed: torch.Tensor) -> torch.Tensor:
+    """Row-major packed [N, K/4] -> the 16-row tiled layout, as uint8
+    [N/16, 4*K] (one row per block of 16 weight rows).  N % 16 == 0 and
+    K % 256 == 0."""
+    _require(packed, torch.uint8, 2, "packed")
+    n, kb = packed.shape
+    if n % 16:
+        raise ValueError("the tiled layout needs N % 16 == 0")
+    tiled = torch.empty((n // 16, 16 * kb), dtype=torch.uint8, device=packed.device)
+    _check(_lib.bitlinear_tile_weights(_ptr(packed), n, 4 * kb, _ptr(tiled), _stream(packed)))
+    return tiled
+
+
+def untile_weights(tiled: torch.Tensor) -> torch.Tensor:
+    """The inverse of tile_weights: [N/16, 4*K] -> row-major [N, K/4]."""
+    _require(tiled, torch.uint8, 2, "tiled")
+    nb, kb16 = tiled.shape
+    n, k = 16 * nb, kb16 // 4
+    packed = torch.empty((n, k // 4), dtype=torch.uint8, device=tiled.device)
+    _check(_lib.bitlinear_untile_weights(_ptr(tiled), n, k, _ptr(packed), _stream(tiled)))
+    return packed
+
+
+def weight_layout(w: torch.Tensor, k: int):
+    """(N, layout) of a weight tensor used against K input features: [N, K/4]
+    is row-major, [N/16, 4*K] the tiled layout."""
+    if w.shape[1] * 4 == k:
+        return w.shape[0], LAYOUT_ROWS
+    if w.shape[1] == 4 * k:
+        return 16 * w.shape[0], LAYOUT_TILED
+    raise ValueError("packed weights do not match K")
+
+
 def act_quant(x: torch.Tensor):
     """bf16 activations [M, K] -> (int8 codes [M, K], fp32 scales [M])."""
     _require(x, torch.bfloat16, 2, "x")
@@ -138,26 +181,26 @@ def forward_workspace_bytes(m: int, n: int, k: int) -> int:
 
 def forward(x: torch.Tensor, packed: torch.Tensor, w_scale: torch.Tensor,
             out: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
-    """y = BitLinear(x) as bf16 [M, N]."""
+    """y = BitLinear(x) as bf16 [M, N]; `packed` in either layout."""
     _require(x, torch.bfloat16, 2, "x")
     _require(packed, torch.uint8, 2, "packed")
     m, k = x.shape
-    n = packed.shape[0]
-    if packed.shape[1] * 4 != k:
-        raise ValueError("packed weights do not match K")
+    n, layout = weight_layout(packed, k)
     if out is None:
         out = torch.empty((m, n), dtype=torch.bfloat16, device=x.device)
     ws = _workspace(forward_workspace_bytes(m, n, k), x.device, workspace)
-    _check(_lib.bitlinear_forward(m, n, k, _ptr(x), _ptr(packed), _ptr(w_scale), _ptr(out),
-                                  _ptr(ws), ws.numel() * ws.element_size(), _stream(x)))
+    fn = _lib.bitlinear_forward_tiled if layout == LAYOUT_TILED else _lib.bitlinear_forward
+    _check(fn(m, n, k, _ptr(x), _ptr(packed), _ptr(w_scale), _ptr(out),
+              _ptr(ws), ws.numel() * ws.element_size(), _stream(x)))
     return out
 
 
 def _projections(xs, packeds, w_scales, outs):
     arr = (Projection * len(xs))()
     for i, (x, p, s, y) in enumerate(zip(xs, packeds, w_scales, outs)):
+        n, layout = weight_layout(p, x.shape[1])
         arr[i] = Projection(x.data_ptr(), p.data_ptr(), s.data_ptr(), y.data_ptr(),
-                            p.shape[0], x.shape[1])
+                            n, x.shape[1], layout, 0)
     return arr
 
 
@@ -177,11 +220,12 @@ class GroupedCall:
         for x, p in zip(xs, packeds):
             _require(x, torch.bfloat16, 2, "x")
             _require(p, torch.uint8, 2, "packed")
-            if x.shape[0] != m or p.shape[1] * 4 != x.shape[1]:
-                raise ValueError("inconsistent shapes in grouped call")
+            if x.shape[0] != m:
+                raise ValueError("inconsistent token counts in grouped call")
+            weight_layout(p, x.shape[1])
         if outs is None:
-            outs = [torch.empty((m, p.shape[0]), dtype=torch.bfloat16, device=x.device)
-                    for x, p in zip(xs, packeds)]
+            outs = [torch.empty((m, weight_layout(p, x.shape[1])[0]), dtype=torch.bfloat16,
+                                device=x.device) for x, p in zip(xs, packeds)]
         self.m = m
         self.outs = outs
         self._keep = (list(xs), list(packeds), list(w_scales), outs)
@@ -205,28 +249,32 @@ def forward_grouped(xs, packeds, w_scales, outs=None, workspace=None):
 
 def forward_acc(q: torch.Tensor, packed: torch.Tensor, out: torch.Tensor | None = None,
                 workspace: torch.Tensor | None = None):
-    """Exact int32 accumulators q . u^T for caller-supplied int8 codes."""
+    """Exact int32 accumulators q . u^T for caller-supplied int8 codes;
+    `packed` in either layout."""
     _require(q, torch.int8, 2, "q")
     _require(packed, torch.uint8, 2, "packed")
     m, k = q.shape
-    n = packed.shape[0]
-    if packed.shape[1] * 4 != k:
-        raise ValueError("packed weights do not match K")
+    n, layout = weight_layout(packed, k)
     if out is None:
         out = torch.empty((m, n), dtype=torch.int32, device=q.device)
     ws = _workspace(forward_workspace_bytes(m, n, k), q.device, workspace)
-    _check(_lib.bitlinear_forward_acc(m, n, k, _ptr(q), _ptr(packed), _ptr(out), _ptr(ws),
-                                      ws.numel() * ws.element_size(), _stream(q)))
+    fn = _lib.bitlinear_forward_acc_tiled if layout == LAYOUT_TILED else _lib.bitlinear_forward_acc
+    _check(fn(m, n, k, _ptr(q), _ptr(packed), _ptr(out), _ptr(ws),
+              ws.numel() * ws.element_size(), _stream(q)))
     return out
 
 
 class BitLinear:
     """Inference-time BitLinear layer (no bias): packs fp32 latent weights
-    once, then runs the forward pass on bf16 activations."""
+    once, then runs the forward pass on bf16 activations.  The weights are
+    kept in the tiled layout when the shape allows it (N % 16 == 0,
+    K % 256 == 0) unless tiled=False; `packed` holds them in that layout."""
 
-    def __init__(self, weight: torch.Tensor):
-        self.packed, self.w_scale = pack_weights(weight.contiguous())
+    def __init__(self, weight: torch.Tensor, tiled: bool = True):
         self.out_features, self.in_features = weight.shape
+        self.packed, self.w_scale = pack_weights(weight.contiguous())
+        if tiled and self.out_features % 16 == 0 and self.in_features % 256 == 0:
+            self.packed = tile_weights(self.packed)
 
     def __call__(self, x: torch.Tensor) -> torch.Tensor:
         lead = x.shape[:-1]

@@ -38,6 +38,12 @@ bl_status check_shape(int64_t m, int64_t n, int64_t k) {
 
 int load_mode_for(int64_t k) { return (k % 64 == 0) ? 0 : (k % 16 == 0) ? 1 : 2; }
 
+// The 16-row tiled weight layout needs whole 16-row blocks and whole 1 KB
+// tiles (256 weights of each of 16 rows).
+bl_status check_tiled_shape(int64_t n, int64_t k) {
+  return (n % 16 == 0 && k % 256 == 0) ? BL_OK : BL_ESHAPE;
+}
+
 // Workspace layout of a forward call (shared by the size query and the call).
 struct Layout {
   bool decode;
@@ -141,6 +147,7 @@ struct ProjIO {
   uint16_t* y;
   int32_t* acc;
   int64_t n, k;
+  int32_t tiled;  // 1: packed is in the 16-row tiled layout
 };
 
 bl_status run_forward(int32_t count, const ProjIO* io, int64_t m, void* workspace,
@@ -222,7 +229,7 @@ bl_status run_forward(int32_t count, const ProjIO* io, int64_t m, void* workspac
       P.tww = pl.tww;
       P.kspw = pl.kspw;
       P.ksplit = pl.ksplit;
-      P.ngroups = pl.ngroups;
+      P.tiled = io[i].tiled;
       da.wg_begin[i] = wgs;
       wgs += pl.ngroups * pl.ksplit;
       lds_row = std::max(lds_row, pl.kspw * 256 + 16);
@@ -262,6 +269,7 @@ bl_status run_forward(int32_t count, const ProjIO* io, int64_t m, void* workspac
       P.ksplit = L.pf_ksplit[i];
       P.kspw = L.pf_kspw[i];
       P.part = P.ksplit > 1 ? reinterpret_cast<int32_t*>(ws + L.pf_part_off[i]) : nullptr;
+      P.tiled = io[i].tiled;
     }
     // The last tile columns of the last projection become narrow tiles when
     // that evens out the launch's last round of workgroups.
@@ -324,7 +332,9 @@ const char* bitlinear_status_string(bl_status s) {
   switch (s) {
     case BL_OK: return "ok";
     case BL_EINVAL: return "invalid argument (null pointer or count out of range)";
-    case BL_ESHAPE: return "unsupported shape (M, N, K >= 1, K % 4 == 0, K <= 2^22)";
+    case BL_ESHAPE:
+      return "unsupported shape (M, N, K >= 1, K % 4 == 0, K <= 2^22; tiled weights: "
+             "N % 16 == 0, K % 256 == 0)";
     case BL_EALIGN: return "pointer not 16-byte aligned";
     case BL_EWORKSPACE: return "workspace missing or too small";
     case BL_EHIP: return "HIP kernel launch failed";
@@ -332,7 +342,7 @@ const char* bitlinear_status_string(bl_status s) {
   return "unknown status";
 }
 
-int bitlinear_abi_version(void) { return 1; }
+int bitlinear_abi_version(void) { return 2; }
 
 size_t bitlinear_pack_workspace_bytes(int64_t n, int64_t k) {
   (void)n;
@@ -366,6 +376,29 @@ bl_status bitlinear_unpack_weights(const uint8_t* packed, int64_t n, int64_t k, 
   return BL_OK;
 }
 
+static bl_status retile(const uint8_t* src, int64_t n, int64_t k, uint8_t* dst, bool untile,
+                        void* stream) {
+  bl_status st;
+  if ((st = check_shape(1, n, k)) != BL_OK || (st = check_tiled_shape(n, k)) != BL_OK) return st;
+  if ((st = check_ptr(src)) != BL_OK || (st = check_ptr(dst)) != BL_OK) return st;
+  const uintptr_t a = reinterpret_cast<uintptr_t>(src), b = reinterpret_cast<uintptr_t>(dst);
+  const uintptr_t bytes = (uintptr_t)(n * (k / 4));
+  if (a < b + bytes && b < a + bytes) return BL_EINVAL;  // overlapping arrays
+  if (launch_tile(src, n, k, dst, untile, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return BL_EHIP;
+  return BL_OK;
+}
+
+bl_status bitlinear_tile_weights(const uint8_t* packed, int64_t n, int64_t k, uint8_t* tiled,
+                                 void* stream) {
+  return retile(packed, n, k, tiled, false, stream);
+}
+
+bl_status bitlinear_untile_weights(const uint8_t* tiled, int64_t n, int64_t k, uint8_t* packed,
+                                   void* stream) {
+  return retile(tiled, n, k, packed, true, stream);
+}
+
 bl_status bitlinear_act_quant(const uint16_t* x, int64_t m, int64_t k, int8_t* q,
                               float* x_scale, void* stream) {
   bl_status st;
@@ -386,16 +419,29 @@ size_t bitlinear_forward_workspace_bytes(int64_t m, int64_t n, int64_t k) {
   return L.total;
 }
 
-bl_status bitlinear_forward(int64_t m, int64_t n, int64_t k, const uint16_t* x,
-                            const uint8_t* packed, const float* w_scale, uint16_t* y,
-                            void* workspace, size_t workspace_bytes, void* stream) {
+static bl_status forward_one(int64_t m, int64_t n, int64_t k, const uint16_t* x,
+                             const uint8_t* packed, const float* w_scale, uint16_t* y,
+                             void* workspace, size_t workspace_bytes, void* stream, int tiled) {
   bl_status st;
   if ((st = check_shape(m, n, k)) != BL_OK) return st;
+  if (tiled && (st = check_tiled_shape(n, k)) != BL_OK) return st;
   if ((st = check_ptr(x)) != BL_OK || (st = check_ptr(packed)) != BL_OK ||
       (st = check_ptr(w_scale)) != BL_OK || (st = check_ptr(y)) != BL_OK)
     return st;
-  ProjIO io = {x, nullptr, packed, w_scale, y, nullptr, n, k};
+  ProjIO io = {x, nullptr, packed, w_scale, y, nullptr, n, k, tiled};
   return run_forward(1, &io, m, workspace, workspace_bytes, static_cast<hipStream_t>(stream));
+}
+
+bl_status bitlinear_forward(int64_t m, int64_t n, int64_t k, const uint16_t* x,
+                            const uint8_t* packed, const float* w_scale, uint16_t* y,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  return forward_one(m, n, k, x, packed, w_scale, y, workspace, workspace_bytes, stream, 0);
+}
+
+bl_status bitlinear_forward_tiled(int64_t m, int64_t n, int64_t k, const uint16_t* x,
+                                  const uint8_t* tiled, const float* w_scale, uint16_t* y,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  return forward_one(m, n, k, x, tiled, w_scale, y, workspace, workspace_bytes, stream, 1);
 }
 
 size_t bitlinear_forward_grouped_workspace_bytes(int32_t count, const bl_projection* projs,
@@ -420,24 +466,41 @@ bl_status bitlinear_forward_grouped(int32_t count, const bl_projection* projs, i
     const bl_projection& p = projs[i];
     bl_status st;
     if ((st = check_shape(m, p.n, p.k)) != BL_OK) return st;
+    if ((p.layout != BL_LAYOUT_ROWS && p.layout != BL_LAYOUT_TILED) || p.reserved != 0)
+      return BL_EINVAL;
+    if (p.layout == BL_LAYOUT_TILED && (st = check_tiled_shape(p.n, p.k)) != BL_OK) return st;
     if ((st = check_ptr(p.x)) != BL_OK || (st = check_ptr(p.packed)) != BL_OK ||
         (st = check_ptr(p.w_scale)) != BL_OK || (st = check_ptr(p.y)) != BL_OK)
       return st;
-    io[i] = ProjIO{p.x, nullptr, p.packed, p.w_scale, p.y, nullptr, p.n, p.k};
+    io[i] = ProjIO{p.x,      nullptr, p.packed, p.w_scale, p.y,
+                   nullptr, p.n,     p.k,      p.layout == BL_LAYOUT_TILED ? 1 : 0};
   }
   return run_forward(count, io, m, workspace, workspace_bytes, static_cast<hipStream_t>(stream));
+}
+
+static bl_status forward_acc_one(int64_t m, int64_t n, int64_t k, const int8_t* q,
+                                 const uint8_t* packed, int32_t* acc, void* workspace,
+                                 size_t workspace_bytes, void* stream, int tiled) {
+  bl_status st;
+  if ((st = check_shape(m, n, k)) != BL_OK) return st;
+  if (tiled && (st = check_tiled_shape(n, k)) != BL_OK) return st;
+  if ((st = check_ptr(q)) != BL_OK || (st = check_ptr(packed)) != BL_OK ||
+      (st = check_ptr(acc)) != BL_OK)
+    return st;
+  ProjIO io = {nullptr, q, packed, nullptr, nullptr, acc, n, k, tiled};
+  return run_forward(1, &io, m, workspace, workspace_bytes, static_cast<hipStream_t>(stream));
 }
 
 bl_status bitlinear_forward_acc(int64_t m, int64_t n, int64_t k, const int8_t* q,
                                 const uint8_t* packed, int32_t* acc, void* workspace,
                                 size_t workspace_bytes, void* stream) {
-  bl_status st;
-  if ((st = check_shape(m, n, k)) != BL_OK) return st;
-  if ((st = check_ptr(q)) != BL_OK || (st = check_ptr(packed)) != BL_OK ||
-      (st = check_ptr(acc)) != BL_OK)
-    return st;
-  ProjIO io = {nullptr, q, packed, nullptr, nullptr, acc, n, k};
-  return run_forward(1, &io, m, workspace, workspace_bytes, static_cast<hipStream_t>(stream));
+  return forward_acc_one(m, n, k, q, packed, acc, workspace, workspace_bytes, stream, 0);
+}
+
+bl_status bitlinear_forward_acc_tiled(int64_t m, int64_t n, int64_t k, const int8_t* q,
+                                      const uint8_t* tiled, int32_t* acc, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+  return forward_acc_one(m, n, k, q, tiled, acc, workspace, workspace_bytes, stream, 1);
 }
 
 }  // extern "C"

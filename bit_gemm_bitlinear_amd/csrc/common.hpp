@@ -49,6 +49,20 @@ __device__ __forceinline__ float load_f32_vmem(const float* p) {
 // fp32(1e-5): the lower clamp of the absmax / absmean denominators.
 constexpr float kEps = 1e-5f;
 
+// The 16-row tiled weight layout (N % 16 == 0, K % 256 == 0).  The same
+// bytes as the row-major [N][K/4] packing, permuted inside each block of 16
+// rows: the block keeps its 16 * K/4 bytes in place, as 1 KB tiles of 16 rows
+// x 64 packed bytes (256 weights) taken along K, and inside a tile the
+// 16-byte chunk g (0..3) of row r (0..15) sits at 256 g + 16 r.  One tile is
+// then exactly what 64 lanes read for one 16-row operand of the 16x16x64
+// matrix-core op (lane 16 g + r: row r, chunk g), as one contiguous 1 KB.
+// Byte offset of the 16-byte chunk at row byte `o` (a multiple of 16) of
+// weight row `row`:
+__host__ __device__ __forceinline__ int64_t tiled_chunk_offset(int64_t row, int64_t o,
+                                                               int64_t rowbytes) {
+  return (row >> 4) * 16 * rowbytes + 1024 * (o >> 6) + 256 * ((o >> 4) & 3) + 16 * (row & 15);
+}
+
 // 2-bit codes of 16 packed weights -> 4 dwords of int8 codes (0..3).
 // Byte b of the packed dword holds weights 4b..4b+3 (2 bits each, least
 // significant first).  Output dword a, byte b, holds the code of weight

@@ -445,15 +445,25 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& A, const DecodePro
   // weights: this wave streams its TWW row tiles over its K slabs, slab-major
   // so each A fragment feeds TWW tiles.  Every load is unconditional (past
   // the end it repeats the last chunk, a cache hit that is never used), so
-  // the memory-counter waits are exact.
+  // the memory-counter waits are exact.  Lane (ln, lg) takes row ln of the
+  // row tile, bytes 16 lg.. of the slab's 64: in the row-major layout 16 rows
+  // x 64 bytes, in the tiled layout (common.hpp) one contiguous 1 KB at
+  // 16 * lane of the tile.  Both are one address formula with per-lane
+  // constants, so the layout costs no branch.
   const int NI = TWW * nw;
   const int last = max(NI - 1, 0);
+  const bool tl = P.tiled != 0;
+  const int row_add = tl ? 0 : ln;
+  const int row_max = tl ? P.n - 16 : P.n - 1;  // tiled: n % 16 == 0
+  const int slab_bytes = tl ? 1024 : 64;
+  const int lane_off = tl ? 16 * lane : 16 * lg;
+  const int lim = tl ? 16 * rowbytes : rowbytes;  // bytes the clamp keeps the load in
   auto wload = [&](int it) {
     const int c = min(it, last);
     const int ls = c / TWW, t = c - ls * TWW;
-    const int row = min(row0 + 16 * t + ln, P.n - 1);
-    return load_w16<MODE>(P.packed + (int64_t)row * rowbytes, (sb + ws0 + ls) * 64 + 16 * lg,
-                          rowbytes);
+    const int row = min(row0 + 16 * t + row_add, row_max);
+    return load_w16<MODE>(P.packed + (int64_t)row * rowbytes, (sb + ws0 + ls) * slab_bytes + lane_off,
+                          lim);
   };
   // token rows m >= M of the A operand repeat row 0: output rows m >= M
   // are never stored, and rows do not mix in the product

@@ -80,7 +80,7 @@ struct DecodeProj {
   int32_t tww;         // 16-row tiles per wave
   int32_t kspw;        // K slabs (256 codes) per WG
   int32_t ksplit;      // WGs sharing one row group along K
-  int32_t ngroups;     // row groups of (4 / wk) * tww * 16 rows
+  int32_t tiled;       // 1: weights in the 16-row tiled layout (common.hpp)
 };
 
 struct DecodeArgs {
@@ -135,6 +135,7 @@ struct PrefillProj {
   // part[kp][m][n] (row stride n); prefill_finish_kernel adds the parts.
   int32_t ksplit, kspw;
   int32_t* part;
+  int32_t tiled;        // 1: weights in the 16-row tiled layout (common.hpp)
 };
 
 struct PrefillArgs {
@@ -164,5 +165,9 @@ hipError_t launch_prefill_finish(const PrefillArgs& a, int total_pieces, hipStre
 hipError_t launch_pack(const float* w, int64_t n, int64_t k, uint8_t* packed, float* w_scale,
                        unsigned long long* buckets, hipStream_t s);
 hipError_t launch_unpack(const uint8_t* packed, int64_t n, int64_t k, int8_t* u, hipStream_t s);
+// Row-major packed weights <-> the 16-row tiled layout (n % 16 == 0,
+// k % 256 == 0); `untile` runs the inverse permutation.
+hipError_t launch_tile(const uint8_t* src, int64_t n, int64_t k, uint8_t* dst, bool untile,
+                       hipStream_t s);
 
 }  // namespace bl

@@ -102,6 +102,23 @@ __global__ __launch_bounds__(256) void unpack_kernel(const uint8_t* __restrict__
   }
 }
 
+// Row-major <-> tiled layout (common.hpp): one 16-byte chunk per thread and
+// step, walked in the order of the tiled bytes.  A block of 16 rows holds
+// rowbytes chunks; chunk u of a block is row u % 16, chunk (u / 16) % 4 of
+// that row's 64 bytes in tile u / 64.
+__global__ __launch_bounds__(256) void tile_kernel(const uint8_t* __restrict__ src, int64_t chunks,
+                                                   int64_t rowbytes, uint8_t* __restrict__ dst,
+                                                   int untile) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t d = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; d < chunks; d += stride) {
+    const int64_t blk = d / rowbytes, u = d - blk * rowbytes;
+    const int64_t row = 16 * blk + (u & 15);
+    const int64_t rowpos = row * rowbytes + 64 * (u >> 6) + 16 * ((u >> 4) & 3);
+    const int64_t from = untile ? 16 * d : rowpos, to = untile ? rowpos : 16 * d;
+    *G(reinterpret_cast<v4i*>(dst + to)) = *G(reinterpret_cast<const v4i*>(src + from));
+  }
+}
+
 int grid_for(int64_t work, int per_block, int cap) {
   int64_t g = (work + per_block - 1) / per_block;
   if (g < 1) g = 1;
@@ -120,6 +137,14 @@ hipError_t launch_pack(const float* w, int64_t n, int64_t k, uint8_t* packed, fl
   const int64_t nbytes = count / 4;
   ternarize_pack_kernel<<<grid_for(nbytes, 256 * 4, 8192), 256, 0, s>>>(w, nbytes, w_scale,
                                                                         packed);
+  return hipGetLastError();
+}
+
+hipError_t launch_tile(const uint8_t* src, int64_t n, int64_t k, uint8_t* dst, bool untile,
+                       hipStream_t s) {
+  const int64_t chunks = n * k / 64;
+  tile_kernel<<<grid_for(chunks, 256 * 4, 8192), 256, 0, s>>>(src, chunks, k / 4, dst,
+                                                              untile ? 1 : 0);
   return hipGetLastError();
 }
 

@@ -87,10 +87,15 @@ __device__ __forceinline__ void load_b(v4i (&b)[4][2], const PrefillProj& P, int
 #pragma unroll
   for (int f = 0; f < 4; ++f) {
     const int row = min(ncol0 + 32 * f + lj, P.n - 1);
-    const uint8_t* rp = P.packed + (int64_t)row * rowbytes;
     const int off = slab * 64 + 32 * lg;
-    b[f][0] = load_w16<MODE>(rp, off, rowbytes);
-    b[f][1] = load_w16<MODE>(rp, off + 16, rowbytes);
+    if (P.tiled) {  // 64-byte aligned rows: two whole chunks (common.hpp)
+      b[f][0] = *G(reinterpret_cast<const v4i*>(P.packed + tiled_chunk_offset(row, off, rowbytes)));
+      b[f][1] = *G(reinterpret_cast<const v4i*>(P.packed + tiled_chunk_offset(row, off + 16, rowbytes)));
+    } else {
+      const uint8_t* rp = P.packed + (int64_t)row * rowbytes;
+      b[f][0] = load_w16<MODE>(rp, off, rowbytes);
+      b[f][1] = load_w16<MODE>(rp, off + 16, rowbytes);
+    }
   }
 }
 
@@ -311,6 +316,7 @@ struct Stager {
   const uint8_t* brow[K::kBDma];
   int bc[K::kBDma];  // byte offset of the lane's chunk within a slab of a weight row
   int rowbytes;
+  int bstep;  // bytes from one slab of a weight row to the next
 
   __device__ __forceinline__ Stager(const PrefillProj& P, int m0, int n0) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -321,12 +327,17 @@ struct Stager {
       a[i] = P.q + (int64_t)(m0 + r) * P.ldq + 16 * c;
     }
     rowbytes = P.k >> 2;
+    // row-major: chunk c of a slab at 16 c, slabs BK/4 bytes apart.  Tiled
+    // (common.hpp, k % 256 == 0): a slab of 16 rows is one contiguous run of
+    // 4 * BK bytes in the rows' block, chunk c of row r at 256 c + 16 (r % 16).
+    bstep = P.tiled ? 4 * BK : BK / 4;
 #pragma unroll
     for (int i = 0; i < K::kBDma; ++i) {
       const int pos = (wave * K::kBDma + i) * 64 + lane;
       const int j = pos / K::kBCh, c = K::bswz(j, pos % K::kBCh);
-      brow[i] = P.packed + (int64_t)min(n0 + j, P.n - 1) * rowbytes;
-      bc[i] = 16 * c;
+      const int64_t r = min(n0 + j, P.n - 1);
+      brow[i] = P.packed + (P.tiled ? (r >> 4) * 16 * rowbytes + 16 * (r & 15) : r * rowbytes);
+      bc[i] = P.tiled ? 256 * c : 16 * c;
     }
   }
 
@@ -338,9 +349,10 @@ struct Stager {
     for (int i = 0; i < K::kADma; ++i) dma16(a[i] + slab * BK, st + (wave * K::kADma + i) * 1024);
     int8_t* bst = st + K::kAChunks * 16;
     const int b0 = slab * (BK / 4);
-    if (b0 + BK / 4 <= rowbytes) {
+    if (b0 + BK / 4 <= rowbytes) {  // always so in the tiled layout
 #pragma unroll
-      for (int i = 0; i < K::kBDma; ++i) dma16(brow[i] + b0 + bc[i], bst + (wave * K::kBDma + i) * 1024);
+      for (int i = 0; i < K::kBDma; ++i)
+        dma16(brow[i] + slab * bstep + bc[i], bst + (wave * K::kBDma + i) * 1024);
     } else {
 #pragma unroll
       for (int i = 0; i < K::kBDma; ++i)

@@ -28,6 +28,19 @@
  * weight k at bits 2*(k%4)..2*(k%4)+1 as the code c = u + 1 (0, 1 or 2).
  * Code 3 is never written; if present in caller data it decodes as +2.
  *
+ * Tiled weight layout (optional, N % 16 == 0 and K % 256 == 0): the same
+ * N*K/4 bytes, permuted inside every block of 16 rows.  The block of rows
+ * 16b..16b+15 keeps its place (bytes 16b*K/4 .. (16b+16)*K/4) and is stored
+ * as K/256 tiles of 1 KB, tile t holding packed bytes 64t..64t+63 of each of
+ * its 16 rows: the 16-byte chunk g (0..3) of row 16b+r sits at byte
+ * 1024t + 256g + 16r of the block.  Row-major byte o of row n is therefore
+ * at (n/16)*16*(K/4) + 1024*(o/64) + 256*((o/16)%4) + 16*(n%16) + o%16.
+ * Each tile is what one 64-lane wavefront reads for a 16-row operand of the
+ * 16x16x64 int8 matrix-core op, so decode streams the weights in contiguous
+ * 1 KB pieces.  bitlinear_tile_weights / bitlinear_untile_weights convert;
+ * the *_tiled entry points and bl_projection.layout take it.  Results are
+ * identical to those on the row-major bytes.
+ *
  * Conventions for every entry point:
  *  - All tensor pointers are DEVICE pointers to contiguous row-major data,
  *    owned by the caller.  The library never allocates, frees, or
@@ -71,7 +84,13 @@ typedef struct {
   uint16_t *y;            /* [M][N] bf16 output (device) */
   int64_t n;              /* N, output features */
   int64_t k;              /* K, input features */
+  int32_t layout;         /* BL_LAYOUT_ROWS (0) or BL_LAYOUT_TILED (1) */
+  int32_t reserved;       /* must be 0 */
 } bl_projection;
+
+/* Weight layouts (bl_projection.layout). */
+#define BL_LAYOUT_ROWS 0  /* row-major [N][K/4] */
+#define BL_LAYOUT_TILED 1 /* 16-row tiled (N % 16 == 0, K % 256 == 0) */
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char *bitlinear_status_string(bl_status s);
@@ -101,6 +120,17 @@ bl_status bitlinear_pack_weights(const float *w, int64_t n, int64_t k,
 bl_status bitlinear_unpack_weights(const uint8_t *packed, int64_t n,
                                    int64_t k, int8_t *u, void *stream);
 
+/* Row-major packed weights -> the tiled layout (a byte permutation; see
+ * above).  packed: [N][K/4]; tiled: N*K/4 bytes (written).  N % 16 == 0 and
+ * K % 256 == 0, else BL_ESHAPE; the two arrays must not overlap (BL_EINVAL).
+ * One kernel. */
+bl_status bitlinear_tile_weights(const uint8_t *packed, int64_t n, int64_t k,
+                                 uint8_t *tiled, void *stream);
+
+/* The inverse: tiled layout -> row-major [N][K/4].  Same rules. */
+bl_status bitlinear_untile_weights(const uint8_t *tiled, int64_t n, int64_t k,
+                                   uint8_t *packed, void *stream);
+
 /* --- activation quantization ------------------------------------------ */
 
 /* The blog's activation_norm_quant on bf16 input.  x: [M][K] bf16.
@@ -126,7 +156,17 @@ bl_status bitlinear_forward(int64_t m, int64_t n, int64_t k,
                             void *workspace, size_t workspace_bytes,
                             void *stream);
 
-/* Bytes of workspace bitlinear_forward_grouped needs. */
+/* bitlinear_forward with the weights in the tiled layout (N % 16 == 0,
+ * K % 256 == 0, else BL_ESHAPE).  Workspace:
+ * bitlinear_forward_workspace_bytes(m, n, k).  Same results. */
+bl_status bitlinear_forward_tiled(int64_t m, int64_t n, int64_t k,
+                                  const uint16_t *x, const uint8_t *tiled,
+                                  const float *w_scale, uint16_t *y,
+                                  void *workspace, size_t workspace_bytes,
+                                  void *stream);
+
+/* Bytes of workspace bitlinear_forward_grouped needs (the layouts do not
+ * change it). */
 size_t bitlinear_forward_grouped_workspace_bytes(int32_t count,
                                                  const bl_projection *projs,
                                                  int64_t m);
@@ -135,7 +175,9 @@ size_t bitlinear_forward_grouped_workspace_bytes(int32_t count,
  * instance the projections of one decoder layer) in one pass: one
  * activation-quantization launch and one contraction launch for all of
  * them.  projs: HOST array of `count` descriptors (1 <= count <= 16);
- * results are identical to calling bitlinear_forward on each. */
+ * results are identical to calling bitlinear_forward on each.  Each
+ * descriptor names its weights' layout; an unknown layout is BL_EINVAL, a
+ * tiled one with N % 16 != 0 or K % 256 != 0 is BL_ESHAPE. */
 bl_status bitlinear_forward_grouped(int32_t count, const bl_projection *projs,
                                     int64_t m, void *workspace,
                                     size_t workspace_bytes, void *stream);
@@ -149,6 +191,13 @@ bl_status bitlinear_forward_acc(int64_t m, int64_t n, int64_t k,
                                 const int8_t *q, const uint8_t *packed,
                                 int32_t *acc, void *workspace,
                                 size_t workspace_bytes, void *stream);
+
+/* bitlinear_forward_acc with the weights in the tiled layout (N % 16 == 0,
+ * K % 256 == 0, else BL_ESHAPE). */
+bl_status bitlinear_forward_acc_tiled(int64_t m, int64_t n, int64_t k,
+                                      const int8_t *q, const uint8_t *tiled,
+                                      int32_t *acc, void *workspace,
+                                      size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

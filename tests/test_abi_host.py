@@ -45,7 +45,7 @@ def declared_functions():
 
 def test_exports_every_declared_function(bl):
     names = declared_functions()
-    assert len(names) == 11
+    assert len(names) == 15
     lib = bl.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -88,7 +88,7 @@ def test_probe_library_exports_and_validation():
 
 def test_status_strings_and_version(bl):
     lib = bl.lib()
-    assert lib.bitlinear_abi_version() == 1
+    assert lib.bitlinear_abi_version() == 2
     for s in range(6):
         assert lib.bitlinear_status_string(s)
     assert lib.bitlinear_status_string(99) == b"unknown status"
@@ -134,6 +134,40 @@ def test_other_entry_points_validation(bl):
     assert lib.bitlinear_unpack_weights(a, 16, 64, None, None) == 1
     assert lib.bitlinear_forward_acc(1, 16, 64, a, b, c, None, 1 << 30, None) == 4
     assert lib.bitlinear_forward_acc(1, 16, 60, None, b, c, d, 1 << 30, None) == 1
+
+
+def test_tiled_layout_validation(bl):
+    """The tiled-layout entry points reject bad calls before enqueueing."""
+    lib = bl.lib()
+    a, b, c, d, e = A16[:5]
+    big = ctypes.c_size_t(1 << 40)
+    for fn in (lib.bitlinear_tile_weights, lib.bitlinear_untile_weights):
+        assert fn(None, 16, 256, b, None) == 1
+        assert fn(a, 16, 256, None, None) == 1
+        assert fn(a, 8, 256, b, None) == 2    # N % 16
+        assert fn(a, 16, 128, b, None) == 2   # K % 256
+        assert fn(a, 16, 258, b, None) == 2   # K % 4
+        assert fn(a, 0, 256, b, None) == 2
+        assert fn(P(0x10008), 16, 256, b, None) == 3
+        assert fn(a, 16, 256, a, None) == 1   # in place
+        assert fn(a, 16, 256, P(0x10000 + 512), None) == 1  # overlapping (1 KB arrays)
+    assert lib.bitlinear_forward_tiled(1, 8, 256, a, b, c, d, e, big, None) == 2
+    assert lib.bitlinear_forward_tiled(1, 16, 192, a, b, c, d, e, big, None) == 2
+    assert lib.bitlinear_forward_tiled(1, 16, 256, a, None, c, d, e, big, None) == 1
+    assert lib.bitlinear_forward_tiled(1, 16, 256, a, b, c, d, None, big, None) == 4
+    assert lib.bitlinear_forward_acc_tiled(1, 24, 256, a, b, c, d, big, None) == 2
+    assert lib.bitlinear_forward_acc_tiled(1, 16, 256, a, b, None, d, big, None) == 1
+    Proj = bl.Projection
+    arr = (Proj * 1)()
+    arr[0] = Proj(0x10000, 0x20000, 0x30000, 0x40000, 64, 256, 2, 0)
+    assert lib.bitlinear_forward_grouped(1, arr, 1, A16[0], 1 << 30, None) == 1  # layout 2
+    arr[0].layout, arr[0].reserved = 1, 7
+    assert lib.bitlinear_forward_grouped(1, arr, 1, A16[0], 1 << 30, None) == 1  # reserved
+    arr[0].reserved, arr[0].n = 0, 40
+    assert lib.bitlinear_forward_grouped(1, arr, 1, A16[0], 1 << 30, None) == 2  # N % 16
+    arr[0].n, arr[0].k = 64, 320
+    assert lib.bitlinear_forward_grouped(1, arr, 1, A16[0], 1 << 30, None) == 2  # K % 256
+    assert ctypes.sizeof(Proj) == 56
 
 
 def test_grouped_validation_and_sizes(bl):

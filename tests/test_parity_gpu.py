@@ -175,6 +175,71 @@ def test_forward_acc_parity(bl, m, n, k):
     assert np.array_equal(acc.cpu().numpy(), ref)
 
 
+# ------------------------------------------------------------------ tiled weight layout
+
+@pytest.mark.parametrize("n,k", [(16, 256), (32, 1024), (48, 14336), (160, 2560), (2048, 2048)])
+def test_tile_parity(bl, n, k):
+    rng = np.random.default_rng(n * 7 + k)
+    packed = rng.integers(0, 256, size=(n, k // 4), dtype=np.int16).astype(np.uint8)
+    dp = torch.from_numpy(packed).to(DEV)
+    tiled = bl.tile_weights(dp)
+    assert tiled.shape == (n // 16, 4 * k)
+    assert np.array_equal(tiled.cpu().numpy(), oracle.tile(packed))
+    assert torch.equal(bl.untile_weights(tiled), dp)
+
+
+TILED_ACC_SHAPES = [
+    # decode: one row tile, split shape, ring shape, rows over several waves,
+    # K split across waves and across workgroups
+    (1, 16, 256), (1, 2048, 2048), (3, 32, 1024), (16, 64, 256), (4, 272, 4096),
+    (16, 3072, 9216), (8, 112, 65536), (13, 80, 30720), (5, 48, 40960),
+    # prefill: one tile, ragged M, K split across workgroups, a narrow tail
+    (17, 16, 256), (128, 128, 256), (129, 48, 2048), (200, 304, 16384), (2048, 8448, 256),
+]
+
+
+@pytest.mark.parametrize("m,n,k", TILED_ACC_SHAPES)
+def test_forward_acc_tiled_parity(bl, m, n, k):
+    rng = np.random.default_rng(m * 1000003 + n * 1009 + k + 1)
+    q = rng.integers(-128, 128, size=(m, k), dtype=np.int16).astype(np.int8)
+    packed = rng.integers(0, 256, size=(n, k // 4), dtype=np.int16).astype(np.uint8)  # incl. code 3
+    tiled = torch.from_numpy(oracle.tile(packed)).to(DEV)
+    acc = bl.forward_acc(torch.from_numpy(q).to(DEV), tiled)
+    assert np.array_equal(acc.cpu().numpy(), oracle.forward_acc(q, packed))
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 2048, 2048), (4, 96, 4096), (16, 304, 9216), (64, 208, 512),
+                                   (256, 384, 2560)])
+def test_forward_tiled_parity(bl, m, n, k):
+    x, w = wls.random_case(37, m, n, k, scale=2.0)
+    if m > 4:
+        x[m // 2] = 0
+    p_ref, ws_ref = oracle.pack_weights(w)
+    packed, ws = bl.pack_weights(torch.from_numpy(w).to(DEV))
+    y = bl.forward(dev_bf16(x), bl.tile_weights(packed), ws)
+    assert_bf16_close(host_bits(y), oracle.forward(x, p_ref, ws_ref), f"tiled {m}x{n}x{k}")
+
+
+@pytest.mark.parametrize("m", [1, 3, 16, 40, 300])
+def test_grouped_mixed_layouts(bl, m):
+    """Tiled and row-major projections in one launch, with a ragged
+    row-major one that makes the launch use the narrow-load variants (the
+    tiled projections then take their weights through those kernels)."""
+    shapes = [(64, 256, True), (33, 260, False), (96, 1024, True), (40, 1024, False)]
+    xs, ps, ss, refs = [], [], [], []
+    for i, (n, k, tiled) in enumerate(shapes):
+        x, w = wls.random_case(90 + 5 * m + i, m, n, k)
+        p, s = bl.pack_weights(torch.from_numpy(w).to(DEV))
+        xs.append(dev_bf16(x))
+        ps.append(bl.tile_weights(p) if tiled else p)
+        ss.append(s)
+        refs.append(oracle.forward(x, *oracle.pack_weights(w)))
+    for use in (slice(0, 4), slice(2, 4)):  # with and without the ragged projection
+        ys = bl.forward_grouped(xs[use], ps[use], ss[use])
+        for (n, k, t), y, r in zip(shapes[use], ys, refs[use]):
+            assert_bf16_close(host_bits(y), r, f"mixed {m}x{n}x{k} tiled={t}")
+
+
 # ------------------------------------------------------------------ forward (bf16)
 
 FWD_SHAPES = [(1, 16, 64), (1, 2048, 2048), (3, 50, 36), (8, 2048, 2048), (16, 96, 4096),
@@ -294,7 +359,8 @@ _PACK_CACHE = {}
 
 def packed_workload(bl, wl):
     """GPU-packed weights of every projection, checked bit-exact against the
-    oracle the first time a workload is used."""
+    oracle the first time a workload is used, and their tiled layout (two
+    sampled blocks of 16 rows checked against the oracle's tiling)."""
     if wl.name not in _PACK_CACHE:
         _PACK_CACHE.clear()
         entries = []
@@ -304,7 +370,12 @@ def packed_workload(bl, wl):
             p, s = bl.pack_weights(torch.from_numpy(w).to(DEV))
             assert f32_bits(s.cpu().numpy()[0]) == f32_bits(s_ref), wl.projections[pi].name
             assert torch.equal(p.cpu(), torch.from_numpy(p_ref)), wl.projections[pi].name
-            entries.append((p, s, p_ref, s_ref))
+            t = bl.tile_weights(p)
+            nb = p_ref.shape[0] // 16
+            for b in (0, nb // 2 + 1, nb - 1):
+                assert np.array_equal(t[b].cpu().numpy(),
+                                      oracle.tile(p_ref[16 * b:16 * b + 16]).reshape(-1))
+            entries.append((p, s, p_ref, s_ref, t))
             del w
         _PACK_CACHE[wl.name] = entries
     return _PACK_CACHE[wl.name]
@@ -313,12 +384,16 @@ def packed_workload(bl, wl):
 @pytest.mark.parametrize("name,m,variant", workload_cases())
 def test_workload_parity(bl, name, m, variant):
     """Every projection of the workload, full size, in one grouped call
-    (the launch configuration the benchmark times)."""
+    (the launch configuration the benchmark times, whose weights are tiled),
+    with the weights in both layouts."""
     wl = wls.WORKLOADS[name]
     entries = packed_workload(bl, wl)
     xs = [wls.activations(wl, pi, m, variant) for pi in range(len(wl.projections))]
-    ys = bl.forward_grouped([dev_bf16(x) for x in xs], [e[0] for e in entries],
-                            [e[1] for e in entries])
-    for pi, (x, y, e) in enumerate(zip(xs, ys, entries)):
+    dxs = [dev_bf16(x) for x in xs]
+    scales = [e[1] for e in entries]
+    ys = bl.forward_grouped(dxs, [e[0] for e in entries], scales)
+    yts = bl.forward_grouped(dxs, [e[4] for e in entries], scales)
+    for pi, (x, y, yt, e) in enumerate(zip(xs, ys, yts, entries)):
         y_ref = oracle.forward(x, e[2], e[3])
         assert_bf16_close(host_bits(y), y_ref, f"{name} {wl.projections[pi].name} M={m}")
+        assert_bf16_close(host_bits(yt), y_ref, f"{name} {wl.projections[pi].name} M={m} tiled")
