@@ -240,6 +240,20 @@ def test_grouped_mixed_layouts(bl, m):
             assert_bf16_close(host_bits(y), r, f"mixed {m}x{n}x{k} tiled={t}")
 
 
+@pytest.mark.parametrize("n,k,tiled", [(96, 512, True), (96, 512, False), (40, 260, True)])
+def test_bitlinear_layer_class(bl, n, k, tiled):
+    """The BitLinear layer class: packs once (tiled when the shape allows and
+    asked for), takes activations of any leading shape."""
+    x, w = wls.random_case(77, 6, n, k)
+    layer = bl.BitLinear(torch.from_numpy(w).to(DEV), tiled=tiled)
+    uses_tiles = tiled and n % 16 == 0 and k % 256 == 0
+    assert tuple(layer.packed.shape) == ((n // 16, 4 * k) if uses_tiles else (n, k // 4))
+    y = layer(dev_bf16(x).reshape(2, 3, k))
+    assert tuple(y.shape) == (2, 3, n)
+    y_ref = oracle.forward(x, *oracle.pack_weights(w))
+    assert_bf16_close(host_bits(y.reshape(6, n).contiguous()), y_ref, "BitLinear class")
+
+
 # ------------------------------------------------------------------ forward (bf16)
 
 FWD_SHAPES = [(1, 16, 64), (1, 2048, 2048), (3, 50, 36), (8, 2048, 2048), (16, 96, 4096),
