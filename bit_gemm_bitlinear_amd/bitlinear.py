@@ -149,6 +149,8 @@ def untile_weights(tiled: torch.Tensor) -> torch.Tensor:
     """The inverse of tile_weights: [N/16, 4*K] -> row-major [N, K/4]."""
     _require(tiled, torch.uint8, 2, "tiled")
     nb, kb16 = tiled.shape
+    if kb16 % 1024:
+        raise ValueError("a tiled weight row holds 16 rows of K/4 bytes, K % 256 == 0")
     n, k = 16 * nb, kb16 // 4
     packed = torch.empty((n, k // 4), dtype=torch.uint8, device=tiled.device)
     _check(_lib.bitlinear_untile_weights(_ptr(tiled), n, k, _ptr(packed), _stream(tiled)))
@@ -160,7 +162,7 @@ def weight_layout(w: torch.Tensor, k: int):
     is row-major, [N/16, 4*K] the tiled layout."""
     if w.shape[1] * 4 == k:
         return w.shape[0], LAYOUT_ROWS
-    if w.shape[1] == 4 * k:
+    if w.shape[1] == 4 * k and k % 256 == 0:
         return 16 * w.shape[0], LAYOUT_TILED
     raise ValueError("packed weights do not match K")
 
