@@ -741,6 +741,7 @@ bool plan_decode_split(int64_t m, int32_t count, const int64_t* ns, const int64_
                        int cus, DecodePlan* plans) {
   constexpr int kMaxChunks = 96;  // per lane: at most six rounds of the ring
   constexpr int kSplitPlanMinChunks = 48;
+  constexpr int kSmallLayerCuShare = 4;  // "most CUs idle": a quarter of them or fewer busy
   if (mode != 0 || count < 1 || count > kMaxProj) return false;
   int S[kMaxProj];
   int64_t tiles[kMaxProj];
@@ -779,8 +780,19 @@ bool plan_decode_split(int64_t m, int32_t count, const int64_t* ns, const int64_
     }
     // Shorter streams are left to the per-projection plans: measured on
     // the 3B-class layer (36 chunks per wave here) the many-workgroup ring
-    // shape was faster, on the 8B-class layer (64) this plan was.
-    if (ok && total <= cus) return x >= kSplitPlanMinChunks;
+    // shape was faster, on the 8B-class layer (64) this plan was.  Except
+    // when those plans would leave most CUs idle (a small layer: a single
+    // 2048 x 2048 projection at M = 8 takes 16 workgroups of 64 KB, against
+    // 128 of 8 KB here; measured 10.8 -> 8.9 us per call).
+    if (ok && total <= cus) {
+      if (x >= kSplitPlanMinChunks) return true;
+      int64_t own = 0;
+      for (int i = 0; i < count; ++i) {
+        const DecodePlan q = plan_decode(m, ns[i], ks[i], mode);
+        own += (int64_t)q.ngroups * q.ksplit;
+      }
+      return own * kSmallLayerCuShare <= cus;
+    }
   }
   return false;
 }
