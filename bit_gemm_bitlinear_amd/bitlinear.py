@@ -53,6 +53,8 @@ _SIGS = {
     "bitlinear_forward_grouped_workspace_bytes": (_sz, [_i32, ctypes.POINTER(Projection), _i64]),
     "bitlinear_forward_grouped": (ctypes.c_int, [_i32, ctypes.POINTER(Projection), _i64, _vp,
                                                  _sz, _vp]),
+    "bitlinear_forward_grouped_noalloc": (ctypes.c_int, [_i32, ctypes.POINTER(Projection), _i64,
+                                                         _vp]),
     "bitlinear_forward_acc": (ctypes.c_int, [_i64, _i64, _i64, _vp, _vp, _vp, _vp, _sz, _vp]),
     "bitlinear_forward_acc_tiled": (ctypes.c_int, [_i64, _i64, _i64, _vp, _vp, _vp, _vp, _sz,
                                                    _vp]),

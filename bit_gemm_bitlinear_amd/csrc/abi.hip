@@ -7,6 +7,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "internal.hpp"
 #include "prefill_plan.hpp"
@@ -324,6 +325,32 @@ bl_status run_forward(int32_t count, const ProjIO* io, int64_t m, void* workspac
   return BL_OK;
 }
 
+// Device memory of bitlinear_forward_grouped_noalloc: a fixed array in the
+// code object, so that call needs no allocation.  Each GPU the library runs
+// on holds its own copy for the life of the process.  Its host-side name is
+// only a stand-in for registration: kernels get the device address that
+// hipGetSymbolAddress reports for the current device.
+constexpr size_t kScratchBytes = (size_t)BL_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device, looked up once per
+// device with that device current; nullptr on failure.
+void* scratch_address() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -458,10 +485,8 @@ size_t bitlinear_forward_grouped_workspace_bytes(int32_t count, const bl_project
   return L.total;
 }
 
-bl_status bitlinear_forward_grouped(int32_t count, const bl_projection* projs, int64_t m,
-                                    void* workspace, size_t workspace_bytes, void* stream) {
+static bl_status grouped_io(int32_t count, const bl_projection* projs, int64_t m, ProjIO* io) {
   if (count < 1 || count > kMaxProj || !projs) return BL_EINVAL;
-  ProjIO io[kMaxProj];
   for (int i = 0; i < count; ++i) {
     const bl_projection& p = projs[i];
     bl_status st;
@@ -475,7 +500,33 @@ bl_status bitlinear_forward_grouped(int32_t count, const bl_projection* projs, i
     io[i] = ProjIO{p.x,      nullptr, p.packed, p.w_scale, p.y,
                    nullptr, p.n,     p.k,      p.layout == BL_LAYOUT_TILED ? 1 : 0};
   }
+  return BL_OK;
+}
+
+bl_status bitlinear_forward_grouped(int32_t count, const bl_projection* projs, int64_t m,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+  ProjIO io[kMaxProj];
+  const bl_status st = grouped_io(count, projs, m, io);
+  if (st != BL_OK) return st;
   return run_forward(count, io, m, workspace, workspace_bytes, static_cast<hipStream_t>(stream));
+}
+
+bl_status bitlinear_forward_grouped_noalloc(int32_t count, const bl_projection* projs, int64_t m,
+                                            void* stream) {
+  ProjIO io[kMaxProj];
+  const bl_status st = grouped_io(count, projs, m, io);
+  if (st != BL_OK) return st;
+  int64_t ns[kMaxProj], ks[kMaxProj];
+  for (int i = 0; i < count; ++i) {
+    ns[i] = io[i].n;
+    ks[i] = io[i].k;
+  }
+  Layout L;
+  make_layout(count, ns, ks, m, false, L);
+  if (L.total > kScratchBytes) return BL_EWORKSPACE;
+  void* ws = scratch_address();
+  if (!ws) return BL_EHIP;
+  return run_forward(count, io, m, ws, kScratchBytes, static_cast<hipStream_t>(stream));
 }
 
 static bl_status forward_acc_one(int64_t m, int64_t n, int64_t k, const int8_t* q,

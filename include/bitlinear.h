@@ -44,7 +44,10 @@
  * Conventions for every entry point:
  *  - All tensor pointers are DEVICE pointers to contiguous row-major data,
  *    owned by the caller.  The library never allocates, frees, or
- *    synchronizes, and keeps no state between calls; calls are thread-safe.
+ *    synchronizes, and keeps no state between calls (apart from the device
+ *    address of the no-alloc entry point's scratch array, looked up once per
+ *    device); calls are thread-safe, except that no-alloc calls on one GPU
+ *    must not overlap.
  *  - `stream` is a hipStream_t (NULL = the default stream).  Work is only
  *    enqueued; results are ready once the stream has reached that point.
  *  - Arguments are validated on the host before anything is enqueued.  On
@@ -181,6 +184,24 @@ size_t bitlinear_forward_grouped_workspace_bytes(int32_t count,
 bl_status bitlinear_forward_grouped(int32_t count, const bl_projection *projs,
                                     int64_t m, void *workspace,
                                     size_t workspace_bytes, void *stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * bitlinear_forward_grouped without a workspace argument.  Its scratch
+ * memory is a fixed array of BL_NOALLOC_SCRATCH_BYTES in the library's code
+ * object; each GPU the library runs on holds its own copy until the process
+ * ends.  The call allocates nothing (no hipMalloc, hipFree or allocating
+ * library routine); on its first use on a device it looks up that device's
+ * copy of the array.  Arguments, results and launches are those of
+ * bitlinear_forward_grouped; a call whose
+ * bitlinear_forward_grouped_workspace_bytes exceeds BL_NOALLOC_SCRATCH_BYTES
+ * returns BL_EWORKSPACE and enqueues nothing.  Every call on one GPU uses the
+ * same array (the library clears what must start at zero): calls that
+ * overlap on one GPU -- on different streams, or from different threads --
+ * race and give undefined results; serialize them. */
+#define BL_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+bl_status bitlinear_forward_grouped_noalloc(int32_t count, const bl_projection *projs,
+                                            int64_t m, void *stream);
 
 /* Integer accumulators of caller-supplied int8 codes: acc = q . u^T.
  * q: [M][K] int8 (any values); packed: [N][K/4]; acc: [M][N] int32

@@ -45,7 +45,7 @@ def declared_functions():
 
 def test_exports_every_declared_function(bl):
     names = declared_functions()
-    assert len(names) == 15
+    assert len(names) == 16
     lib = bl.lib()
     for n in names:
         assert hasattr(lib, n), n
