@@ -1,29 +1,38 @@
 """Benchmark of the BitLinear forward pass on one MI355X.
 
-Default workload: decode (M=1) over the seven BitLinear projections of a
-d=2048 / ffn=8192 decoder layer -- one grouped forward per step, which is one
-kernel launch (activation quantization is fused into the decode kernel).  The
-metric is GB/s of packed (2-bit) weights streamed, as a fraction of HBM
-bandwidth.  A secondary measurement times the matrix-core prefill path (M=2048
-over the d=2560 / ffn=6912 FFN) in int8 TOPS against the int8 MFMA peak.
+Headline: decode (M=1) over the seven BitLinear projections of the 8B-class
+layer (d=4096, ffn=14336, GQA k/v 1024) -- one grouped forward per step, one
+kernel launch.  The metric is GB/s of packed (2-bit) weights streamed, as a
+fraction of HBM bandwidth.  Every other workload is measured in the same run
+and reported in the `configs` array: decode configurations in GB/s of packed
+weights (HBM roofline), prefill configurations in int8 TOPS (matrix-core
+roofline).
 
-Protocol: inputs are seeded synthetic tensors resident in HBM before the
-timed region.  To measure HBM rather than the 256 MB Infinity Cache, each
-step uses the next of R copies of the layer's packed weights (R copies span
-at least 1 GiB).  Steps are replayed from a captured HIP graph (one graph
-holds one pass over the R copies), so host launch overhead is not timed.
-The timed region is bracketed by torch.cuda.synchronize() and by HIP events
-recorded on the stream the kernels are launched on.
+Protocol (every configuration):
+  * inputs are seeded synthetic tensors, packed and tiled on the GPU by the
+    library, resident in HBM before the timed region;
+  * to measure HBM rather than the 256 MB Infinity Cache, step i uses copy
+    i % R of the configuration's operands (decode: the packed weights;
+    prefill: weights, activations and outputs), R copies spanning >= 1 GiB;
+  * a "sample" is one replay of a captured HIP graph of exactly --steps
+    steps; graphs cover successive ranges of the copy rotation;
+  * --warmup steps run untimed first; then samples are replayed back to back
+    (at least --min-seconds of GPU time, the headline --headline-seconds),
+    each bracketed by HIP events on the stream the graph is launched on,
+    with torch.cuda.synchronize() before and after;
+  * ms_per_step is the median over samples of (sample time / steps); the
+    10th/90th percentiles and the minimum are reported as the spread.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--m M]
+    python bench.py [--steps K] [--warmup W] [--only W:M[,W:M]]
 
 Profiling helpers (the summaries under profiles/ are written by these):
 
-    python bench.py --pmc-probe ...            eager steps + a copy kernel of known size
-    python bench.py --summarize-stats DIR      text summary of a rocprofv3 --stats run
-    python bench.py --summarize-pmc FDIR WDIR [--pmc-kernel decode|prefill]
-                                               HBM traffic per dispatch from FETCH_SIZE /
-                                               WRITE_SIZE runs, scaled by the copy kernel
+    python bench.py --pmc-probe --workload W --m M   eager steps + a copy kernel of known size
+    python bench.py --summarize-stats DIR            text summary of a rocprofv3 --stats run
+    python bench.py --summarize-pmc FDIR WDIR --workload W --m M --pmc-kernel decode|prefill
+                                                     HBM traffic per dispatch, scaled by the copy kernel
+    python bench.py --summarize-counters DIR --workload W --m M --pmc-kernel prefill
+                                                     matrix-core counters per dispatch
 """
 
 from __future__ import annotations
@@ -33,6 +42,7 @@ import csv
 import glob
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -44,47 +54,53 @@ sys.path.insert(0, ROOT)
 
 METRIC = "BitLinear decode GB/s of packed weights (% HBM peak); prefill int8 TOPS (% MFMA)"
 HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, published
-MFMA_I8_PEAK_TOPS = 5000.0  # MI355X dense int8 matrix peak, published
+MFMA_I8_PEAK_TOPS = 5000.0  # MI355X dense int8 matrix peak, published (POPS x 1000)
 
-# Per kernel: the name rocprofv3 reports, the sources it is built from (a
-# traffic figure measured on other sources is stale and is not reported) and
-# the committed summary of its HBM traffic.
+# (workload, M) of every configuration, in the workload list's order; the
+# headline is the largest single-GPU decode configuration.
+CONFIGS = [("single_2048_m8", 8), ("decode_1b_m1", 1), ("decode_3b", 1), ("decode_3b", 4),
+           ("decode_3b", 16), ("prefill_2b_m2048", 2048), ("layer_8b", 1), ("layer_8b", 512)]
+HEADLINE = ("layer_8b", 1)
+
+# Per kernel: the name rocprofv3 reports and the sources it is built from (a
+# counter figure measured on other sources is stale and is not reported).
 PMC_KERNELS = {
-    "decode": {
-        "name": "decode_kernel",
-        "sources": ["decode.hip", "common.hpp", "row_div.hpp", "internal.hpp"],
-        "file": os.path.join(ROOT, "profiles", "decode_kernel_decode_1b_m1_traffic.txt"),
-    },
-    "prefill": {
-        "name": "prefill_kernel",
-        "sources": ["prefill.hip", "prefill_plan.hpp", "abi.hip", "common.hpp", "row_div.hpp",
-                    "internal.hpp"],
-        "file": os.path.join(ROOT, "profiles", "prefill_kernel_prefill_2b_m2048_traffic.txt"),
-    },
+    "decode": {"name": "decode_kernel",
+               "sources": ["decode.hip", "common.hpp", "row_div.hpp", "internal.hpp"]},
+    "prefill": {"name": "prefill_kernel",
+                "sources": ["prefill.hip", "prefill_plan.hpp", "abi.hip", "common.hpp",
+                            "row_div.hpp", "internal.hpp"]},
 }
 COPY_PROBE_MIB = 512
+
+
+def traffic_file(kind, workload, m):
+    return os.path.join(ROOT, "profiles", f"{PMC_KERNELS[kind]['name']}_{workload}_m{m}_traffic.txt")
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=4096)
-    ap.add_argument("--warmup", type=int, default=256)
-    ap.add_argument("--workload", default="decode_1b_m1")
+    ap.add_argument("--steps", type=int, default=100, help="steps per timed sample")
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--min-seconds", type=float, default=0.3,
+                    help="GPU time of the timed samples per configuration")
+    ap.add_argument("--headline-seconds", type=float, default=1.5)
+    ap.add_argument("--only", default="", help="comma list of workload:M to measure")
+    ap.add_argument("--workload", default=None)
     ap.add_argument("--m", type=int, default=None)
     ap.add_argument("--rotate-bytes", type=float, default=float(1 << 30))
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-context", action="store_true",
-                    help="skip the warm-cache and copy-bandwidth context numbers")
-    ap.add_argument("--eager", action="store_true", help="launch steps from Python, no graph")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+                    help="skip the ceilings, warm-cache, copy, other-layout and bf16 context")
+    ap.add_argument("--cpu-seconds", type=float, default=0.5,
+                    help="CPU time per oracle measurement (single-threaded and all cores)")
     ap.add_argument("--pmc-probe", action="store_true",
-                    help="eager steps of the workload, then a copy kernel of known size")
+                    help="eager steps of --workload at --m, then a copy kernel of known size")
     ap.add_argument("--summarize-stats", metavar="DIR")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
-    ap.add_argument("--pmc-kernel", choices=sorted(PMC_KERNELS), default="decode",
-                    help="kernel whose traffic --summarize-pmc reports")
+    ap.add_argument("--summarize-counters", metavar="DIR")
+    ap.add_argument("--pmc-kernel", choices=sorted(PMC_KERNELS), default="decode")
     ap.add_argument("--command", default="", help="command line recorded in a summary")
     ap.add_argument("--layout", choices=["tiled", "rows"], default="tiled",
                     help="weight layout: the 16-row tiled layout, or row-major [N][K/4]")
@@ -105,72 +121,148 @@ def dev_bf16(torch, bits, dev):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
 
 
+def is_prefill(m):
+    return m > 16
+
+
+def step_bytes(wl, m):
+    """Bytes one step's operands occupy: packed weights (+ activations and
+    bf16 outputs for prefill, which rotates them too)."""
+    b = wl.packed_bytes
+    if is_prefill(m):
+        b += sum(2 * m * (p.k + p.n) for p in wl.projections)
+    return b
+
+
+_WEIGHTS = {}   # workload -> latent fp32 weights of every projection (host)
+_PACKED = {}    # (workload, tiled) -> (packed weights, scales) on the GPU
+
+
+def latent_weights(wls, wl):
+    """The workload's seeded latent weights, drawn once per run."""
+    if wl.name not in _WEIGHTS:
+        _WEIGHTS[wl.name] = [wls.weights(wl, pi) for pi in range(len(wl.projections))]
+    return _WEIGHTS[wl.name]
+
+
+def packed_weights(torch, bl, wls, wl, dev, tiled):
+    """Weights packed on the GPU by the library (and put in the 16-row tiled
+    layout), once per workload and layout."""
+    key = (wl.name, tiled)
+    if key not in _PACKED:
+        _PACKED.clear()  # one workload's weights on the GPU at a time
+        packed, scales = [], []
+        for w in latent_weights(wls, wl):
+            p, s = bl.pack_weights(torch.from_numpy(w).to(dev))
+            packed.append(bl.tile_weights(p) if tiled else p)
+            scales.append(s)
+        _PACKED[key] = (packed, scales)
+    return _PACKED[key]
+
+
 def prepare(torch, bl, wls, wl, m, copies, dev, tiled=True):
-    """Packed weights (packed on the GPU by the library, then put in the
-    16-row tiled layout), R rotated copies, activations, and one prepared
-    grouped call per copy."""
-    xs, packed, scales = [], [], []
-    for pi in range(len(wl.projections)):
-        w = torch.from_numpy(wls.weights(wl, pi)).to(dev)
-        p, s = bl.pack_weights(w)
-        del w
-        if tiled:
-            p = bl.tile_weights(p)
-        packed.append(p)
-        scales.append(s)
-        xs.append(dev_bf16(torch, wls.activations(wl, pi, m), dev))
+    """R prepared grouped calls over the workload's packed weights and
+    activations at M; copy c > 0 clones the weights (and for prefill the
+    activations, with outputs of its own)."""
+    packed, scales = packed_weights(torch, bl, wls, wl, dev, tiled)
+    xs = [dev_bf16(torch, wls.activations(wl, pi, m), dev) for pi in range(len(wl.projections))]
     calls = []
     for c in range(copies):
         ps = packed if c == 0 else [p.clone() for p in packed]
-        calls.append(bl.GroupedCall(xs, ps, scales))
+        cx = xs if (c == 0 or not is_prefill(m)) else [x.clone() for x in xs]
+        calls.append(bl.GroupedCall(cx, ps, scales))
     torch.cuda.synchronize()
     return calls
 
 
-def time_steps(torch, calls, steps, warmup, eager):
-    """Run `steps` steps (step i uses copy i % R); returns (host seconds,
-    event seconds, steps actually run)."""
-    stream = torch.cuda.current_stream()
-    r = len(calls)
-    if eager:
-        for i in range(warmup):
-            calls[i % r]()
-        torch.cuda.synchronize()
-        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        t0 = time.perf_counter()
-        ev0.record(stream)
-        for i in range(steps):
-            calls[i % r]()
-        ev1.record(stream)
-        torch.cuda.synchronize()
-        t1 = time.perf_counter()
-        return t1 - t0, ev0.elapsed_time(ev1) / 1e3, steps
+def capture(torch, fn):
     g = torch.cuda.CUDAGraph()
+    stream = torch.cuda.current_stream()
     side = torch.cuda.Stream()
     side.wait_stream(stream)
     with torch.cuda.stream(side):
-        for c in calls:  # warm once outside capture
-            c()
+        fn()  # warm once outside capture
     stream.wait_stream(side)
     torch.cuda.synchronize()
     with torch.cuda.graph(g):
-        for c in calls:
-            c()
-    reps = max(1, steps // r)
-    for _ in range(max(1, warmup // r)):
-        g.replay()
-    torch.cuda.synchronize()
-    # graph replays are launched on the current stream: the events go there too
+        fn()
+    return g
+
+
+def time_config(torch, calls, steps, warmup, min_seconds):
+    """Graphs of exactly `steps` steps over successive ranges of the copy
+    rotation; warmup, then samples replayed back to back, each between two
+    HIP events on the replay stream.  Returns per-step seconds of every
+    sample and the sample count."""
+    r = len(calls)
+    ngraphs = r // math.gcd(r, steps)
+    graphs = []
+    for gi in range(ngraphs):
+        base = gi * steps
+
+        def body(base=base):
+            for j in range(steps):
+                calls[(base + j) % r]()
+
+        graphs.append(capture(torch, body))
     stream = torch.cuda.current_stream()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(reps):
-        g.replay()
-    ev1.record(stream)
+    for i in range(max(1, -(-warmup // steps))):
+        graphs[i % ngraphs].replay()
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    return t1 - t0, ev0.elapsed_time(ev1) / 1e3, reps * r
+    # calibrate the sample count from one pass over the graphs
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(stream)
+    for g in graphs:
+        g.replay()
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    per_sample = max(ev[0].elapsed_time(ev[1]) / 1e3 / ngraphs, 1e-7)
+    samples = int(min(max(5, math.ceil(min_seconds / per_sample)), 20000))
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(samples + 1)]
+    torch.cuda.synchronize()
+    evs[0].record(stream)
+    for i in range(samples):
+        graphs[i % ngraphs].replay()
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    secs = np.array([evs[i].elapsed_time(evs[i + 1]) / 1e3 for i in range(samples)])
+    return secs / steps, samples
+
+
+def spread(per_step):
+    return {"ms_per_step_p10": float(np.percentile(per_step, 10) * 1e3),
+            "ms_per_step_p90": float(np.percentile(per_step, 90) * 1e3),
+            "ms_per_step_min": float(per_step.min() * 1e3)}
+
+
+def measure(torch, bl, wls, name, m, args, dev, min_seconds, tiled=True):
+    wl = wls.WORKLOADS[name]
+    copies = max(1, int(math.ceil(args.rotate_bytes / step_bytes(wl, m))))
+    calls = prepare(torch, bl, wls, wl, m, copies, dev, tiled)
+    per_step, samples = time_config(torch, calls, args.steps, args.warmup, min_seconds)
+    del calls
+    torch.cuda.empty_cache()
+    t = float(np.median(per_step))
+    shapes = [(p.n, p.k) for p in wl.projections]
+    out = {"workload": name, "m": m, "ms_per_step": t * 1e3, **spread(per_step),
+           "samples": samples, "steps_per_sample": args.steps, "rotated_copies": copies,
+           "kernel_launches_per_step": bl.forward_grouped_launches(m, shapes),
+           "weight_layout": "tiled" if tiled else "rows"}
+    if is_prefill(m):
+        tops = wl.ops(m) / t / 1e12
+        out.update(value=tops, unit="TOPS", ops_per_step=wl.ops(m),
+                   roofline={"bound": "mfma", "achieved": tops, "peak": MFMA_I8_PEAK_TOPS,
+                             "unit": "TOP/s", "frac": tops / MFMA_I8_PEAK_TOPS,
+                             "traffic": read_traffic("prefill", name, m),
+                             "note": "from the whole step (activation quantization + "
+                                     "matrix-core GEMM [+ the K-part sum])"})
+    else:
+        gbs = wl.packed_bytes / t / 1e9
+        out.update(value=gbs, unit="GB/s", packed_bytes_per_step=wl.packed_bytes,
+                   roofline={"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS,
+                             "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                             "traffic": read_traffic("decode", name, m)})
+    return out
 
 
 def copy_bandwidth(torch, dev, mib=1024, reps=10):
@@ -230,89 +322,145 @@ def measured_ceilings(torch, dev, reps=10):
     }
 
 
-def cpu_baseline(wls, wl, m, budget_s):
-    """The oracle as it stands, on host cores, over whole passes of the layer
-    (all projections at token count m) until about `budget_s` seconds."""
-    import oracle
+def warm_cache(torch, bl, wls, name, m, args, dev):
+    """The same decode step with one weight copy (resident in the Infinity Cache)."""
+    wl = wls.WORKLOADS[name]
+    calls = prepare(torch, bl, wls, wl, m, 1, dev)
+    per_step, _ = time_config(torch, calls, args.steps, args.warmup, 0.1)
+    del calls
+    return wl.packed_bytes / float(np.median(per_step)) / 1e9
 
+
+def native_bf16(torch, wls, name, m, dev, min_seconds=0.2):
+    """Context: the same layer as dense bf16 weights through torch.matmul
+    (the vendor BLAS), weights rotated like the ternary step; the bytes a
+    bf16 model streams per step and the time it takes."""
+    wl = wls.WORKLOADS[name]
+    wbytes = sum(2 * p.n * p.k for p in wl.projections)
+    copies = max(1, int(math.ceil((1 << 30) / wbytes))) if not is_prefill(m) else 1
+    g = torch.Generator(device="cpu").manual_seed(3)
+    ws = [[(torch.randn(p.k, p.n, generator=g) * 0.02).to(torch.bfloat16).to(dev)
+           for p in wl.projections] for _ in range(1)]
+    for _ in range(copies - 1):
+        ws.append([w.clone() for w in ws[0]])
+    xs = [torch.randn(m, p.k, generator=g).to(torch.bfloat16).to(dev) for p in wl.projections]
+    ys = [torch.empty(m, p.n, dtype=torch.bfloat16, device=dev) for p in wl.projections]
+    calls = [lambda c=c: [torch.matmul(x, w, out=y) for x, w, y in zip(xs, ws[c], ys)]
+             for c in range(copies)]
+    steps = 20
+    launch = "hip-graph"
+    try:
+        per_step, _ = time_config(torch, calls, steps, steps, min_seconds)
+    except Exception:  # the vendor library refused graph capture: eager launches
+        launch = "eager"
+        torch.cuda.synchronize()
+        for i in range(steps):
+            calls[i % copies]()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        ev0.record()
+        for i in range(50 * steps):
+            calls[i % copies]()
+        ev1.record()
+        torch.cuda.synchronize()
+        per_step = np.array([ev0.elapsed_time(ev1) / 1e3 / (50 * steps)])
+    t = float(np.median(per_step))
+    del ws, xs, ys, calls
+    torch.cuda.empty_cache()
+    out = {"workload": name, "m": m, "ms_per_step": t * 1e3, "weight_bytes_per_step": wbytes,
+           "rotated_copies": copies, "launch": launch}
+    if is_prefill(m):
+        out["TFLOPs"] = wl.ops(m) / t / 1e12
+    else:
+        out["GBs_of_bf16_weights"] = wbytes / t / 1e9
+    return out
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle as it stands, on the host cores
+
+
+def _threads_info():
     try:
         from threadpoolctl import threadpool_info
 
-        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
-        blas_threads = 1
-    proj = []
-    for pi in range(len(wl.projections)):
-        w = wls.weights(wl, pi)
-        p, s = oracle.pack_weights(w)
-        proj.append((wls.activations(wl, pi, m), p, s))
-        del w
-    done_bytes, passes = 0, 0
-    t0 = time.perf_counter()
+        return 1
+
+
+def _time_oracle(fn, budget_s):
+    """One untimed call, then fn() at least once and until about budget_s;
+    returns seconds per call."""
+    fn()
+    n, t0 = 0, time.perf_counter()
     while True:
-        for x, p, s in proj:
-            oracle.forward(x, p, s)
-            done_bytes += p.nbytes
-        passes += 1
+        fn()
+        n += 1
         if time.perf_counter() - t0 >= budget_s:
             break
-    dt = time.perf_counter() - t0
+    return (time.perf_counter() - t0) / n, n
+
+
+def cpu_baseline(wls, budget_s):
+    """The oracle (oracle/, NumPy, never tuned) on a bounded sample of every
+    configuration, single-threaded and on all cores, plus its weight packing;
+    the headline configuration's all-core figure is `value`."""
+    import oracle
+    from threadpoolctl import threadpool_limits
+
+    all_threads = _threads_info()
+    rows = []
+    ns_max = 512  # output rows of every projection in the sample
+    packed_sample = {}
+    for name, m in CONFIGS:
+        wl = wls.WORKLOADS[name]
+        # the first 512 output rows of every projection (weights of that
+        # slice packed by the oracle); decode: every token row, prefill: the
+        # first 64
+        ms = m if not is_prefill(m) else 64
+        if name not in packed_sample:
+            packed_sample[name] = [oracle.pack_weights(np.ascontiguousarray(w[:ns_max]))
+                                   for w in latent_weights(wls, wl)]
+        proj = [(wls.activations(wl, pi, m)[:ms], p, s)
+                for pi, (p, s) in enumerate(packed_sample[name])]
+
+        def one_pass():
+            for x, p, s in proj:
+                oracle.forward(x, p, s)
+
+        nbytes = sum(p.nbytes for _, p, _ in proj)
+        ops = sum(2 * ms * p.shape[0] * 4 * p.shape[1] for _, p, _ in proj)
+        res = {"workload": name, "m": m, "sample": (
+            f"the first {ns_max} output rows of each of the {len(proj)} projections, "
+            f"{ms} of {m} token rows ({nbytes} packed bytes, {ops} int8 ops per pass)")}
+        for label, threads in (("single_thread", 1), ("all_cores", all_threads)):
+            with threadpool_limits(limits=threads):
+                sec, n = _time_oracle(one_pass, budget_s)
+            if not is_prefill(m):
+                res[label] = {"value": nbytes / sec / 1e9, "unit": "GB/s",
+                              "threads": threads, "passes": n}
+            else:
+                res[label] = {"value": ops / sec / 1e12, "unit": "TOPS", "threads": threads,
+                              "passes": n}
+        rows.append(res)
+        del proj
+    # weight preparation (absmean, ternarize, pack) on the 2048 x 2048 projection
+    w = latent_weights(wls, wls.WORKLOADS["single_2048_m8"])[0]
+    sec, n = _time_oracle(lambda: oracle.pack_weights(w), budget_s)
+    pack = {"value": w.nbytes / sec / 1e9, "unit": "GB/s of fp32 weights read",
+            "sample": "oracle.pack_weights on the 2048x2048 fp32 projection", "passes": n,
+            "threads": 1}
+    head = next(r for r in rows if (r["workload"], r["m"]) == HEADLINE)
     return {
-        "value": done_bytes / dt / 1e9,
-        "unit": "GB/s",
-        "cores": int(blas_threads),
-        "kind": "oracle",
-        "sample": f"{passes} full pass(es) of the {wl.name} layer at M={m} "
-                  f"({len(proj)} projections, {wl.packed_bytes} packed bytes each pass), "
-                  f"{dt:.1f} s on host cores (numpy; BLAS threads={blas_threads}, "
-                  f"affinity={len(os.sched_getaffinity(0))}, os.cpu_count={os.cpu_count()})",
+        "value": head["all_cores"]["value"], "unit": head["all_cores"]["unit"],
+        "cores": int(all_threads), "kind": "oracle",
+        "sample": f"{head['sample']} of {HEADLINE[0]} (all cores); per configuration below, "
+                  f"single-threaded and on all cores, each ~{budget_s:.1f} s "
+                  f"(numpy; BLAS threads={all_threads}, affinity={len(os.sched_getaffinity(0))}, "
+                  f"os.cpu_count={os.cpu_count()})",
+        "per_config": rows, "pack": pack,
     }
-
-
-def prefill_measure(torch, bl, wls, dev, steps, tiled=True):
-    wl = wls.WORKLOADS["prefill_2b_m2048"]
-    m = wl.ms[0]
-    # one weight copy (6.5 MB of packed weights stay cached, as in a model
-    # whose prefill is compute bound); 8 steps per captured graph so the
-    # replay launches do not show between steps
-    calls = prepare(torch, bl, wls, wl, m, 1, dev, tiled) * 8
-    host_s, ev_s, n = time_steps(torch, calls, max(64, steps // 8), 16, eager=False)
-    tops = wl.ops(m) * n / ev_s / 1e12
-    return {
-        "workload": wl.name, "m": m, "value": tops, "unit": "TOPS",
-        "note": "end to end: activation quantization pass + MFMA GEMM, 3 projections",
-        "weight_layout": "tiled" if tiled else "rows",
-        "library_int8_gemm_TOPS": library_int8_gemm(torch, wl, m, dev),
-        "library_int8_gemm_note": "context: torch._int_mm (dense int8 x int8 -> int32, "
-                                  "vendor GEMM library) on the same three shapes",
-        "ms_per_step": ev_s / n * 1e3, "ops_per_step": wl.ops(m), "steps": n,
-        "roofline": {"bound": "mfma", "achieved": tops, "peak": MFMA_I8_PEAK_TOPS,
-                     "unit": "TFLOP/s", "frac": tops / MFMA_I8_PEAK_TOPS,
-                     "traffic": read_traffic("prefill")},
-    }
-
-
-def library_int8_gemm(torch, wl, m, dev, reps=20):
-    """Dense int8 GEMM of the vendor library on the same shapes (context only)."""
-    try:
-        mats = []
-        for p in wl.projections:
-            a = torch.randint(-127, 128, (m, p.k), dtype=torch.int8, device=dev)
-            b = torch.randint(-1, 2, (p.k, p.n), dtype=torch.int8, device=dev)
-            mats.append((a, b))
-        for a, b in mats:
-            torch._int_mm(a, b)
-        torch.cuda.synchronize()
-        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        ev0.record()
-        for _ in range(reps):
-            for a, b in mats:
-                torch._int_mm(a, b)
-        ev1.record()
-        torch.cuda.synchronize()
-        return wl.ops(m) * reps / (ev0.elapsed_time(ev1) / 1e3) / 1e12
-    except Exception as e:  # pragma: no cover - depends on the installed torch
-        return f"unavailable: {type(e).__name__}"
 
 
 # ---------------------------------------------------------------------------
@@ -342,7 +490,7 @@ def summarize_stats(d, command):
 
 
 def _per_kernel_counter(d, counter):
-    """Mean counter value per dispatch, by kernel name."""
+    """Counter value per dispatch, by kernel name."""
     rows = _csv_rows(os.path.join(d, "**", "*counter_collection.csv"))
     acc = {}
     for r in rows:
@@ -356,26 +504,30 @@ def _per_kernel_counter(d, counter):
     return by_name
 
 
-def summarize_pmc(fdir, wdir, command, kind):
+def summarize_pmc(fdir, wdir, command, kind, workload, m):
     fetch = _per_kernel_counter(fdir, "FETCH_SIZE")
     write = _per_kernel_counter(wdir, "WRITE_SIZE")
     copy_name = next((n for n in fetch if "neg" in n.lower()), None)
-    dec_name = next((n for n in fetch if PMC_KERNELS[kind]["name"] in n), None)
-    if copy_name is None or dec_name is None:
+    names = [n for n in fetch if PMC_KERNELS[kind]["name"] in n]
+    if copy_name is None or not names:
         sys.exit(f"kernels not found: {list(fetch)[:8]}")
     copy_bytes = COPY_PROBE_MIB * (1 << 20)
     cf = float(np.median(fetch[copy_name]))
     cw = float(np.median(write[copy_name]))
     f_fac, w_fac = copy_bytes / (cf * 1024), copy_bytes / (cw * 1024)
-    df = float(np.mean(fetch[dec_name]))
-    dw = float(np.mean(write[dec_name]))
+    fl = [v for n in names for v in fetch[n]]
+    wr = [v for n in names for v in write.get(n, [])]
+    df, dw = float(np.mean(fl)), float(np.mean(wr))
     traffic = df * 1024 * f_fac + dw * 1024 * w_fac
     lines = [
-        f"# HBM traffic of the {kind} kernel (rocprofv3 PMC, one counter per run)",
+        f"# HBM traffic of the {kind} kernel on {workload} at M={m} "
+        "(rocprofv3 PMC, one counter per run)",
         f"command: {command}",
         f"sources_sha256: {sources_sha256(kind)}",
-        f"kernel: {dec_name[:140]}",
-        f"dispatches: {len(fetch[dec_name])} (FETCH_SIZE run), {len(write.get(dec_name, []))} (WRITE_SIZE run)",
+        f"workload: {workload}",
+        f"m: {m}",
+        "kernel: " + "; ".join(n[:120] for n in names),
+        f"dispatches: {len(fl)} (FETCH_SIZE run), {len(wr)} (WRITE_SIZE run)",
         f"FETCH_SIZE_KiB_per_dispatch: {df:.1f}",
         f"WRITE_SIZE_KiB_per_dispatch: {dw:.1f}",
         f"copy_kernel: {copy_name[:140]}",
@@ -386,15 +538,33 @@ def summarize_pmc(fdir, wdir, command, kind):
         f"fetch_scale: {f_fac:.4f}",
         f"write_scale: {w_fac:.4f}",
         f"traffic_bytes_per_dispatch: {traffic:.0f}",
+        f"fetched_bytes_per_dispatch: {df * 1024 * f_fac:.0f}",
+        f"written_bytes_per_dispatch: {dw * 1024 * w_fac:.0f}",
     ]
     print("\n".join(lines))
 
 
-def read_traffic(kind):
-    """Traffic figure of the committed PMC summary of a kernel, or None if it
-    is missing or was measured on other sources of that kernel."""
+def summarize_counters(d, command, kind, workload, m):
+    """Mean per dispatch of every counter in a --pmc run, for the kernel."""
+    rows = _csv_rows(os.path.join(d, "**", "*counter_collection.csv"))
+    names = sorted({r["Counter_Name"] for r in rows})
+    lines = [f"# rocprofv3 counters of the {kind} kernel on {workload} at M={m}",
+             f"command: {command}", f"sources_sha256: {sources_sha256(kind)}",
+             f"workload: {workload}", f"m: {m}"]
+    for c in names:
+        per = _per_kernel_counter(d, c)
+        for kn, vals in per.items():
+            if PMC_KERNELS[kind]["name"] in kn:
+                lines.append(f"{c}: {float(np.mean(vals)):.6g}  (dispatches {len(vals)}; {kn[:90]})")
+    print("\n".join(lines))
+
+
+def read_traffic(kind, workload, m):
+    """Traffic figure of the committed PMC summary of a kernel on a
+    configuration, or None if it is missing or was measured on other sources
+    of that kernel."""
     try:
-        with open(PMC_KERNELS[kind]["file"]) as f:
+        with open(traffic_file(kind, workload, m)) as f:
             kv = dict(l.split(": ", 1) for l in f.read().splitlines() if ": " in l)
     except OSError:
         return None
@@ -408,29 +578,25 @@ def read_traffic(kind):
 
 def pmc_probe(torch, bl, wls, args):
     dev = torch.device("cuda:0")
-    wl = wls.WORKLOADS[args.workload]
+    wl = wls.WORKLOADS[args.workload or HEADLINE[0]]
     m = args.m if args.m is not None else wl.ms[0]
-    copies = max(1, int(np.ceil(args.rotate_bytes / wl.packed_bytes)))
-    tiled = args.layout == "tiled"
-    calls = prepare(torch, bl, wls, wl, m, copies, dev, tiled)
-    time_steps(torch, calls, args.steps, 0, eager=True)
+    copies = max(1, int(math.ceil(args.rotate_bytes / step_bytes(wl, m))))
+    calls = prepare(torch, bl, wls, wl, m, copies, dev, args.layout == "tiled")
+    for i in range(args.steps):
+        calls[i % len(calls)]()
+    torch.cuda.synchronize()
     del calls
-    # the prefill workload, a few eager steps (one weight copy, as timed)
-    pwl = wls.WORKLOADS["prefill_2b_m2048"]
-    pcalls = prepare(torch, bl, wls, pwl, pwl.ms[0], 1, dev, tiled)
-    time_steps(torch, pcalls, 8, 0, eager=True)
-    del pcalls
     n = COPY_PROBE_MIB * (1 << 20) // 4
     a = torch.ones(n, dtype=torch.float32, device=dev)
     b = torch.empty_like(a)
     for _ in range(3):
         torch.neg(a, out=b)
     torch.cuda.synchronize()
-    print(f"pmc probe: {args.steps} eager steps of {wl.name}, 8 of prefill_2b_m2048, "
+    print(f"pmc probe: {args.steps} eager steps of {wl.name} at M={m}, "
           f"3 copies of {COPY_PROBE_MIB} MiB", flush=True)
 
 
-def bandwidth_curve(torch, bl, dev, layout, k=4096, sizes_mib=(1, 4, 16, 64, 256, 1024)):
+def bandwidth_curve(torch, bl, dev, layout, args, k=4096, sizes_mib=(1, 4, 16, 64, 256, 1024)):
     """Decode (M=1) on a single N x K projection of random packed bytes (code 3
     included: timing only), cold: rotated over copies spanning >= 1 GiB."""
     rows = []
@@ -444,9 +610,8 @@ def bandwidth_curve(torch, bl, dev, layout, k=4096, sizes_mib=(1, 4, 16, 64, 256
         if layout == "tiled":
             base = bl.tile_weights(base)
         calls = [bl.GroupedCall([x], [base if c == 0 else base.clone()], [ws]) for c in range(copies)]
-        steps = max(64, min(4096, 256 * copies // max(1, mib // 16)))
-        _, ev_s, nrun = time_steps(torch, calls, steps, min(64, steps), False)
-        us = ev_s / nrun * 1e6
+        per_step, _ = time_config(torch, calls, max(2, min(args.steps, 64)), 4, 0.2)
+        us = float(np.median(per_step)) * 1e6
         rows.append({"MiB": mib, "n": n, "k": k, "layout": layout, "us": us,
                      "GBs": (mib << 20) / (us * 1e-6) / 1e9})
         del calls, base
@@ -459,11 +624,17 @@ def main():
     if args.summarize_stats:
         return summarize_stats(args.summarize_stats, args.command)
     if args.summarize_pmc:
-        return summarize_pmc(*args.summarize_pmc, args.command, args.pmc_kernel)
+        return summarize_pmc(*args.summarize_pmc, args.command, args.pmc_kernel,
+                             args.workload, args.m)
+    if args.summarize_counters:
+        return summarize_counters(args.summarize_counters, args.command, args.pmc_kernel,
+                                  args.workload, args.m)
     if args.gpus != 1:
-        print("bench.py runs on one GPU only: the library has no multi-GPU path; "
-              "run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU: the library has no multi-GPU path (how it would "
+              "shard is described in the design notes); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
+    if args.steps < 1 or args.warmup < 0:
+        sys.exit("--steps must be >= 1 and --warmup >= 0")
     import torch
 
     from bit_gemm_bitlinear_amd import bitlinear as bl
@@ -471,78 +642,86 @@ def main():
 
     if args.pmc_probe:
         return pmc_probe(torch, bl, wls, args)
+    dev = torch.device("cuda:0")
     if args.curve:
-        for r in bandwidth_curve(torch, bl, torch.device("cuda:0"), args.layout):
+        for r in bandwidth_curve(torch, bl, dev, args.layout, args):
             print(json.dumps(r), flush=True)
         return
 
-    dev = torch.device("cuda:0")
-    wl = wls.WORKLOADS[args.workload]
-    m = args.m if args.m is not None else wl.ms[0]
-    copies = max(1, int(np.ceil(args.rotate_bytes / wl.packed_bytes)))
+    configs = CONFIGS
+    if args.only:
+        configs = [(s.split(":")[0], int(s.split(":")[1])) for s in args.only.split(",")]
+    head = HEADLINE if HEADLINE in configs else configs[0]
     tiled = args.layout == "tiled"
-    calls = prepare(torch, bl, wls, wl, m, copies, dev, tiled)
-    host_s, ev_s, n = time_steps(torch, calls, args.steps, args.warmup, args.eager)
-    per_step = ev_s / n
-    gbs = wl.packed_bytes / per_step / 1e9
-    traffic = (read_traffic("decode") if (args.workload == "decode_1b_m1" and m == 1 and tiled)
-               else None)
-
+    rows = []
+    for name, m in configs:
+        secs = args.headline_seconds if (name, m) == head else args.min_seconds
+        r = measure(torch, bl, wls, name, m, args, dev, secs, tiled)
+        print(f"# {name} M={m}: {r['ms_per_step'] * 1e3:.2f} us/step, {r['value']:.1f} "
+              f"{r['unit']} ({r['roofline']['frac'] * 100:.1f}% of the roofline), "
+              f"{r['samples']} samples", file=sys.stderr, flush=True)
+        rows.append(r)
+    h = next(r for r in rows if (r["workload"], r["m"]) == head)
+    wl = wls.WORKLOADS[head[0]]
     out = {
         "metric": METRIC,
-        "value": gbs,
-        "unit": "GB/s",
+        "value": h["value"],
+        "unit": h["unit"],
         "n_gpus": 1,
-        "steps": n,
+        "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": per_step * 1e3,
+        "ms_per_step": h["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "int8",
         "data": "synthetic",
         "config": {
-            "workload": wl.name, "m": m,
+            "workload": head[0], "m": head[1],
             "projections": [[p.name, p.n, p.k] for p in wl.projections],
             "packed_bytes_per_step": wl.packed_bytes,
             "weight_layout": args.layout,
-            "kernel_launches_per_step": 1,
-            "rotated_weight_copies": copies,
-            "launch": "eager" if args.eager else "hip-graph",
-            "host_ms_per_step": host_s / n * 1e3,
+            "kernel_launches_per_step": h["kernel_launches_per_step"],
+            "rotated_weight_copies": h["rotated_copies"],
+            "launch": "hip-graph",
+            "samples": h["samples"], "steps_per_sample": args.steps,
+            "timed_steps": h["samples"] * args.steps,
+            "ms_per_step_p10": h["ms_per_step_p10"], "ms_per_step_p90": h["ms_per_step_p90"],
+            "ms_per_step_min": h["ms_per_step_min"],
         },
-        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": gbs / HBM_PEAK_GBS, "traffic": traffic},
+        "roofline": {k: v for k, v in h["roofline"].items() if k != "note"},
+        "configs": rows,
     }
     if not args.no_context:
-        # the same step with one weight copy: resident in the Infinity Cache
-        w_calls = calls[:1] * len(calls)  # as many launches per graph, all on copy 0
-        _, w_s, w_n = time_steps(torch, w_calls, args.steps, args.warmup, args.eager)
-        del calls
-        out["context"] = {
-            "warm_mall_GBs": wl.packed_bytes / (w_s / w_n) / 1e9,
-            "warm_mall_note": "same step, one weight copy (16 MiB stays in the 256 MB Infinity Cache)",
-            "copy_GBs": copy_bandwidth(torch, dev),
-            "copy_note": "plain device copy of 1 GiB (read + write bytes / time), torch elementwise kernel",
-        }
-        # the same step on the other weight layout
-        o_calls = prepare(torch, bl, wls, wl, m, copies, dev, not tiled)
-        _, o_s, o_n = time_steps(torch, o_calls, args.steps, args.warmup, args.eager)
-        del o_calls
-        out["context"]["other_layout"] = "rows" if tiled else "tiled"
-        out["context"]["other_layout_GBs"] = wl.packed_bytes / (o_s / o_n) / 1e9
-    else:
-        del calls
-    if not args.no_prefill:
-        out["prefill"] = prefill_measure(torch, bl, wls, dev, args.steps, tiled)
-    if not args.no_context:
+        ctx = {}
+        ctx["warm_mall_GBs"] = warm_cache(torch, bl, wls, head[0], head[1], args, dev) \
+            if not is_prefill(head[1]) else None
+        ctx["warm_mall_note"] = "the headline step with one weight copy (resident in the 256 MB Infinity Cache)"
+        ctx["copy_GBs"] = copy_bandwidth(torch, dev)
+        ctx["copy_note"] = "plain device copy of 1 GiB (read + write bytes / time), torch elementwise kernel"
+        other = measure(torch, bl, wls, head[0], head[1], args, dev, 0.2, not tiled)
+        ctx["other_layout"] = other["weight_layout"]
+        ctx["other_layout_GBs"] = other["value"]
+        ctx["native_bf16"] = []
+        for n, m in (("layer_8b", 1), ("decode_1b_m1", 1), ("prefill_2b_m2048", 2048),
+                     ("layer_8b", 512)):
+            try:
+                ctx["native_bf16"].append(native_bf16(torch, wls, n, m, dev))
+            except Exception as e:  # context only: never fail the run for it
+                ctx["native_bf16"].append({"workload": n, "m": m,
+                                           "unavailable": f"{type(e).__name__}: {e}"[:200]})
+        ctx["native_bf16_note"] = ("the same layers as dense bf16 weights through torch.matmul "
+                                   "(vendor BLAS), random weights, rotated like the ternary "
+                                   "steps; compare ms_per_step with the configs array")
         peaks = measured_ceilings(torch, dev)
-        peaks["decode_frac_of_stream_read"] = gbs / peaks["stream_read_GBs"]
-        if "prefill" in out:
-            peaks["prefill_frac_of_mfma_loop"] = out["prefill"]["value"] / peaks["mfma_i8_loop_TOPS"]
+        peaks["headline_frac_of_stream_read"] = h["value"] / peaks["stream_read_GBs"]
+        for r in rows:
+            r["frac_of_measured_ceiling"] = r["value"] / (
+                peaks["mfma_i8_loop_TOPS"] if r["unit"] == "TOPS" else peaks["stream_read_GBs"])
         out["measured_peaks"] = peaks
+        out["context"] = ctx
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wls, wl, m, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(wls, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
 

@@ -33,6 +33,12 @@ class Projection(ctypes.Structure):
                 ("n", _i64), ("k", _i64), ("layout", _i32), ("reserved", _i32)]
 
 
+class Inspect(ctypes.Structure):
+    """bl_inspect: side outputs of a forward call (codes, scales, code sums,
+    int32 accumulators)."""
+    _fields_ = [("q", _vp), ("x_scale", _vp), ("qsum", _vp), ("acc", _vp)]
+
+
 LAYOUT_ROWS = 0   # BL_LAYOUT_ROWS: packed uint8 [N, K/4]
 LAYOUT_TILED = 1  # BL_LAYOUT_TILED: uint8 [N/16, 4*K], one row per block of 16 weight rows
 
@@ -51,8 +57,12 @@ _SIGS = {
     "bitlinear_forward_tiled": (ctypes.c_int, [_i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _sz,
                                                _vp]),
     "bitlinear_forward_grouped_workspace_bytes": (_sz, [_i32, ctypes.POINTER(Projection), _i64]),
+    "bitlinear_forward_grouped_launches": (_i32, [_i32, ctypes.POINTER(Projection), _i64]),
     "bitlinear_forward_grouped": (ctypes.c_int, [_i32, ctypes.POINTER(Projection), _i64, _vp,
                                                  _sz, _vp]),
+    "bitlinear_forward_grouped_inspect": (ctypes.c_int, [_i32, ctypes.POINTER(Projection), _i64,
+                                                         ctypes.POINTER(Inspect), _vp, _i32, _vp,
+                                                         _sz, _vp]),
     "bitlinear_forward_grouped_noalloc": (ctypes.c_int, [_i32, ctypes.POINTER(Projection), _i64,
                                                          _vp]),
     "bitlinear_forward_acc": (ctypes.c_int, [_i64, _i64, _i64, _vp, _vp, _vp, _vp, _sz, _vp]),
@@ -92,20 +102,48 @@ def _ptr(t: torch.Tensor):
     return ctypes.c_void_p(t.data_ptr())
 
 
-def _require(t: torch.Tensor, dtype, ndim, name):
+def _require(t: torch.Tensor, dtype, ndim, name, shape=None, device=None):
+    """Checks a tensor handed to the library: a contiguous device tensor of
+    the given dtype and rank (and shape and device, when given).  The kernels
+    trust these; a host tensor or a short buffer would be read or written out
+    of bounds on the GPU."""
     if not isinstance(t, torch.Tensor) or not t.is_cuda:
         raise TypeError(f"{name} must be a CUDA (HIP) tensor")
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if t.dim() != ndim:
         raise ValueError(f"{name} must have {ndim} dimensions")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
 
 
+def _require_scale(s: torch.Tensor, device, name="w_scale"):
+    """A weight scale: fp32 device tensor with at least one element."""
+    if not isinstance(s, torch.Tensor) or not s.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if s.dtype != torch.float32 or s.numel() < 1:
+        raise TypeError(f"{name} must be float32 with at least one element")
+    if s.device != device:
+        raise ValueError(f"{name} is on {s.device}, expected {device}")
+
+
+def _nbytes(t: torch.Tensor) -> int:
+    return t.numel() * t.element_size()
+
+
 def _workspace(nbytes: int, device, workspace):
     if workspace is not None:
-        if workspace.numel() * workspace.element_size() < nbytes:
+        if not isinstance(workspace, torch.Tensor) or not workspace.is_cuda:
+            raise TypeError("workspace must be a CUDA (HIP) tensor")
+        if workspace.device != device:
+            raise ValueError(f"workspace is on {workspace.device}, expected {device}")
+        if not workspace.is_contiguous():
+            raise ValueError("workspace must be contiguous")
+        if _nbytes(workspace) < nbytes:
             raise ValueError("workspace too small")
         return workspace
     return torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
@@ -121,7 +159,7 @@ def pack_weights(w: torch.Tensor):
     w_scale = torch.empty(4, dtype=torch.float32, device=w.device)[:1]
     ws = _workspace(_lib.bitlinear_pack_workspace_bytes(n, k), w.device, None)
     _check(_lib.bitlinear_pack_weights(_ptr(w), n, k, _ptr(packed), _ptr(w_scale), _ptr(ws),
-                                       ws.numel(), _stream(w)))
+                                       _nbytes(ws), _stream(w)))
     return packed, w_scale
 
 
@@ -187,15 +225,17 @@ def forward(x: torch.Tensor, packed: torch.Tensor, w_scale: torch.Tensor,
             out: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
     """y = BitLinear(x) as bf16 [M, N]; `packed` in either layout."""
     _require(x, torch.bfloat16, 2, "x")
-    _require(packed, torch.uint8, 2, "packed")
+    _require(packed, torch.uint8, 2, "packed", device=x.device)
+    _require_scale(w_scale, x.device)
     m, k = x.shape
     n, layout = weight_layout(packed, k)
     if out is None:
         out = torch.empty((m, n), dtype=torch.bfloat16, device=x.device)
+    _require(out, torch.bfloat16, 2, "out", shape=(m, n), device=x.device)
     ws = _workspace(forward_workspace_bytes(m, n, k), x.device, workspace)
     fn = _lib.bitlinear_forward_tiled if layout == LAYOUT_TILED else _lib.bitlinear_forward
     _check(fn(m, n, k, _ptr(x), _ptr(packed), _ptr(w_scale), _ptr(out),
-              _ptr(ws), ws.numel() * ws.element_size(), _stream(x)))
+              _ptr(ws), _nbytes(ws), _stream(x)))
     return out
 
 
@@ -215,21 +255,38 @@ def forward_grouped_workspace_bytes(m: int, shapes: Sequence[tuple]) -> int:
     return int(_lib.bitlinear_forward_grouped_workspace_bytes(len(shapes), arr, m))
 
 
+def forward_grouped_launches(m: int, shapes: Sequence[tuple]) -> int:
+    """Kernels a grouped forward over projections of these (N, K) enqueues."""
+    arr = (Projection * len(shapes))()
+    for i, (n, k) in enumerate(shapes):
+        arr[i] = Projection(0, 0, 0, 0, n, k)
+    return int(_lib.bitlinear_forward_grouped_launches(len(shapes), arr, m))
+
+
 class GroupedCall:
     """A prepared grouped forward: descriptors and workspace built once, so
     repeated calls only enqueue the two kernels."""
 
     def __init__(self, xs, packeds, w_scales, outs=None, workspace=None):
+        if not (len(xs) == len(packeds) == len(w_scales)) or not xs:
+            raise ValueError("xs, packeds and w_scales must be non-empty lists of one length")
         m = xs[0].shape[0]
-        for x, p in zip(xs, packeds):
-            _require(x, torch.bfloat16, 2, "x")
-            _require(p, torch.uint8, 2, "packed")
+        dev = xs[0].device
+        for x, p, s in zip(xs, packeds, w_scales):
+            _require(x, torch.bfloat16, 2, "x", device=dev)
+            _require(p, torch.uint8, 2, "packed", device=dev)
+            _require_scale(s, dev)
             if x.shape[0] != m:
                 raise ValueError("inconsistent token counts in grouped call")
             weight_layout(p, x.shape[1])
         if outs is None:
             outs = [torch.empty((m, weight_layout(p, x.shape[1])[0]), dtype=torch.bfloat16,
                                 device=x.device) for x, p in zip(xs, packeds)]
+        if len(outs) != len(xs):
+            raise ValueError("one output per projection")
+        for x, p, y in zip(xs, packeds, outs):
+            _require(y, torch.bfloat16, 2, "out", shape=(m, weight_layout(p, x.shape[1])[0]),
+                     device=dev)
         self.m = m
         self.outs = outs
         self._keep = (list(xs), list(packeds), list(w_scales), outs)
@@ -242,7 +299,7 @@ class GroupedCall:
         s = ctypes.c_void_p(stream) if stream is not None else _stream(self._dev)
         _check(_lib.bitlinear_forward_grouped(len(self._arr), self._arr, self.m,
                                               _ptr(self.workspace),
-                                              self.workspace.numel(), s))
+                                              _nbytes(self.workspace), s))
         return self.outs
 
 
@@ -251,20 +308,45 @@ def forward_grouped(xs, packeds, w_scales, outs=None, workspace=None):
     return GroupedCall(xs, packeds, w_scales, outs, workspace)()
 
 
+def forward_grouped_inspect(xs, packeds, w_scales, wait_polls: int = 0):
+    """bitlinear_forward_grouped_inspect: the grouped forward, plus what its
+    kernels computed on the way.  Returns (ys, inspections, status) where
+    inspections[i] is a dict of the int8 codes [M, K], fp32 scales [M], int32
+    code sums [M] and int32 accumulators [M, N] of projection i, and status
+    is the device int32 status word (1: a decode wait gave up)."""
+    call = GroupedCall(xs, packeds, w_scales)
+    m, dev = call.m, call._dev.device
+    ins = (Inspect * len(xs))()
+    keep = []
+    for i, (x, y) in enumerate(zip(xs, call.outs)):
+        d = {"q": torch.empty((m, x.shape[1]), dtype=torch.int8, device=dev),
+             "x_scale": torch.empty(max(m, 4), dtype=torch.float32, device=dev)[:m],
+             "qsum": torch.empty(max(m, 4), dtype=torch.int32, device=dev)[:m],
+             "acc": torch.empty((m, y.shape[1]), dtype=torch.int32, device=dev)}
+        ins[i] = Inspect(d["q"].data_ptr(), d["x_scale"].data_ptr(), d["qsum"].data_ptr(),
+                         d["acc"].data_ptr())
+        keep.append(d)
+    status = torch.zeros(4, dtype=torch.int32, device=dev)
+    _check(_lib.bitlinear_forward_grouped_inspect(
+        len(xs), call._arr, m, ins, _ptr(status), int(wait_polls), _ptr(call.workspace),
+        _nbytes(call.workspace), _stream(call._dev)))
+    return call.outs, keep, status[:1]
+
+
 def forward_acc(q: torch.Tensor, packed: torch.Tensor, out: torch.Tensor | None = None,
                 workspace: torch.Tensor | None = None):
     """Exact int32 accumulators q . u^T for caller-supplied int8 codes;
     `packed` in either layout."""
     _require(q, torch.int8, 2, "q")
-    _require(packed, torch.uint8, 2, "packed")
+    _require(packed, torch.uint8, 2, "packed", device=q.device)
     m, k = q.shape
     n, layout = weight_layout(packed, k)
     if out is None:
         out = torch.empty((m, n), dtype=torch.int32, device=q.device)
+    _require(out, torch.int32, 2, "out", shape=(m, n), device=q.device)
     ws = _workspace(forward_workspace_bytes(m, n, k), q.device, workspace)
     fn = _lib.bitlinear_forward_acc_tiled if layout == LAYOUT_TILED else _lib.bitlinear_forward_acc
-    _check(fn(m, n, k, _ptr(q), _ptr(packed), _ptr(out), _ptr(ws),
-              ws.numel() * ws.element_size(), _stream(q)))
+    _check(fn(m, n, k, _ptr(q), _ptr(packed), _ptr(out), _ptr(ws), _nbytes(ws), _stream(q)))
     return out
 
 

@@ -146,13 +146,23 @@ struct ProjIO {
   const uint8_t* packed;
   const float* w_scale;
   uint16_t* y;
-  int32_t* acc;
+  int32_t* acc;   // int32 accumulators: the output of forward_acc, or inspection
   int64_t n, k;
   int32_t tiled;  // 1: packed is in the 16-row tiled layout
+  // inspection of the activation quantization (bf16 input), or nullptr
+  int8_t* ins_q;
+  float* ins_xs;
+  int32_t* ins_qs;
+};
+
+// Diagnostics of a call: the decode kernel's wait bound and status word.
+struct CallDiag {
+  int32_t* status = nullptr;
+  int32_t wait_polls = kDefaultWaitPolls;
 };
 
 bl_status run_forward(int32_t count, const ProjIO* io, int64_t m, void* workspace,
-                      size_t ws_bytes, hipStream_t stream) {
+                      size_t ws_bytes, hipStream_t stream, const CallDiag& diag = CallDiag()) {
   int64_t ns[kMaxProj], ks[kMaxProj];
   for (int i = 0; i < count; ++i) {
     ns[i] = io[i].n;
@@ -195,6 +205,9 @@ bl_status run_forward(int32_t count, const ProjIO* io, int64_t m, void* workspac
     J.m_pad = L.m_pad;
     J.row_begin = rows;
     J.paired = L.decode ? 1 : 0;
+    J.ins_q = io[i].ins_q;
+    J.ins_xs = io[i].ins_xs;
+    J.ins_qs = io[i].ins_qs;
     rows += L.m_pad;
   }
   qa.count = jobs;
@@ -209,6 +222,8 @@ bl_status run_forward(int32_t count, const ProjIO* io, int64_t m, void* workspac
     da.count = count;
     da.m = (int32_t)m;
     da.load_mode = load_mode;
+    da.status = diag.status;
+    da.wait_polls = diag.wait_polls;
     int wgs = 0, lds_row = 0;
     for (int i = 0; i < count; ++i) {
       DecodeProj& P = da.p[i];
@@ -218,9 +233,10 @@ bl_status run_forward(int32_t count, const ProjIO* io, int64_t m, void* workspac
       P.y = io[i].y;
       P.acc_out = io[i].acc;
       P.x = pl.fused ? io[i].x : nullptr;
-      P.q = qptr[i];
-      P.x_scale = xsptr[i];
-      P.qsum = qsptr[i];
+      // fused: the kernel quantizes, and these are its inspection outputs
+      P.q = pl.fused ? io[i].ins_q : qptr[i];
+      P.x_scale = pl.fused ? io[i].ins_xs : xsptr[i];
+      P.qsum = pl.fused ? io[i].ins_qs : qsptr[i];
       P.part = pl.ksplit > 1 ? reinterpret_cast<int32_t*>(ws + L.part_off[i]) : nullptr;
       P.count = pl.ksplit > 1 ? reinterpret_cast<uint32_t*>(ws + L.cnt_off[i]) : nullptr;
       P.n = (int32_t)ns[i];
@@ -333,7 +349,6 @@ bl_status run_forward(int32_t count, const ProjIO* io, int64_t m, void* workspac
 constexpr size_t kScratchBytes = (size_t)BL_NOALLOC_SCRATCH_BYTES;
 static __device__ __align__(256) uint8_t scratch[kScratchBytes];
 
-constexpr int kMaxDevices = 64;
 std::mutex g_scratch_mu;
 void* g_scratch_ptr[kMaxDevices] = {};
 
@@ -369,7 +384,7 @@ const char* bitlinear_status_string(bl_status s) {
   return "unknown status";
 }
 
-int bitlinear_abi_version(void) { return 2; }
+int bitlinear_abi_version(void) { return 3; }
 
 size_t bitlinear_pack_workspace_bytes(int64_t n, int64_t k) {
   (void)n;
@@ -455,7 +470,7 @@ static bl_status forward_one(int64_t m, int64_t n, int64_t k, const uint16_t* x,
   if ((st = check_ptr(x)) != BL_OK || (st = check_ptr(packed)) != BL_OK ||
       (st = check_ptr(w_scale)) != BL_OK || (st = check_ptr(y)) != BL_OK)
     return st;
-  ProjIO io = {x, nullptr, packed, w_scale, y, nullptr, n, k, tiled};
+  ProjIO io = {x, nullptr, packed, w_scale, y, nullptr, n, k, tiled, nullptr, nullptr, nullptr};
   return run_forward(1, &io, m, workspace, workspace_bytes, static_cast<hipStream_t>(stream));
 }
 
@@ -497,10 +512,34 @@ static bl_status grouped_io(int32_t count, const bl_projection* projs, int64_t m
     if ((st = check_ptr(p.x)) != BL_OK || (st = check_ptr(p.packed)) != BL_OK ||
         (st = check_ptr(p.w_scale)) != BL_OK || (st = check_ptr(p.y)) != BL_OK)
       return st;
-    io[i] = ProjIO{p.x,      nullptr, p.packed, p.w_scale, p.y,
-                   nullptr, p.n,     p.k,      p.layout == BL_LAYOUT_TILED ? 1 : 0};
+    io[i] = ProjIO{p.x,     nullptr, p.packed, p.w_scale, p.y,    nullptr,
+                   p.n,     p.k,     p.layout == BL_LAYOUT_TILED ? 1 : 0,   nullptr, nullptr,
+                   nullptr};
   }
   return BL_OK;
+}
+
+int32_t bitlinear_forward_grouped_launches(int32_t count, const bl_projection* projs, int64_t m) {
+  if (count < 1 || count > kMaxProj || !projs) return -1;
+  int64_t ns[kMaxProj], ks[kMaxProj];
+  for (int i = 0; i < count; ++i) {
+    if (check_shape(m, projs[i].n, projs[i].k) != BL_OK) return -1;
+    ns[i] = projs[i].n;
+    ks[i] = projs[i].k;
+  }
+  Layout L;
+  make_layout(count, ns, ks, m, true, L);  // bf16 activations, as the grouped call takes
+  int jobs = 0;
+  for (int i = 0; i < count; ++i) jobs += (L.decode && L.plan[i].fused) ? 0 : 1;
+  int32_t launches = (jobs > 0 || L.zero_bytes > 0) ? 1 : 0;  // activation quantization
+  launches += 1;                                              // the contraction
+  if (!L.decode)
+    for (int i = 0; i < count; ++i)
+      if (L.pf_ksplit[i] > 1) {  // the pass that adds the K parts
+        launches += 1;
+        break;
+      }
+  return launches;
 }
 
 bl_status bitlinear_forward_grouped(int32_t count, const bl_projection* projs, int64_t m,
@@ -529,6 +568,33 @@ bl_status bitlinear_forward_grouped_noalloc(int32_t count, const bl_projection* 
   return run_forward(count, io, m, ws, kScratchBytes, static_cast<hipStream_t>(stream));
 }
 
+bl_status bitlinear_forward_grouped_inspect(int32_t count, const bl_projection* projs, int64_t m,
+                                            const bl_inspect* inspect, int32_t* status,
+                                            int32_t wait_polls, void* workspace,
+                                            size_t workspace_bytes, void* stream) {
+  ProjIO io[kMaxProj];
+  bl_status st = grouped_io(count, projs, m, io);
+  if (st != BL_OK) return st;
+  if (!inspect) return BL_EINVAL;
+  if (status && (st = check_ptr(status)) != BL_OK) return st;
+  for (int i = 0; i < count; ++i) {
+    const bl_inspect& d = inspect[i];
+    // optional outputs: 16-byte aligned when given
+    for (const void* p : {(const void*)d.q, (const void*)d.x_scale, (const void*)d.qsum,
+                          (const void*)d.acc})
+      if (p && !aligned16(p)) return BL_EALIGN;
+    io[i].ins_q = d.q;
+    io[i].ins_xs = d.x_scale;
+    io[i].ins_qs = d.qsum;
+    io[i].acc = d.acc;
+  }
+  CallDiag diag;
+  diag.status = status;
+  diag.wait_polls = wait_polls > 0 ? wait_polls : (wait_polls == 0 ? kDefaultWaitPolls : 0);
+  return run_forward(count, io, m, workspace, workspace_bytes, static_cast<hipStream_t>(stream),
+                     diag);
+}
+
 static bl_status forward_acc_one(int64_t m, int64_t n, int64_t k, const int8_t* q,
                                  const uint8_t* packed, int32_t* acc, void* workspace,
                                  size_t workspace_bytes, void* stream, int tiled) {
@@ -538,7 +604,7 @@ static bl_status forward_acc_one(int64_t m, int64_t n, int64_t k, const int8_t* 
   if ((st = check_ptr(q)) != BL_OK || (st = check_ptr(packed)) != BL_OK ||
       (st = check_ptr(acc)) != BL_OK)
     return st;
-  ProjIO io = {nullptr, q, packed, nullptr, nullptr, acc, n, k, tiled};
+  ProjIO io = {nullptr, q, packed, nullptr, nullptr, acc, n, k, tiled, nullptr, nullptr, nullptr};
   return run_forward(1, &io, m, workspace, workspace_bytes, static_cast<hipStream_t>(stream));
 }
 

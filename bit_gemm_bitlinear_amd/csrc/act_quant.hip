@@ -13,6 +13,8 @@
 #include "common.hpp"
 #include "internal.hpp"
 
+#include <type_traits>
+
 namespace bl {
 
 namespace {
@@ -149,6 +151,16 @@ __device__ __forceinline__ v4i transpose16(const int32_t (&q)[16]) {
   return o;
 }
 
+// Inspection output: codes 16g .. 16g+15 of a row of k codes in the natural
+// layout, from dwords nat[j] holding codes 4j .. 4j+3 (byte i = code 4j + i).
+// k % 4 == 0, so a dword never straddles the row end.
+__device__ __forceinline__ void put_natural(int8_t* __restrict__ row, int k, int g,
+                                            const uint32_t (&nat)[4]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    if (16 * g + 4 * j < k) *reinterpret_cast<uint32_t*>(row + 16 * g + 4 * j) = nat[j];
+}
+
 // Stores the 16 codes of group g of a row (dword a, byte b = code 4b + a).
 // GEMM order: the group's 16 bytes as they are.  Decode order: within each
 // 32-code block (groups 2i, 2i+1), dwords 0 and 2 of group 2i, dwords 0 and
@@ -208,7 +220,9 @@ __device__ __forceinline__ uint32_t wave_reduce(uint32_t v, Op op) {
 __device__ __forceinline__ void quant_row_internal_fast(const uint16_t* __restrict__ xr, int k,
                                                         int ngroups, v4i* __restrict__ qv,
                                                         uint32_t* red, int32_t* qsum,
-                                                        float* x_scale, bool paired) {
+                                                        float* x_scale, bool paired,
+                                                        int8_t* nat_row, float* ins_xs,
+                                                        int32_t* ins_qs) {
   constexpr int NB = kBatch;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   v4i lo[NB], hi[NB];
@@ -252,6 +266,17 @@ __device__ __forceinline__ void quant_row_internal_fast(const uint16_t* __restri
 #pragma unroll
       for (int a = 0; a < 4; ++a) usum = __builtin_amdgcn_sad_u8(d[a], 0u, usum);
       ++ng;
+      if (nat_row) {  // inspection: byte i of natural dword j = byte j of d[i]
+        uint32_t nat[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          uint32_t v = 0;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v |= ((d[i] >> (8 * j)) & 0xFFu) << (8 * i);
+          nat[j] = v ^ 0x80808080u;
+        }
+        put_natural(nat_row, k, g, nat);
+      }
       put_group(qv, g,
                 v4i{(int32_t)(d[0] ^ 0x80808080u), (int32_t)(d[1] ^ 0x80808080u),
                     (int32_t)(d[2] ^ 0x80808080u), (int32_t)(d[3] ^ 0x80808080u)},
@@ -264,8 +289,11 @@ __device__ __forceinline__ void quant_row_internal_fast(const uint16_t* __restri
   if (lane == 0) red[wave] = (uint32_t)sum;
   __syncthreads();
   if (tid == 0) {
-    *qsum = (int32_t)(red[0] + red[1] + red[2] + red[3]);
+    const int32_t total = (int32_t)(red[0] + red[1] + red[2] + red[3]);
+    *qsum = total;
     *x_scale = s;
+    if (ins_qs) *ins_qs = total;
+    if (ins_xs) *ins_xs = s;
   }
 }
 
@@ -278,10 +306,11 @@ __device__ __forceinline__ void quant_row_internal_fast(const uint16_t* __restri
 // rounds to an integer with ties to even and leaves q in two's complement in
 // the low byte of the sum's bits, which byte permutes gather into the
 // internal order (dword a, byte b = code 4b + a).
-template <int NBW>
+template <int NBW, bool INS>
 __device__ __forceinline__ void quant_row_wave(const uint16_t* __restrict__ xr, int k, int ngroups,
                                                v4i* __restrict__ qv, int32_t* qsum,
-                                               float* x_scale) {
+                                               float* x_scale, int8_t* nat_row, float* ins_xs,
+                                               int32_t* ins_qs) {
   const int lane = threadIdx.x & 63;
   const int kg = k >> 4;  // groups holding data (a last half group: k % 16 == 8)
   v4i lo[NBW], hi[NBW];
@@ -330,15 +359,30 @@ __device__ __forceinline__ void quant_row_wave(const uint16_t* __restrict__ xr, 
       sum = __builtin_amdgcn_sdot4(o[a], 0x01010101, sum, false);
     }
     qv[g] = o;
+    if (INS && nat_row) {  // inspection: natural dword j, byte i = byte j of o[i]
+      uint32_t nat[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t sel = 0x0c0c0000u | ((4u + j) << 8) | (uint32_t)j;
+        const uint32_t l2 = __builtin_amdgcn_perm((uint32_t)o[1], (uint32_t)o[0], sel);
+        const uint32_t h2 = __builtin_amdgcn_perm((uint32_t)o[3], (uint32_t)o[2], sel);
+        nat[j] = __builtin_amdgcn_perm(h2, l2, 0x05040100u);
+      }
+      put_natural(nat_row, k, g, nat);
+    }
   }
   sum = (int32_t)wave_reduce((uint32_t)sum, [](uint32_t x, uint32_t y) { return x + y; });
   if (lane == 0) {
     *qsum = sum;
     *x_scale = s;
+    if (INS && ins_qs) *ins_qs = sum;
+    if (INS && ins_xs) *ins_xs = s;
   }
 }
 
-template <int NBW>
+// INS: some job has inspection outputs (a separate instance, so that the
+// bench path carries none of their registers).
+template <int NBW, bool INS>
 __global__ __launch_bounds__(kThreads) void act_quant_rows_kernel(const ActQuantArgs a) {
   constexpr int kRowsPerBlock = kThreads / 64;
   const int b = blockIdx.x;
@@ -360,7 +404,9 @@ __global__ __launch_bounds__(kThreads) void act_quant_rows_kernel(const ActQuant
     for (int g = threadIdx.x & 63; g < J.ldq / 16; g += 64) qv[g] = v4i{0, 0, 0, 0};
     return;
   }
-  quant_row_wave<NBW>(J.x + (int64_t)m * J.k, J.k, J.ldq / 16, qv, J.qsum + m, J.x_scale + m);
+  quant_row_wave<NBW, INS>(J.x + (int64_t)m * J.k, J.k, J.ldq / 16, qv, J.qsum + m, J.x_scale + m,
+                      J.ins_q ? J.ins_q + (int64_t)m * J.k : nullptr,
+                      J.ins_xs ? J.ins_xs + m : nullptr, J.ins_qs ? J.ins_qs + m : nullptr);
 }
 
 __global__ __launch_bounds__(kThreads) void act_quant_internal_kernel(const ActQuantArgs a) {
@@ -386,9 +432,11 @@ __global__ __launch_bounds__(kThreads) void act_quant_internal_kernel(const ActQ
   int32_t sum = 0;
   v4i* qv = reinterpret_cast<v4i*>(qr);
   float s = 0.0f;
+  int8_t* nat_row = (J.x && J.ins_q) ? J.ins_q + (int64_t)m * J.k : nullptr;
   if (J.x && (J.k & 7) == 0 && J.ldq / 16 <= kThreads * kBatch) {
     quant_row_internal_fast(J.x + (int64_t)m * J.k, J.k, J.ldq / 16, qv, red, J.qsum + m,
-                            J.x_scale + m, J.paired != 0);
+                            J.x_scale + m, J.paired != 0, nat_row,
+                            J.ins_xs ? J.ins_xs + m : nullptr, J.ins_qs ? J.ins_qs + m : nullptr);
     return;
   }
   if (J.x) {
@@ -397,6 +445,16 @@ __global__ __launch_bounds__(kThreads) void act_quant_internal_kernel(const ActQ
 #pragma unroll
                     for (int i = 0; i < 16; ++i) sum += c[i];
                     put_group(qv, g, transpose16(c), J.paired != 0);
+                    if (nat_row) {
+                      uint32_t nat[4];
+#pragma unroll
+                      for (int j = 0; j < 4; ++j)
+                        nat[j] = ((uint32_t)c[4 * j] & 0xFFu) |
+                                 (((uint32_t)c[4 * j + 1] & 0xFFu) << 8) |
+                                 (((uint32_t)c[4 * j + 2] & 0xFFu) << 16) |
+                                 (((uint32_t)c[4 * j + 3] & 0xFFu) << 24);
+                      put_natural(nat_row, J.k, g, nat);
+                    }
                   });
   } else {
     const int8_t* qin = J.q_in + (int64_t)m * J.k;
@@ -412,6 +470,8 @@ __global__ __launch_bounds__(kThreads) void act_quant_internal_kernel(const ActQ
   if (threadIdx.x == 0) {
     J.qsum[m] = sum;
     if (J.x) J.x_scale[m] = s;
+    if (J.x && J.ins_qs) J.ins_qs[m] = sum;
+    if (J.x && J.ins_xs) J.ins_xs[m] = s;
   }
 }
 
@@ -445,14 +505,24 @@ hipError_t launch_act_quant_internal(const ActQuantArgs& a, int total_rows, hipS
     const int row_blocks = (total_rows + kThreads / 64 - 1) / (kThreads / 64);
     args.zero_blocks_begin = row_blocks;
     const dim3 grid((unsigned)(row_blocks + zero_blocks));
-    if (groups <= 64 * 4)
-      act_quant_rows_kernel<4><<<grid, kThreads, 0, s>>>(args);
-    else if (groups <= 64 * 7)
-      act_quant_rows_kernel<7><<<grid, kThreads, 0, s>>>(args);
-    else if (groups <= 64 * 8)
-      act_quant_rows_kernel<8><<<grid, kThreads, 0, s>>>(args);
+    bool ins = false;
+    for (int i = 0; i < args.count; ++i)
+      ins = ins || args.j[i].ins_q || args.j[i].ins_xs || args.j[i].ins_qs;
+    auto go = [&](auto insc) {
+      constexpr bool I = decltype(insc)::value;
+      if (groups <= 64 * 4)
+        act_quant_rows_kernel<4, I><<<grid, kThreads, 0, s>>>(args);
+      else if (groups <= 64 * 7)
+        act_quant_rows_kernel<7, I><<<grid, kThreads, 0, s>>>(args);
+      else if (groups <= 64 * 8)
+        act_quant_rows_kernel<8, I><<<grid, kThreads, 0, s>>>(args);
+      else
+        act_quant_rows_kernel<16, I><<<grid, kThreads, 0, s>>>(args);
+    };
+    if (ins)
+      go(std::true_type{});
     else
-      act_quant_rows_kernel<16><<<grid, kThreads, 0, s>>>(args);
+      go(std::false_type{});
     return hipGetLastError();
   }
   args.zero_blocks_begin = total_rows;

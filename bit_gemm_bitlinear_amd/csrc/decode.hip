@@ -33,6 +33,7 @@
 #include "common.hpp"
 #include "internal.hpp"
 
+#include <atomic>
 #include <type_traits>
 
 namespace bl {
@@ -158,17 +159,31 @@ struct Shared {
   // split shape: LDS handshakes between the two wave roles
   int32_t amax_count;  // activation waves that posted their absmax
   int32_t ready;       // activation waves done with codes and scalars
+  int32_t bad;         // an activation wave's wait gave up
 };
 
 // Waits until *c reaches `target` (other waves of this workgroup add to it).
 // Only LDS is involved, so a waiting wave's outstanding weight loads are left
-// alone.  The bound only guarantees an exit.
-__device__ __forceinline__ void lds_wait(const int32_t* c, int target) {
-  for (int it = 0; it < (1 << 24); ++it) {
-    if (__hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= target) break;
+// alone.  The waves of a workgroup are resident together, so the counter does
+// get there; the bound (`polls`) only guarantees an exit.  Returns false if
+// the wait gave up: the caller then reports it and poisons its outputs rather
+// than pass off what LDS held as a result.
+__device__ __forceinline__ bool lds_wait(const int32_t* c, int target, int polls) {
+  bool ok = false;
+  for (int it = 0; it < polls; ++it) {
+    if (__hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= target) {
+      ok = true;
+      break;
+    }
     __builtin_amdgcn_s_sleep(1);
   }
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  return ok;
+}
+
+// Records a wait that gave up: once per wave, in the caller's status word.
+__device__ __forceinline__ void report_giveup(const DecodeArgs& A) {
+  if (A.status && (threadIdx.x & 63) == 0) atomicOr(A.status, 1);
 }
 
 // Workgroup barrier ordering LDS only: weight loads in flight are not waited
@@ -185,13 +200,17 @@ __device__ __forceinline__ void lds_post(int32_t* c) {
   if ((threadIdx.x & 63) == 0) __hip_atomic_fetch_add(c, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
-// Writes one output (bf16, or the int32 accumulator for inspection).
+// Writes one output: bf16, or the int32 accumulator (forward_acc); with INS
+// (inspection) both where both are set.  A workgroup whose wait gave up
+// (`bad`) writes NaN / INT32_MIN.
+template <bool INS>
 __device__ __forceinline__ void store_out(const DecodeProj& P, int m, int n, int32_t acc,
-                                          const Shared& sh) {
+                                          const Shared& sh, bool bad) {
   if (P.y)
-    *G(P.y + (int64_t)m * P.n + n) = dequant_bf16_row(acc - sh.qs[m], sh.rd[m]);
-  else
-    *G(P.acc_out + (int64_t)m * P.n + n) = acc - sh.qs[m];
+    *G(P.y + (int64_t)m * P.n + n) =
+        bad ? (uint16_t)0x7FC0u : dequant_bf16_row(acc - sh.qs[m], sh.rd[m]);
+  if ((INS || !P.y) && P.acc_out)
+    *G(P.acc_out + (int64_t)m * P.n + n) = bad ? (int32_t)0x80000000u : acc - sh.qs[m];
 }
 
 // Stores the 16 codes of group g (dword a, byte b = code 4b + a of the group)
@@ -254,10 +273,12 @@ __device__ __forceinline__ void load_codes(const DecodeArgs& A, const DecodeProj
 // stage the loaded codes.  The four waves meet through barriers (single
 // shape) or LDS counters (split shape, where the streaming waves must not
 // wait with them).
+// `inspect` (fused, the projection's first workgroup): also write the codes
+// in the natural layout and the scales to P.q and P.x_scale when those are set.
 template <bool SPLIT, bool FUSED>
 __device__ __forceinline__ void prepare_codes(const DecodeArgs& A, const DecodeProj& P, int ns,
                                               const v4i (&xin)[kXChunks<FUSED>], const float ws,
-                                              int8_t* __restrict__ lds, Shared& sh) {
+                                              int8_t* __restrict__ lds, Shared& sh, bool inspect) {
   constexpr int NA = 256;  // activation threads
   constexpr int NX = kXChunks<FUSED>;
   const int M = A.m;
@@ -319,10 +340,14 @@ __device__ __forceinline__ void prepare_codes(const DecodeArgs& A, const DecodeP
       const int c = i - m * padg;
       put_group(lds + m * lrow, (pad0 >> 4) + c, v4i{0, 0, 0, 0});
     }
-    if constexpr (SPLIT)
-      lds_wait(&sh.amax_count, 4);
-    else
+    if constexpr (SPLIT) {
+      if (!lds_wait(&sh.amax_count, 4, A.wait_polls)) {
+        sh.bad = 1;  // published with the codes (lds_post below)
+        report_giveup(A);
+      }
+    } else {
       lds_barrier();
+    }
     float s[kFusedMaxM];
 #pragma unroll
     for (int r = 0; r < kFusedMaxM; ++r) {
@@ -373,6 +398,16 @@ __device__ __forceinline__ void prepare_codes(const DecodeArgs& A, const DecodeP
         const int k0 = 16 * (g - m * gpr);
         put_group(lds + m * lrow, k0 >> 4,
                   v4i{(int32_t)d[0], (int32_t)d[1], (int32_t)d[2], (int32_t)d[3]});
+        if (inspect && P.q) {  // natural order: byte e of the group = code e
+          v4i nat;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const uint32_t lo = __builtin_amdgcn_perm(r[4 * j + 1], r[4 * j], 0x0c0c0400u);
+            const uint32_t hi = __builtin_amdgcn_perm(r[4 * j + 3], r[4 * j + 2], 0x0c0c0400u);
+            nat[j] = (int32_t)__builtin_amdgcn_perm(hi, lo, 0x05040100u);
+          }
+          *G(reinterpret_cast<v4i*>(P.q + (int64_t)m * P.k + k0)) = nat;
+        }
       }
     }
 #pragma unroll
@@ -382,6 +417,7 @@ __device__ __forceinline__ void prepare_codes(const DecodeArgs& A, const DecodeP
         if (lane == 0) atomicAdd(&sh.qs[r], v);  // zeroed before the absmax meeting
       }
       if (xt == r && r < M && P.y) sh.rd[r] = row_div_setup(s[r] * ws);
+      if (xt == r && r < M && inspect && P.x_scale) *G(P.x_scale + r) = s[r];
     }
   }
   if constexpr (SPLIT)
@@ -416,7 +452,8 @@ __device__ __forceinline__ void mma_chunk(v4i& acc1, v4i& acc4, const v4i (&a)[4
 
 // EARLY (ring shape, several token rows): the first weight loads go out
 // before the code preparation instead of after it.
-template <int TWW, int MODE, bool FUSED, bool SPLIT, bool EARLY = false>
+// INS: inspection outputs are written (a separate kernel instance).
+template <int TWW, int MODE, bool FUSED, bool SPLIT, bool EARLY, bool INS>
 __device__ __forceinline__ void decode_body(const DecodeArgs& A, const DecodeProj& P, int wl,
                                             int8_t* __restrict__ lds, Shared& sh) {
   constexpr int NT = SPLIT ? 512 : 256;
@@ -441,6 +478,8 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& A, const DecodePro
   const int nw = min(ns, ws0 + nsw) - ws0;  // slabs of this wave (may be 0)
   const int rowbytes = P.k >> 2;
   const int lrow = A.lds_row;
+  const bool inspect = INS && FUSED && wl == 0;  // one workgroup writes the inspection outputs
+  bool bad = false;                       // split shape: a wait of this wave gave up
 
   // weights: this wave streams its TWW row tiles over its K slabs, slab-major
   // so each A fragment feeds TWW tiles.  Every load is unconditional (past
@@ -489,7 +528,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& A, const DecodePro
       __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");  // counters are zero
-      prepare_codes<true, FUSED>(A, P, ns, xin, ws, lds, sh);
+      prepare_codes<true, FUSED>(A, P, ns, xin, ws, lds, sh, inspect);
     } else {
       // a ring of NC chunks per lane: every slot is refilled with the chunk
       // NC ahead right after it is read, so NC loads stay in flight until
@@ -502,7 +541,12 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& A, const DecodePro
 #pragma unroll
       for (int d = 0; d < NC; ++d) ring[d] = wload(d);
       __builtin_amdgcn_sched_barrier(0);
-      lds_wait(&sh.ready, 4);
+      if (!lds_wait(&sh.ready, 4, A.wait_polls)) {
+        bad = true;
+        report_giveup(A);
+      }
+      // an activation wave's give-up, published with `ready` (wave-uniform)
+      bad = __builtin_amdgcn_readfirstlane((bad || sh.bad) ? 1 : 0) != 0;
       v4i a[4];
       auto round = [&](int base, auto refill) {
         static_for<NC>([&](auto dc) {
@@ -543,7 +587,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& A, const DecodePro
       load_codes<FUSED>(A, P, sb, ns, xin, ws);
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (EARLY) fill();
-      prepare_codes<false, FUSED>(A, P, ns, xin, ws, lds, sh);
+      prepare_codes<false, FUSED>(A, P, ns, xin, ws, lds, sh, inspect);
     }
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (!EARLY) fill();
@@ -580,6 +624,10 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& A, const DecodePro
 #pragma unroll
   for (int t = 0; t < TWW; ++t) acc[t] += acc4[t] >> 2;  // exact: multiples of 4
 
+  // inspection: the code sums of the fused quantization (final once the codes
+  // are posted, which every streaming wave has waited for)
+  if (INS && FUSED && inspect && P.qsum && tid < M) *G(P.qsum + tid) = sh.qs[tid];
+
   // epilogue.  Streaming lane (ln, lg) holds rows m = 4*lg + r of output
   // column row0 + 16*t + ln.
   if (P.wk == 1 && P.ksplit == 1) {
@@ -590,7 +638,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& A, const DecodePro
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int m = 4 * lg + r;
-        if (m < M && n < P.n) store_out(P, m, n, acc[t][r], sh);
+        if (m < M && n < P.n) store_out<INS>(P, m, n, acc[t][r], sh, bad);
       }
     }
     return;
@@ -608,8 +656,11 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& A, const DecodePro
         if (m < M) red[((sw * TWW + t) * M + m) * 16 + ln] = acc[t][r];
       }
     }
+    if constexpr (SPLIT)
+      if (bad) sh.bad = 1;
   }
   __syncthreads();
+  if constexpr (SPLIT) bad = __builtin_amdgcn_readfirstlane(sh.bad) != 0;
   // output idx -> row m and local column nl; rows_wg and TWW * 16 are powers
   // of two, so the split is shifts and masks
   const int lrw = 31 - __builtin_clz(rows_wg), ltw = 31 - __builtin_clz(TWW * 16);
@@ -622,7 +673,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& A, const DecodePro
     for (int q = 0; q < P.wk; ++q) v += red[(((g * P.wk + q) * TWW + t) * M + m) * 16 + c];
     if (n >= P.n) continue;
     if (P.ksplit == 1)
-      store_out(P, m, n, v, sh);
+      store_out<INS>(P, m, n, v, sh, bad);
     else
       atomicAdd(P.part + (int64_t)m * P.n + n, v);
   }
@@ -658,26 +709,26 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& A, const DecodePro
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      if (base + NT * i < nout && outn[i] < P.n) store_out(P, outm[i], outn[i], vals[i], sh);
+      if (base + NT * i < nout && outn[i] < P.n) store_out<INS>(P, outm[i], outn[i], vals[i], sh, bad);
   }
 }
 
-template <int TWW, int MODE, bool SPLIT, bool EARLY>
+template <int TWW, int MODE, bool SPLIT, bool EARLY, bool INS>
 __device__ __forceinline__ void decode_tw(const DecodeArgs& A, const DecodeProj& P, int wl,
                                           int8_t* lds, Shared& sh) {
   if constexpr (MODE == 0) {
     if (P.x) {
-      decode_body<TWW, MODE, true, SPLIT, EARLY>(A, P, wl, lds, sh);
+      decode_body<TWW, MODE, true, SPLIT, EARLY, INS>(A, P, wl, lds, sh);
       return;
     }
   }
-  decode_body<TWW, MODE, false, SPLIT, EARLY>(A, P, wl, lds, sh);
+  decode_body<TWW, MODE, false, SPLIT, EARLY, INS>(A, P, wl, lds, sh);
 }
 
 // SPLIT: 8 waves, for launches that fit on the chip in one wave of WGs (the
 // activation work of a WG then overlaps its weight stream instead of
 // preceding it); otherwise 4 waves, so that several WGs share a CU.
-template <int MODE, bool SPLIT, bool EARLY = false>
+template <int MODE, bool SPLIT, bool EARLY, bool INS>
 __global__ __launch_bounds__(SPLIT ? 512 : 256) void decode_kernel(const DecodeArgs A) {
   extern __shared__ __align__(16) int8_t lds[];
   __shared__ Shared sh;
@@ -685,17 +736,18 @@ __global__ __launch_bounds__(SPLIT ? 512 : 256) void decode_kernel(const DecodeA
     if (threadIdx.x == 0) {
       sh.amax_count = 0;
       sh.ready = 0;
+      sh.bad = 0;
     }
   }
   int wl;
   const DecodeProj P = select_proj(A.count, &wl);
   switch (P.tww) {
-    case 1: decode_tw<1, MODE, SPLIT, EARLY>(A, P, wl, lds, sh); break;
-    case 2: decode_tw<2, MODE, SPLIT, EARLY>(A, P, wl, lds, sh); break;
+    case 1: decode_tw<1, MODE, SPLIT, EARLY, INS>(A, P, wl, lds, sh); break;
+    case 2: decode_tw<2, MODE, SPLIT, EARLY, INS>(A, P, wl, lds, sh); break;
     case 3:  // split-shape plans only, with the K range unsplit (wk = 1)
-      if constexpr (SPLIT) decode_tw<3, MODE, SPLIT, EARLY>(A, P, wl, lds, sh);
+      if constexpr (SPLIT) decode_tw<3, MODE, SPLIT, EARLY, INS>(A, P, wl, lds, sh);
       break;
-    default: decode_tw<4, MODE, SPLIT, EARLY>(A, P, wl, lds, sh); break;
+    default: decode_tw<4, MODE, SPLIT, EARLY, INS>(A, P, wl, lds, sh); break;
   }
 }
 
@@ -797,10 +849,15 @@ bool plan_decode_split(int64_t m, int32_t count, const int64_t* ns, const int64_
   return false;
 }
 
-int device_cu_count() {
-  static int cus[64] = {0};
+int current_device_index() {
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = 0;
+  return dev;
+}
+
+int device_cu_count() {
+  static int cus[kMaxDevices] = {0};
+  const int dev = current_device_index();
   if (cus[dev] == 0) {
     int n = 0;
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) n = 1;
@@ -814,38 +871,55 @@ size_t decode_lds_bytes(int64_t m, int lds_row) {
 }
 
 // Lets kernel K use up to `bytes` of dynamic LDS (needed above 64 KB); once
-// per instantiation.
+// per instantiation and device.
 template <auto Kern>
 hipError_t allow_lds(size_t bytes) {
   if (bytes <= 64 * 1024) return hipSuccess;
-  static const hipError_t e = hipFuncSetAttribute(
+  static std::atomic<bool> done[kMaxDevices];
+  const int dev = current_device_index();
+  if (done[dev].load(std::memory_order_acquire)) return hipSuccess;
+  const hipError_t e = hipFuncSetAttribute(
       reinterpret_cast<const void*>(Kern), hipFuncAttributeMaxDynamicSharedMemorySize,
       (int)decode_lds_bytes(kDecodeMaxM, kDecodeLdsA / kDecodeMaxM + 16));
+  if (e == hipSuccess) done[dev].store(true, std::memory_order_release);
   return e;
 }
 
-hipError_t launch_decode(const DecodeArgs& a, int total_wgs, size_t lds_bytes, hipStream_t s) {
+template <bool INS>
+hipError_t launch_decode_as(const DecodeArgs& a, int total_wgs, size_t lds_bytes, hipStream_t s) {
   const bool split = a.load_mode == 0 && total_wgs <= device_cu_count();
   const dim3 grid((unsigned)total_wgs);
   hipError_t e = hipSuccess;
   if (split) {
-    e = allow_lds<&decode_kernel<0, true>>(lds_bytes);
-    if (e == hipSuccess) decode_kernel<0, true><<<grid, 512, lds_bytes, s>>>(a);
+    e = allow_lds<&decode_kernel<0, true, false, INS>>(lds_bytes);
+    if (e == hipSuccess) decode_kernel<0, true, false, INS><<<grid, 512, lds_bytes, s>>>(a);
   } else if (a.load_mode == 0 && a.m > 1) {
-    e = allow_lds<&decode_kernel<0, false, true>>(lds_bytes);
-    if (e == hipSuccess) decode_kernel<0, false, true><<<grid, 256, lds_bytes, s>>>(a);
+    e = allow_lds<&decode_kernel<0, false, true, INS>>(lds_bytes);
+    if (e == hipSuccess) decode_kernel<0, false, true, INS><<<grid, 256, lds_bytes, s>>>(a);
   } else if (a.load_mode == 0) {
-    e = allow_lds<&decode_kernel<0, false>>(lds_bytes);
-    if (e == hipSuccess) decode_kernel<0, false><<<grid, 256, lds_bytes, s>>>(a);
+    e = allow_lds<&decode_kernel<0, false, false, INS>>(lds_bytes);
+    if (e == hipSuccess) decode_kernel<0, false, false, INS><<<grid, 256, lds_bytes, s>>>(a);
   } else if (a.load_mode == 1) {
-    e = allow_lds<&decode_kernel<1, false>>(lds_bytes);
-    if (e == hipSuccess) decode_kernel<1, false><<<grid, 256, lds_bytes, s>>>(a);
+    e = allow_lds<&decode_kernel<1, false, false, INS>>(lds_bytes);
+    if (e == hipSuccess) decode_kernel<1, false, false, INS><<<grid, 256, lds_bytes, s>>>(a);
   } else {
-    e = allow_lds<&decode_kernel<2, false>>(lds_bytes);
-    if (e == hipSuccess) decode_kernel<2, false><<<grid, 256, lds_bytes, s>>>(a);
+    e = allow_lds<&decode_kernel<2, false, false, INS>>(lds_bytes);
+    if (e == hipSuccess) decode_kernel<2, false, false, INS><<<grid, 256, lds_bytes, s>>>(a);
   }
   if (e != hipSuccess) return e;
   return hipGetLastError();
+}
+
+hipError_t launch_decode(const DecodeArgs& a, int total_wgs, size_t lds_bytes, hipStream_t s) {
+  // inspection: int32 accumulators next to bf16 outputs, or the fused
+  // quantization's codes, scales or code sums asked for
+  bool ins = false;
+  for (int i = 0; i < a.count; ++i) {
+    const DecodeProj& P = a.p[i];
+    ins = ins || (P.y && P.acc_out) || (P.x && (P.q || P.x_scale || P.qsum));
+  }
+  return ins ? launch_decode_as<true>(a, total_wgs, lds_bytes, s)
+             : launch_decode_as<false>(a, total_wgs, lds_bytes, s);
 }
 
 }  // namespace bl

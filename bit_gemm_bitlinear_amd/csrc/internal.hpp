@@ -8,6 +8,9 @@
 namespace bl {
 
 constexpr int kMaxProj = 16;
+constexpr int kMaxDevices = 64;  // device indices the per-device caches cover
+
+int current_device_index();  // hipGetDevice, clamped to [0, kMaxDevices)
 
 // Decode path (M <= 16) limits.
 constexpr int kDecodeMaxM = 16;
@@ -42,6 +45,11 @@ struct ActQuantJob {
   int32_t k, ldq, m, m_pad;
   int32_t row_begin;   // first block of this job in the launch
   int32_t paired;      // 1: the decode kernel's order (put_group in act_quant.hip), 0: the GEMM's
+  // optional inspection outputs (bf16 input only; nullptr: not written): the
+  // codes in the natural layout [m][k], the scales [m] and the code sums [m]
+  int8_t* ins_q;
+  float* ins_xs;
+  int32_t* ins_qs;
 };
 
 struct ActQuantArgs {
@@ -68,11 +76,15 @@ struct DecodeProj {
   const uint8_t* packed;
   const float* w_scale;
   uint16_t* y;         // bf16 output, or nullptr
-  int32_t* acc_out;    // int32 output when y == nullptr
+  int32_t* acc_out;    // int32 accumulators [m][n] (as well as y when both are set), or nullptr
   const uint16_t* x;   // fused: bf16 activations [m][k]; nullptr otherwise
-  const int8_t* q;     // not fused: internal-layout codes [m][ldq]
-  const float* x_scale;
-  const int32_t* qsum;
+  // Not fused: the staged inputs -- internal-layout codes [m][ldq], scales
+  // and code sums prepared by act_quant.hip.  Fused: optional inspection
+  // outputs the kernel writes (codes in the natural layout [m][k], scales,
+  // code sums), or nullptr.
+  int8_t* q;
+  float* x_scale;
+  int32_t* qsum;
   int32_t* part;       // [m][n] int32 split-K partials (zeroed beforehand)
   uint32_t* count;     // [ngroups] split-K arrival counters (zeroed beforehand)
   int32_t n, k, ldq;
@@ -90,7 +102,14 @@ struct DecodeArgs {
   int32_t m;
   int32_t load_mode;  // 0: 16-byte rows, 1: 4-byte rows, 2: byte rows
   int32_t lds_row;    // LDS row stride of the staged codes (bytes)
+  // The split shape's waves meet through LDS counters polled at most
+  // wait_polls times (0: a wait gives up at once).  A workgroup whose wait
+  // gave up writes NaN (bf16) or INT32_MIN (int32) outputs and, if status is
+  // set, ORs 1 into *status.
+  int32_t* status;
+  int32_t wait_polls;
 };
+constexpr int32_t kDefaultWaitPolls = 1 << 24;
 
 struct DecodePlan {
   int32_t wk, tww, kspw, ksplit, ngroups;
@@ -122,7 +141,7 @@ struct PrefillProj {
   const uint8_t* packed;
   const float* w_scale;
   uint16_t* y;
-  int32_t* acc_out;
+  int32_t* acc_out;     // int32 accumulators (as well as y when both are set), or nullptr
   const int8_t* q;      // internal layout [m_pad][ldq]
   const float* x_scale;
   const int32_t* qsum;

@@ -35,6 +35,7 @@
 #include "common.hpp"
 #include "internal.hpp"
 
+#include <atomic>
 #include <type_traits>
 
 namespace bl {
@@ -232,10 +233,8 @@ __global__ __launch_bounds__(kThreads) void prefill_reg_kernel(const PrefillArgs
         const int n = ncol0 + 32 * f + lj;
         if (n >= P.n) continue;
         const int32_t v = acc[i][f][r] - qs;
-        if (P.y)
-          *G(P.y + (int64_t)m * P.ldy + n) = dequant_bf16_row(v, rd);
-        else
-          *G(P.acc_out + (int64_t)m * P.ldy + n) = v;
+        if (P.y) *G(P.y + (int64_t)m * P.ldy + n) = dequant_bf16_row(v, rd);
+        if (P.acc_out) *G(P.acc_out + (int64_t)m * P.ldy + n) = v;
       }
     }
   }
@@ -365,7 +364,9 @@ struct Stager {
 // the tile and its own columns, so every weight column is expanded once per
 // workgroup; with WMI = 2 two waves share (and both expand) each column.
 // One output tile (BM rows x BNT columns) of projection P.
-template <int BNT, int NST, int WMI, int NW, int BK>
+// INS: int32 accumulators are written next to the bf16 outputs where a
+// projection asks for both (inspection; a separate kernel instance).
+template <int BNT, int NST, int WMI, int NW, int BK, bool INS>
 __device__ __forceinline__ void prefill_tile(const PrefillArgs& A, const PrefillProj& P, int tm, int tn,
                                              int kp, int8_t* __restrict__ smem) {
   using K = Cfg<BNT, WMI, NW, BK>;
@@ -464,7 +465,9 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& A, const Prefill
   for (int i = 0; i < WMI; ++i) {
     const int m = m0 + wm0 + 32 * i + lj;
     const bool row_ok = m < A.m;
-    if (!bf || P.ksplit > 1) {  // int32 sums: the output, or a K part's partial sums
+    // int32 sums: the output (forward_acc, or inspection next to the bf16
+    // output), or a K part's partial sums
+    if (!bf || P.ksplit > 1 || (INS && P.acc_out)) {
       const int ld = P.ksplit > 1 ? P.n : P.ldy;
       const bool wide = (ld & 3) == 0;  // rows are 16-byte aligned
       int32_t* yrow = (P.ksplit > 1 ? P.part + (int64_t)kp * A.m * P.n : P.acc_out) + (int64_t)m * ld;
@@ -481,7 +484,11 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& A, const Prefill
             for (int e = 0; e < 4 && n + e < P.n; ++e) *G(yrow + n + e) = v[e];
           }
         }
-      continue;
+      if constexpr (INS) {
+        if (!bf || P.ksplit > 1) continue;
+      } else {
+        continue;
+      }
     }
     const RowDiv d = row_div_setup(xs[i] * ws);
     const bool wide = (P.ldy & 7) == 0;  // output rows are 16-byte aligned
@@ -532,7 +539,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& A, const Prefill
 // entries marked narrow: the host gives the tiles that would otherwise run
 // in a last, partly filled round of workgroups that width, so that the
 // round fills the chip and ends sooner.
-template <int NST, int WMI, int NW, int BK>
+template <int NST, int WMI, int NW, int BK, bool INS>
 __global__ __launch_bounds__(64 * NW)
 __attribute__((amdgpu_waves_per_eu(NW * kPrefillWgsPerCu / 4))) void prefill_kernel(const PrefillArgs A) {
   extern __shared__ __align__(16) int8_t smem[];
@@ -546,9 +553,9 @@ __attribute__((amdgpu_waves_per_eu(NW * kPrefillWgsPerCu / 4))) void prefill_ker
   const int kp = tn / P.tiles_n;
   tn -= kp * P.tiles_n;
   if (P.narrow)
-    prefill_tile<kPrefillNarrowBN, NST, WMI, NW, BK>(A, P, tm, tn, kp, smem);
+    prefill_tile<kPrefillNarrowBN, NST, WMI, NW, BK, INS>(A, P, tm, tn, kp, smem);
   else
-    prefill_tile<kPrefillBN, NST, WMI, NW, BK>(A, P, tm, tn, kp, smem);
+    prefill_tile<kPrefillBN, NST, WMI, NW, BK, INS>(A, P, tm, tn, kp, smem);
 }
 
 // Adds the K parts of the split projections.  Piece i of a projection is 8
@@ -584,7 +591,7 @@ __global__ __launch_bounds__(kThreads) void prefill_finish_kernel(const PrefillA
     for (int kp = 0; kp < P.ksplit; ++kp)
       for (int e = 0; e < 8 && n + e < P.n; ++e) v[e] += *G(src + kp * slice + e);
   }
-  if (!P.y) {
+  if (P.acc_out) {
     int32_t* dst = P.acc_out + (int64_t)m * P.ldy + n;
     if ((P.ldy & 3) == 0 && whole) {
       *G(reinterpret_cast<v4i*>(dst)) = v4i{v[0], v[1], v[2], v[3]};
@@ -592,8 +599,8 @@ __global__ __launch_bounds__(kThreads) void prefill_finish_kernel(const PrefillA
     } else {
       for (int e = 0; e < 8 && n + e < P.n; ++e) *G(dst + e) = v[e];
     }
-    return;
   }
+  if (!P.y) return;
   const RowDiv d = row_div_setup(*G(P.x_scale + m) * *G(P.w_scale));
   float yf[8];
 #pragma unroll
@@ -634,11 +641,26 @@ hipError_t launch_prefill(const PrefillArgs& a, int total_tiles, hipStream_t s) 
                   NW = BL_PREFILL_NW, BK = BL_PREFILL_BK;
     static_assert(BNT >= kPrefillNarrowBN, "the wide tiles' slab buffers hold the narrow ones'");
     constexpr size_t lds = (size_t)NST * Cfg<BNT, WMI, NW, BK>::kStageBytes;
-    static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&prefill_kernel<NST, WMI, NW, BK>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (attr != hipSuccess) return attr;
-    prefill_kernel<NST, WMI, NW, BK><<<(unsigned)total_tiles, 64 * NW, lds, s>>>(a);
+    bool ins = false;
+    for (int i = 0; i < a.count; ++i) ins = ins || (a.p[i].y && a.p[i].acc_out);
+    auto go = [&](auto insc) -> hipError_t {
+      constexpr bool I = decltype(insc)::value;
+      if (lds > 64 * 1024) {  // the attribute is needed above 64 KB; once per device
+        static std::atomic<bool> done[kMaxDevices];
+        const int dev = current_device_index();
+        if (!done[dev].load(std::memory_order_acquire)) {
+          const hipError_t attr = hipFuncSetAttribute(
+              reinterpret_cast<const void*>(&prefill_kernel<NST, WMI, NW, BK, I>),
+              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+          if (attr != hipSuccess) return attr;
+          done[dev].store(true, std::memory_order_release);
+        }
+      }
+      prefill_kernel<NST, WMI, NW, BK, I><<<(unsigned)total_tiles, 64 * NW, lds, s>>>(a);
+      return hipSuccess;
+    };
+    const hipError_t e = ins ? go(std::true_type{}) : go(std::false_type{});
+    if (e != hipSuccess) return e;
   } else if (a.load_mode == 1) {
     prefill_reg_kernel<1><<<(unsigned)total_tiles, kThreads, 0, s>>>(a);
   } else {

@@ -151,8 +151,11 @@ size_t bitlinear_forward_workspace_bytes(int64_t m, int64_t n, int64_t k);
  * bf16 (written).  workspace: at least
  * bitlinear_forward_workspace_bytes(m, n, k) bytes; contents on entry do
  * not matter.  M <= 16 runs the decode GEMV path, larger M the int8
- * matrix-core GEMM path; both give identical results.  Enqueues two
- * kernels (activation quantization, then the contraction). */
+ * matrix-core GEMM path; both give identical results.  Enqueues one to
+ * three kernels, by M, K and the launch plan: the decode kernel alone when
+ * it quantizes the activations itself; otherwise an activation-quantization
+ * kernel, then the contraction, and for a GEMM whose K is split across
+ * workgroups a pass that adds the parts. */
 bl_status bitlinear_forward(int64_t m, int64_t n, int64_t k,
                             const uint16_t *x, const uint8_t *packed,
                             const float *w_scale, uint16_t *y,
@@ -174,6 +177,12 @@ size_t bitlinear_forward_grouped_workspace_bytes(int32_t count,
                                                  const bl_projection *projs,
                                                  int64_t m);
 
+/* Kernels one bitlinear_forward_grouped call with these shapes enqueues (1
+ * to 3: see bitlinear_forward), or -1 for invalid arguments.  Host only;
+ * only the shapes of `projs` are read. */
+int32_t bitlinear_forward_grouped_launches(int32_t count, const bl_projection *projs,
+                                           int64_t m);
+
 /* Several independent BitLinear forwards with the same token count M (for
  * instance the projections of one decoder layer) in one pass: one
  * activation-quantization launch and one contraction launch for all of
@@ -184,6 +193,33 @@ size_t bitlinear_forward_grouped_workspace_bytes(int32_t count,
 bl_status bitlinear_forward_grouped(int32_t count, const bl_projection *projs,
                                     int64_t m, void *workspace,
                                     size_t workspace_bytes, void *stream);
+
+/* Side outputs of a forward call, for inspecting the values the forward
+ * path itself computed (all DEVICE pointers, 16-byte aligned; each may be
+ * NULL, and is then not written). */
+typedef struct {
+  int8_t *q;        /* [M][K] the int8 codes x was quantized to (the blog's
+                       activation_norm_quant), natural row-major layout */
+  float *x_scale;   /* [M] the per-token scales 127 / max(max_k |x|, 1e-5) */
+  int32_t *qsum;    /* [M] sum over k of q[m][k] */
+  int32_t *acc;     /* [M][N] the exact accumulators sum_k q[m][k] * u[n][k] */
+} bl_inspect;
+
+/* bitlinear_forward_grouped with inspection: the same plans, kernels and
+ * outputs y, and in addition the codes, scales, code sums and int32
+ * accumulators each projection's kernels computed (inspect: HOST array of
+ * `count` bl_inspect).  wait_polls bounds the waits between the waves of a
+ * decode workgroup (0: the default, 2^24 polls; negative: every such wait
+ * gives up at once, which exercises the error report).  A workgroup whose
+ * wait gave up writes NaN (bf16 0x7FC0) outputs and INT32_MIN accumulators,
+ * and if `status` (a DEVICE int32, may be NULL) is given ORs 1 into it; the
+ * library never clears it.  The other entry points use the default bound
+ * and no status word (their outputs are still poisoned on a give-up). */
+bl_status bitlinear_forward_grouped_inspect(int32_t count, const bl_projection *projs,
+                                            int64_t m, const bl_inspect *inspect,
+                                            int32_t *status, int32_t wait_polls,
+                                            void *workspace, size_t workspace_bytes,
+                                            void *stream);
 
 /* For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc):

@@ -45,7 +45,7 @@ def declared_functions():
 
 def test_exports_every_declared_function(bl):
     names = declared_functions()
-    assert len(names) == 16
+    assert len(names) == 18
     lib = bl.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -88,7 +88,7 @@ def test_probe_library_exports_and_validation():
 
 def test_status_strings_and_version(bl):
     lib = bl.lib()
-    assert lib.bitlinear_abi_version() == 2
+    assert lib.bitlinear_abi_version() == 3
     for s in range(6):
         assert lib.bitlinear_status_string(s)
     assert lib.bitlinear_status_string(99) == b"unknown status"
@@ -189,6 +189,53 @@ def test_grouped_validation_and_sizes(bl):
     assert need >= 2 * lib.bitlinear_forward_workspace_bytes(1, 64, 128) - 512
     assert lib.bitlinear_forward_grouped(2, arr, 1, A16[0], need - 1, None) == 4
     assert lib.bitlinear_forward_grouped_workspace_bytes(0, arr, 1) == 0
+
+
+def test_inspect_and_launch_query_validation(bl):
+    """The inspection entry point and the launch-count query reject bad
+    arguments on the host; the query counts the kernels of each path."""
+    lib = bl.lib()
+    Proj, Ins = bl.Projection, bl.Inspect
+    arr = (Proj * 2)()
+    for i in range(2):
+        arr[i] = Proj(0x10000, 0x20000, 0x30000, 0x40000, 64, 256)
+    ins = (Ins * 2)()
+    big = 1 << 30
+    assert lib.bitlinear_forward_grouped_inspect(2, arr, 1, None, None, 0, A16[0], big, None) == 1
+    ins[1].acc = 0x50008  # misaligned optional output
+    assert lib.bitlinear_forward_grouped_inspect(2, arr, 1, ins, None, 0, A16[0], big, None) == 3
+    ins[1].acc = 0
+    assert lib.bitlinear_forward_grouped_inspect(2, arr, 1, ins, P(0x60004), 0, A16[0], big,
+                                                 None) == 3
+    assert lib.bitlinear_forward_grouped_inspect(2, arr, 1, ins, None, 0, None, big, None) == 4
+    assert lib.bitlinear_forward_grouped_inspect(0, arr, 1, ins, None, 0, A16[0], big, None) == 1
+    assert lib.bitlinear_forward_grouped_launches(0, arr, 1) == -1
+    assert lib.bitlinear_forward_grouped_launches(2, None, 1) == -1
+    arr[1].k = 258
+    assert lib.bitlinear_forward_grouped_launches(2, arr, 1) == -1
+    # decode with fused quantization (one kernel), decode with staged codes
+    # (quantization + contraction), prefill (two), prefill with K split
+    # across workgroups (plus the pass that adds the parts)
+    assert bl.forward_grouped_launches(1, [(64, 256)]) == 1
+    assert bl.forward_grouped_launches(16, [(64, 4096)]) == 2
+    assert bl.forward_grouped_launches(300, [(640, 4096)]) == 2
+    assert bl.forward_grouped_launches(256, [(301, 16384)]) == 3
+
+
+def test_binding_rejects_host_tensors(bl):
+    """The binding refuses host tensors before any library call (a host
+    pointer handed to a kernel would fault the GPU)."""
+    import torch
+
+    x = torch.zeros((2, 256), dtype=torch.bfloat16)
+    with pytest.raises(TypeError):
+        bl.forward(x, torch.zeros((32, 64), dtype=torch.uint8), torch.ones(1))
+    with pytest.raises(TypeError):
+        bl.forward_acc(torch.zeros((2, 256), dtype=torch.int8), torch.zeros((32, 64), dtype=torch.uint8))
+    with pytest.raises(TypeError):
+        bl.pack_weights(torch.zeros((4, 16)))
+    with pytest.raises(TypeError):
+        bl.GroupedCall([x], [torch.zeros((32, 64), dtype=torch.uint8)], [torch.ones(1)])
 
 
 def test_workspace_sizes_cover_codes(bl):

@@ -395,11 +395,30 @@ def packed_workload(bl, wl):
     return _PACK_CACHE[wl.name]
 
 
+def check_inspection(name, x, y, ins, p_ref, s_ref, y_ref):
+    """The forward path's own intermediates against the oracle: int8 codes,
+    scales and code sums bit for bit (the blog's activation_norm_quant), the
+    int32 accumulators bit for bit (the F.linear contraction), and the bf16
+    output."""
+    q_ref, xs_ref = oracle.act_quant(x)
+    q = ins["q"].cpu().numpy()
+    bad = np.argwhere(q != q_ref)
+    assert bad.size == 0, f"{name}: {len(bad)} codes differ, first at {bad[0].tolist()}"
+    assert np.array_equal(f32_bits(ins["x_scale"].cpu().numpy()), f32_bits(xs_ref)), f"{name}: scales"
+    assert np.array_equal(ins["qsum"].cpu().numpy(), q_ref.astype(np.int64).sum(axis=1)), f"{name}: sums"
+    acc_ref = oracle.contract(q_ref, oracle.unpack(p_ref))
+    assert np.array_equal(ins["acc"].cpu().numpy(), acc_ref), f"{name}: accumulators"
+    assert_bf16_close(host_bits(y), y_ref, f"{name} (inspect call)")
+
+
 @pytest.mark.parametrize("name,m,variant", workload_cases())
 def test_workload_parity(bl, name, m, variant):
     """Every projection of the workload, full size, in one grouped call
     (the launch configuration the benchmark times, whose weights are tiled),
-    with the weights in both layouts."""
+    with the weights in both layouts.  The inspection call runs the same
+    kernels and also returns the codes, scales, code sums and int32
+    accumulators the forward path computed; each is compared element by
+    element with the oracle."""
     wl = wls.WORKLOADS[name]
     entries = packed_workload(bl, wl)
     xs = [wls.activations(wl, pi, m, variant) for pi in range(len(wl.projections))]
@@ -407,7 +426,129 @@ def test_workload_parity(bl, name, m, variant):
     scales = [e[1] for e in entries]
     ys = bl.forward_grouped(dxs, [e[0] for e in entries], scales)
     yts = bl.forward_grouped(dxs, [e[4] for e in entries], scales)
+    yis, inss, status = bl.forward_grouped_inspect(dxs, [e[4] for e in entries], scales)
+    yri, insr, status_r = bl.forward_grouped_inspect(dxs, [e[0] for e in entries], scales)
+    assert int(status.item()) == 0 and int(status_r.item()) == 0
     for pi, (x, y, yt, e) in enumerate(zip(xs, ys, yts, entries)):
+        what = f"{name} {wl.projections[pi].name} M={m}"
         y_ref = oracle.forward(x, e[2], e[3])
-        assert_bf16_close(host_bits(y), y_ref, f"{name} {wl.projections[pi].name} M={m}")
-        assert_bf16_close(host_bits(yt), y_ref, f"{name} {wl.projections[pi].name} M={m} tiled")
+        assert_bf16_close(host_bits(y), y_ref, what)
+        assert_bf16_close(host_bits(yt), y_ref, f"{what} tiled")
+        assert torch.equal(yis[pi].view(torch.int16), yt.view(torch.int16)), f"{what}: inspect call"
+        check_inspection(f"{what} tiled", x, yis[pi], inss[pi], e[2], e[3], y_ref)
+        check_inspection(f"{what} rows", x, yri[pi], insr[pi], e[2], e[3], y_ref)
+
+
+def workload_shapes():
+    """(workload, M, projection index) for every projection shape of every
+    workload at its own token counts."""
+    out = []
+    for wl in wls.WORKLOADS.values():
+        for m in wl.ms:
+            for pi, p in enumerate(wl.projections):
+                out.append(pytest.param(wl.name, m, pi, id=f"{wl.name}-m{m}-{p.name}"))
+    return out
+
+
+@pytest.mark.parametrize("name,m,pi", workload_shapes())
+def test_forward_acc_with_oracle_codes(bl, name, m, pi):
+    """The contraction alone at every workload shape: the oracle's own codes
+    of the workload's activations against the GPU-packed, tiled weights; every
+    int32 accumulator bit-equal to the oracle's."""
+    wl = wls.WORKLOADS[name]
+    entries = packed_workload(bl, wl)
+    x = wls.activations(wl, pi, m, wls.variants(wl, m)[-1])
+    q_ref, _ = oracle.act_quant(x)
+    _, _, p_ref, _, tiled = entries[pi]
+    acc = bl.forward_acc(torch.from_numpy(q_ref).to(DEV), tiled)
+    assert np.array_equal(acc.cpu().numpy(), oracle.contract(q_ref, oracle.unpack(p_ref)))
+
+
+def tie_rows(m, k, seed):
+    """Rows whose codes are decided by round-half-to-even: absmax 127/64 (so
+    the scale is exactly 64) and values (2j+1)/128, which scale to j + 0.5."""
+    rng = np.random.default_rng(seed)
+    j = rng.integers(-63, 63, size=(m, k))
+    xf = ((2 * j + 1) / 128.0).astype(np.float32)
+    xf[np.arange(m), rng.integers(0, k, size=m)] = np.float32(127 / 64) * np.where(
+        rng.random(m) < 0.5, 1, -1).astype(np.float32)
+    return wls.to_bf16_bits(xf)
+
+
+# fused decode quantizer (M <= 4); decode rows staged by the activation kernel
+# (M = 8, 16); GEMM rows, a workgroup per row (M = 40) and a wave per row
+# (1100 rows); the general row path (K % 8 != 0; K past the register batch)
+@pytest.mark.parametrize("m,k", [(1, 2048), (4, 2048), (8, 2048), (16, 4096), (40, 1024),
+                                 (1100, 2560), (24, 1036), (20, 16400)])
+def test_forward_path_ties_round_to_even(bl, m, k):
+    """Ties through the forward path's own quantizers: every code, scale and
+    code sum equals the oracle's round-half-to-even result."""
+    x = tie_rows(m, k, 100 + m)
+    q_ref, s_ref = oracle.act_quant(x)
+    assert np.all(s_ref == np.float32(64.0))
+    frac = bf16_bits_to_f32(x) * np.float32(64.0)
+    ties = np.abs(frac - np.floor(frac)) == 0.5
+    assert ties.mean() > 0.9 and np.all(q_ref[ties] % 2 == 0)
+    _, w = wls.random_case(7, 1, 64, k)
+    p_ref, ws_ref = oracle.pack_weights(w)
+    packed, ws = bl.pack_weights(torch.from_numpy(w).to(DEV))
+    weights = bl.tile_weights(packed) if k % 256 == 0 else packed
+    ys, inss, status = bl.forward_grouped_inspect([dev_bf16(x)], [weights], [ws])
+    assert int(status.item()) == 0
+    check_inspection(f"ties M={m} K={k}", x, ys[0], inss[0], p_ref, ws_ref,
+                     oracle.forward(x, p_ref, ws_ref))
+
+
+def bf16_bits_to_f32(bits):
+    return (np.asarray(bits, np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def test_decode_wait_giveup_is_reported(bl):
+    """The decode kernel's waits between its waves are bounded.  Forced to
+    give up at once (wait_polls < 0, host-side), the split-shape launch must
+    report it in the status word and poison its outputs (NaN / INT32_MIN)
+    instead of returning numbers.  A following default call is exact again."""
+    wl = wls.WORKLOADS["decode_1b_m1"]
+    entries = packed_workload(bl, wl)
+    xs = [dev_bf16(wls.activations(wl, pi, 1)) for pi in range(len(wl.projections))]
+    packs, scales = [e[4] for e in entries], [e[1] for e in entries]
+    ys, inss, status = bl.forward_grouped_inspect(xs, packs, scales, wait_polls=-1)
+    assert int(status.item()) == 1
+    for y, ins in zip(ys, inss):
+        assert torch.all(y.view(torch.int16) == 0x7FC0), "outputs not poisoned"
+        assert torch.all(ins["acc"] == -2 ** 31)
+    ys2, _, status2 = bl.forward_grouped_inspect(xs, packs, scales)
+    assert int(status2.item()) == 0
+    for pi, y in enumerate(ys2):
+        x = wls.activations(wl, pi, 1)
+        assert_bf16_close(host_bits(y), oracle.forward(x, entries[pi][2], entries[pi][3]))
+
+
+def test_binding_rejects_bad_outputs_and_scales(bl):
+    """The binding checks caller-supplied outputs, scales and workspaces
+    before the library sees them (wrong shape, dtype or device)."""
+    x = torch.zeros((2, 256), dtype=torch.bfloat16, device=DEV)
+    packed = torch.zeros((32, 64), dtype=torch.uint8, device=DEV)
+    ws = torch.ones(1, dtype=torch.float32, device=DEV)
+    with pytest.raises(ValueError):
+        bl.forward(x, packed, ws, out=torch.empty((2, 31), dtype=torch.bfloat16, device=DEV))
+    with pytest.raises(TypeError):
+        bl.forward(x, packed, ws, out=torch.empty((2, 32), dtype=torch.float32, device=DEV))
+    with pytest.raises(TypeError):
+        bl.forward(x, packed, torch.ones(1, dtype=torch.float32))  # host scale
+    with pytest.raises(TypeError):
+        bl.forward(x, packed, torch.ones(0, dtype=torch.float32, device=DEV))
+    with pytest.raises(TypeError):
+        bl.forward(x, packed, ws, workspace=torch.empty(1 << 20, dtype=torch.uint8))
+    with pytest.raises(ValueError):
+        bl.forward_acc(torch.zeros((2, 256), dtype=torch.int8, device=DEV), packed,
+                       out=torch.empty((2, 32, 1), dtype=torch.int32, device=DEV))
+    with pytest.raises(ValueError):
+        bl.GroupedCall([x], [packed], [ws], outs=[torch.empty((3, 32), dtype=torch.bfloat16,
+                                                              device=DEV)])
+    # a workspace of 4-byte elements is counted in bytes
+    need = bl.forward_grouped_workspace_bytes(2, [(32, 256)])
+    wsp = torch.empty((need + 3) // 4, dtype=torch.int32, device=DEV)
+    y = bl.GroupedCall([x], [packed], [ws], workspace=wsp)()
+    torch.cuda.synchronize()
+    assert y[0].shape == (2, 32)
