@@ -7,10 +7,12 @@ this package; the product path never imports it.
 from .bitlinear_oracle import (  # noqa: F401
     absmean_exact,
     act_quant,
+    add_bf16,
     bf16_to_f32,
     contract,
     contract_loops,
     dequant,
+    export_bf16,
     f32_to_bf16,
     forward,
     forward_acc,

@@ -38,6 +38,12 @@ Steps (every function below cites the one it follows):
 5. dequantization y = acc / (input_scale * weight_scale) (``dequant``);
    [FE-ar] ``post_quant_process``, rounded to bfloat16 ("half precision" in
    the [FE-ko] prose under ``activation_norm_quant``).
+6. the optional bias, added to the dequantized output (``add_bf16`` in
+   ``forward``); [FE-ar] the last lines of ``BitLinear.forward``.  A residual
+   tensor, which the layer around BitLinear adds, goes in the same way after
+   it (a reading: the pages' code stops at the bias).
+7. the "universal" bf16 export u / scale (``export_bf16``); [FE-ar] the
+   ``state_dict`` loop after ``_weight_quant``.
 
 Readings where the pages leave a step open (each is also listed in the
 design notes of the repository):
@@ -60,6 +66,15 @@ R6  The contraction is exact integer arithmetic (int32 result), not a
 R7  Dequantization divides fp32(acc) by the fp32 product
     fp32(input_scale * weight_scale) (one correctly rounded division),
     then rounds to bfloat16 with round-to-nearest-even.
+R12 The bias and the residual are bf16 tensors, added to the bf16 output one
+    at a time as a bf16 tensor add does: both operands widened to fp32, one
+    fp32 add, the sum rounded to bf16 (round-to-nearest-even); bias first,
+    then residual.  The fp32 add of two bf16 values is exact whenever the
+    result can differ from one of them after the bf16 rounding, so this is
+    the exact sum rounded once to bf16.
+R13 The export computes u / scale as one correctly rounded fp32 division
+    and rounds the quotient to bf16 (the checkpoint the [FE-ar] text calls
+    the bfloat16 variant).
 R11 (a storage choice of this project, not a reading of the pages) The
     optional tiled layout (``tile`` / ``untile``) permutes the R5 bytes
     inside each block of 16 rows (N % 16 == 0, K % 256 == 0); it changes
@@ -340,10 +355,38 @@ def forward_acc(q: np.ndarray, packed: np.ndarray) -> np.ndarray:
     return contract(q, unpack(packed))
 
 
-def forward(x_bf16: np.ndarray, packed: np.ndarray, w_scale: np.float32) -> np.ndarray:
-    """[FE-ar] ``BitLinear.forward`` without bias: unpack the stored weights,
-    quantize the activations, contract, dequantize.  Returns bf16 bits."""
+def add_bf16(a_bits: np.ndarray, b_bits: np.ndarray) -> np.ndarray:
+    """a + b for bf16 tensors (broadcasting): both widened to fp32, one fp32
+    add, the sum rounded to bf16 (reading R12).  [FE-ar] the
+    ``y += self.bias`` line of ``BitLinear.forward``."""
+    s = bf16_to_f32(a_bits) + bf16_to_f32(b_bits)
+    return f32_to_bf16(s.astype(np.float32))
+
+
+def forward(x_bf16: np.ndarray, packed: np.ndarray, w_scale: np.float32,
+            bias: np.ndarray | None = None, residual: np.ndarray | None = None) -> np.ndarray:
+    """[FE-ar] ``BitLinear.forward``: unpack the stored weights, quantize the
+    activations, contract, dequantize, then add the bias (bf16 [N]) if one
+    is given; then the residual (bf16 [M, N]) if one is given (R12).
+    Returns bf16 bits."""
     u = unpack(packed)
     q, s = act_quant(x_bf16)
     acc = contract(q, u)
-    return dequant(acc, s, w_scale)
+    y = dequant(acc, s, w_scale)
+    if bias is not None:
+        y = add_bf16(y, np.asarray(bias, np.uint16)[None, :])
+    if residual is not None:
+        y = add_bf16(y, residual)
+    return y
+
+
+# --------------------------------------------------------------------------
+# Step 7: the "universal" bf16 export
+# --------------------------------------------------------------------------
+
+def export_bf16(packed: np.ndarray, w_scale: np.float32) -> np.ndarray:
+    """Dense bf16 weights u / scale from the packed codes: [N, K/4] bytes ->
+    [N, K] bf16 bits.  [FE-ar] the ``state_dict`` loop that follows
+    ``_weight_quant`` (``param_value / param_scale``); reading R13."""
+    u = unpack(packed).astype(np.float32)
+    return f32_to_bf16((u / np.float32(w_scale)).astype(np.float32))

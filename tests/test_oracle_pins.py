@@ -449,3 +449,118 @@ def test_dequant_divides_rather_than_multiplying_by_reciprocal():
     for j, v in enumerate(pick):
         yf = nearest_f32(Fraction(int(v)) / Fraction(float(dd)))
         assert y[0, j] == torch_bf16_bits(np.array([yf], np.float32))[0]
+
+
+# ---------------------------------------------------------------- bias and residual (R12)
+
+def nearest_bf16_bits(fr: Fraction) -> int:
+    """Brute force: the bf16 bit pattern nearest to the rational ``fr``, ties
+    to the even pattern (no fp32 step in between)."""
+    if fr == 0:
+        return 0
+    sign = 0x8000 if fr < 0 else 0
+    a = abs(fr)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    q = Fraction(2) ** (max(e, -126) - 7)  # bf16 spacing: 8 significant bits
+    lo = (a / q).numerator // (a / q).denominator
+    cands = [lo, lo + 1]
+
+    def bits(mant):
+        v = float(mant * q)
+        return int(torch_bf16_bits(np.array([v], np.float32))[0])  # exact: 8-bit mantissa
+
+    best = min(cands, key=lambda c: (abs(c * q - a), bits(c) & 1))
+    return sign | bits(best)
+
+
+def test_add_bf16_hand_cases():
+    # 0.7578125 + 0.5 = 1.2578125 = 1 + 2^-2 + 2^-7, exactly a bf16 (0x3FA1)
+    assert oracle.add_bf16(np.array([0x3F42], np.uint16), np.array([0x3F00], np.uint16)).tolist() == [0x3FA1]
+    # 1 + 2^-8 lies half way between 1 (0x3F80) and 1 + 2^-7: ties to even -> 1
+    assert oracle.add_bf16(np.array([0x3F80], np.uint16), np.array([0x3B80], np.uint16)).tolist() == [0x3F80]
+    # (1 + 2^-7) + 2^-8: half way between 0x3F81 and 0x3F82 -> the even 0x3F82
+    assert oracle.add_bf16(np.array([0x3F81], np.uint16), np.array([0x3B80], np.uint16)).tolist() == [0x3F82]
+    # x + (-x) is +0 under round-to-nearest
+    assert oracle.add_bf16(np.array([0x3F80], np.uint16), np.array([0xBF80], np.uint16)).tolist() == [0x0000]
+
+
+def test_add_bf16_is_the_exact_sum_rounded_once():
+    rng = np.random.default_rng(77)
+    a = rng.integers(0, 0x10000, size=3000).astype(np.uint16)
+    b = rng.integers(0, 0x10000, size=3000).astype(np.uint16)
+    # close exponents (sums that cancel or carry) as well as distant ones
+    b[:1000] = (a[:1000] ^ 0x8000) + rng.integers(-3, 4, size=1000).astype(np.uint16)
+    fa, fb = oracle.bf16_to_f32(a), oracle.bf16_to_f32(b)
+    ok = np.isfinite(fa) & np.isfinite(fb) & (np.abs(fa) < 1e38) & (np.abs(fb) < 1e38)
+    ok &= (np.abs(fa) > 1e-37) | (fa == 0)
+    ok &= (np.abs(fb) > 1e-37) | (fb == 0)
+    got = oracle.add_bf16(a[ok], b[ok])
+    for x, y, g in zip(fa[ok], fb[ok], got):
+        want = nearest_bf16_bits(Fraction(float(x)) + Fraction(float(y)))
+        if want == 0x8000:
+            want = 0  # an exact zero sum is +0
+        assert int(g) == want, (x, y)
+
+
+def test_add_bf16_matches_torch_bf16_add():
+    rng = np.random.default_rng(78)
+    a = torch_bf16_bits(rng.standard_normal(5000).astype(np.float32) * 3)
+    b = torch_bf16_bits(rng.standard_normal(5000).astype(np.float32))
+    ta = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16)
+    tb = torch.from_numpy(b.view(np.int16)).view(torch.bfloat16)
+    want = (ta + tb).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(oracle.add_bf16(a, b), want)
+
+
+def test_forward_bias_and_residual_hand_example():
+    # the worked example (y = 96/127 -> 0x3F42), then bias 0.5 -> 1.2578125
+    # (0x3FA1), then residual -1.25 -> 2^-7 (0x3C00); the bias broadcasts
+    # over token rows and is added before the residual
+    x = torch_bf16_bits(np.array([[1.0, -0.5, 0.25, 0.0], [1.0, -0.5, 0.25, 0.0]], np.float32))
+    w = np.array([[0.5, -1.5, 1.0, 1.0]], np.float32)
+    packed, ws = oracle.pack_weights(w)
+    assert oracle.forward(x, packed, ws).tolist() == [[0x3F42], [0x3F42]]
+    bias = np.array([0x3F00], np.uint16)
+    assert oracle.forward(x, packed, ws, bias=bias).tolist() == [[0x3FA1], [0x3FA1]]
+    res = torch_bf16_bits(np.array([[-1.25], [0.0]], np.float32))
+    assert oracle.forward(x, packed, ws, bias=bias, residual=res).tolist() == [[0x3C00], [0x3FA1]]
+    # residual alone
+    assert oracle.forward(x, packed, ws, residual=res).tolist() == [
+        [int(torch_bf16_bits(np.array([0.7578125 - 1.25], np.float32))[0])], [0x3F42]]
+
+
+def test_forward_adds_bias_before_residual():
+    # x = [1, 2^-7, 0, 0] -> scale 127, q = [127, 1, 0, 0]; w = 1 everywhere ->
+    # w_scale 1, u = 1; acc = 128 and 128/127 = 1.00787 rounds to the bf16
+    # 1 + 2^-7 (0x3F81).  Bias 2^-8 then residual -2^-8: 1 + 2^-7 + 2^-8 is a
+    # tie that goes to the even 1 + 2^-6 (0x3F82), and 1 + 2^-6 - 2^-8 is a
+    # tie that stays at 0x3F82.  The other order would give 1 (0x3F80).
+    x = torch_bf16_bits(np.array([[1.0, 2.0 ** -7, 0.0, 0.0]], np.float32))
+    packed, ws = oracle.pack_weights(np.ones((1, 4), np.float32))
+    assert oracle.forward(x, packed, ws).tolist() == [[0x3F81]]
+    y = oracle.forward(x, packed, ws, bias=np.array([0x3B80], np.uint16),
+                       residual=np.array([[0xBB80]], np.uint16))
+    assert y.tolist() == [[0x3F82]]
+
+
+# ---------------------------------------------------------------- bf16 export (R13)
+
+def test_export_hand_example_and_torch_division():
+    # w = [0.5, -1.5, 1, 1] -> w_scale 1, u = [0, -1, 1, 1] -> bf16 [0, -1, 1, 1]
+    packed, ws = oracle.pack_weights(np.array([[0.5, -1.5, 1.0, 1.0]], np.float32))
+    assert oracle.export_bf16(packed, ws).tolist() == [[0x0000, 0xBF80, 0x3F80, 0x3F80]]
+    # scale 3: 1/3 in fp32 is 0x3EAAAAAB, which rounds up to the bf16 0x3EAB;
+    # code 3 (value +2) exports as 2/3
+    packed = np.array([[0b11100100]], np.uint8)  # codes 0, 1, 2, 3 -> u = -1, 0, 1, 2
+    assert oracle.export_bf16(packed, np.float32(3.0)).tolist() == [[0xBEAB, 0x0000, 0x3EAB, 0x3F2B]]
+    # against torch's fp32 division and bf16 cast on a workload tensor
+    wl = wls.WORKLOADS["layer_8b"]
+    w = wls.weights(wl, 1)[:64]
+    packed, ws = oracle.pack_weights(w)
+    u = torch.from_numpy(oracle.unpack(packed).astype(np.float32))
+    want = (u / torch.tensor(ws, dtype=torch.float32)).to(torch.bfloat16)
+    assert np.array_equal(oracle.export_bf16(packed, ws), want.view(torch.int16).numpy().view(np.uint16))
