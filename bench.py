@@ -331,16 +331,19 @@ def warm_cache(torch, bl, wls, name, m, args, dev):
     return wl.packed_bytes / float(np.median(per_step)) / 1e9
 
 
-def native_bf16(torch, wls, name, m, dev, min_seconds=0.2):
-    """Context: the same layer as dense bf16 weights through torch.matmul
-    (the vendor BLAS), weights rotated like the ternary step; the bytes a
-    bf16 model streams per step and the time it takes."""
+def native_bf16(torch, bl, wls, name, m, dev, min_seconds=0.2):
+    """Context: the same layer as dense bf16 weights -- the library's
+    "universal" export u / w_scale of the packed weights -- through
+    torch.matmul (the vendor BLAS), weights rotated like the ternary step;
+    the bytes a bf16 model streams per step and the time it takes."""
     wl = wls.WORKLOADS[name]
     wbytes = sum(2 * p.n * p.k for p in wl.projections)
     copies = max(1, int(math.ceil((1 << 30) / wbytes))) if not is_prefill(m) else 1
     g = torch.Generator(device="cpu").manual_seed(3)
-    ws = [[(torch.randn(p.k, p.n, generator=g) * 0.02).to(torch.bfloat16).to(dev)
-           for p in wl.projections] for _ in range(1)]
+    packed, scales = packed_weights(torch, bl, wls, wl, dev, True)
+    # [K, N] operands, so that x @ w needs no transposed view
+    ws = [[bl.export_bf16(p, s, k=pr.k).t().contiguous()
+           for p, s, pr in zip(packed, scales, wl.projections)]]
     for _ in range(copies - 1):
         ws.append([w.clone() for w in ws[0]])
     xs = [torch.randn(m, p.k, generator=g).to(torch.bfloat16).to(dev) for p in wl.projections]
@@ -706,13 +709,14 @@ def main():
         for n, m in (("layer_8b", 1), ("decode_1b_m1", 1), ("prefill_2b_m2048", 2048),
                      ("layer_8b", 512)):
             try:
-                ctx["native_bf16"].append(native_bf16(torch, wls, n, m, dev))
+                ctx["native_bf16"].append(native_bf16(torch, bl, wls, n, m, dev))
             except Exception as e:  # context only: never fail the run for it
                 ctx["native_bf16"].append({"workload": n, "m": m,
                                            "unavailable": f"{type(e).__name__}: {e}"[:200]})
-        ctx["native_bf16_note"] = ("the same layers as dense bf16 weights through torch.matmul "
-                                   "(vendor BLAS), random weights, rotated like the ternary "
-                                   "steps; compare ms_per_step with the configs array")
+        ctx["native_bf16_note"] = ("the same layers as dense bf16 weights (the library's bf16 "
+                                   "export of the packed weights) through torch.matmul (vendor "
+                                   "BLAS), rotated like the ternary steps; compare ms_per_step "
+                                   "with the configs array")
         peaks = measured_ceilings(torch, dev)
         peaks["headline_frac_of_stream_read"] = h["value"] / peaks["stream_read_GBs"]
         for r in rows:

@@ -30,7 +30,8 @@ _i64, _i32, _sz, _vp = ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t, ctypes.c
 class Projection(ctypes.Structure):
     """bl_projection: one projection of a grouped forward call."""
     _fields_ = [("x", _vp), ("packed", _vp), ("w_scale", _vp), ("y", _vp),
-                ("n", _i64), ("k", _i64), ("layout", _i32), ("reserved", _i32)]
+                ("n", _i64), ("k", _i64), ("layout", _i32), ("reserved", _i32),
+                ("bias", _vp), ("residual", _vp)]
 
 
 class Inspect(ctypes.Structure):
@@ -49,6 +50,10 @@ _SIGS = {
     "bitlinear_pack_workspace_bytes": (_sz, [_i64, _i64]),
     "bitlinear_pack_weights": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp, _vp, _sz, _vp]),
     "bitlinear_unpack_weights": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp]),
+    "bitlinear_export_bf16": (ctypes.c_int, [_vp, _i64, _i64, _i32, _vp, _vp, _vp]),
+    "bitlinear_forward_latent_workspace_bytes": (_sz, [_i64, _i64, _i64]),
+    "bitlinear_forward_latent": (ctypes.c_int, [_i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _sz,
+                                                _vp]),
     "bitlinear_tile_weights": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp]),
     "bitlinear_untile_weights": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp]),
     "bitlinear_act_quant": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp, _vp]),
@@ -172,6 +177,41 @@ def unpack_weights(packed: torch.Tensor) -> torch.Tensor:
     return u
 
 
+def export_bf16(packed: torch.Tensor, w_scale: torch.Tensor, k: int | None = None) -> torch.Tensor:
+    """The "universal" bf16 weights u / w_scale, [N, K] bf16, from packed
+    weights in either layout (K is inferred for the row-major layout; give it
+    for the tiled one, where [N/16, 4K] is ambiguous with row-major)."""
+    _require(packed, torch.uint8, 2, "packed")
+    _require_scale(w_scale, packed.device)
+    if k is None:
+        k = 4 * packed.shape[1]
+    n, layout = weight_layout(packed, k)
+    out = torch.empty((n, k), dtype=torch.bfloat16, device=packed.device)
+    _check(_lib.bitlinear_export_bf16(_ptr(packed), n, k, layout, _ptr(w_scale), _ptr(out),
+                                      _stream(packed)))
+    return out
+
+
+def forward_latent(x: torch.Tensor, w: torch.Tensor, out: torch.Tensor | None = None):
+    """The forward pass on latent fp32 weights [N, K], ternarized on the fly
+    (exact absmean, then block-wise packing, then the forward).  Returns
+    (y bf16 [M, N], w_scale fp32 [1])."""
+    _require(x, torch.bfloat16, 2, "x")
+    _require(w, torch.float32, 2, "w", device=x.device)
+    m, k = x.shape
+    n = w.shape[0]
+    if w.shape[1] != k:
+        raise ValueError("w must be [N, K] with K = x.shape[1]")
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.bfloat16, device=x.device)
+    _require(out, torch.bfloat16, 2, "out", shape=(m, n), device=x.device)
+    w_scale = torch.empty(4, dtype=torch.float32, device=x.device)[:1]
+    ws = _workspace(int(_lib.bitlinear_forward_latent_workspace_bytes(m, n, k)), x.device, None)
+    _check(_lib.bitlinear_forward_latent(m, n, k, _ptr(x), _ptr(w), _ptr(w_scale), _ptr(out),
+                                         _ptr(ws), _nbytes(ws), _stream(x)))
+    return out, w_scale
+
+
 def tile_weights(packed: torch.Tensor) -> torch.Tensor:
     """Row-major packed [N, K/4] -> the 16-row tiled layout, as uint8
     [N/16, 4*K] (one row per block of 16 weight rows).  N % 16 == 0 and
@@ -222,8 +262,15 @@ def forward_workspace_bytes(m: int, n: int, k: int) -> int:
 
 
 def forward(x: torch.Tensor, packed: torch.Tensor, w_scale: torch.Tensor,
-            out: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
-    """y = BitLinear(x) as bf16 [M, N]; `packed` in either layout."""
+            out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+            bias: torch.Tensor | None = None, residual: torch.Tensor | None = None):
+    """y = BitLinear(x) as bf16 [M, N]; `packed` in either layout.  With a bf16
+    bias [N] and/or a bf16 residual [M, N] (which may be `out` itself), the
+    output is (y + bias) + residual, each add rounded to bf16."""
+    if bias is not None or residual is not None:
+        outs = None if out is None else [out]
+        return GroupedCall([x], [packed], [w_scale], outs, workspace,
+                           biases=[bias], residuals=[residual])()[0]
     _require(x, torch.bfloat16, 2, "x")
     _require(packed, torch.uint8, 2, "packed", device=x.device)
     _require_scale(w_scale, x.device)
@@ -239,12 +286,16 @@ def forward(x: torch.Tensor, packed: torch.Tensor, w_scale: torch.Tensor,
     return out
 
 
-def _projections(xs, packeds, w_scales, outs):
+def _projections(xs, packeds, w_scales, outs, biases=None, residuals=None):
     arr = (Projection * len(xs))()
-    for i, (x, p, s, y) in enumerate(zip(xs, packeds, w_scales, outs)):
+    biases = biases or [None] * len(xs)
+    residuals = residuals or [None] * len(xs)
+    for i, (x, p, s, y, b, r) in enumerate(zip(xs, packeds, w_scales, outs, biases, residuals)):
         n, layout = weight_layout(p, x.shape[1])
         arr[i] = Projection(x.data_ptr(), p.data_ptr(), s.data_ptr(), y.data_ptr(),
-                            n, x.shape[1], layout, 0)
+                            n, x.shape[1], layout, 0,
+                            b.data_ptr() if b is not None else 0,
+                            r.data_ptr() if r is not None else 0)
     return arr
 
 
@@ -265,9 +316,12 @@ def forward_grouped_launches(m: int, shapes: Sequence[tuple]) -> int:
 
 class GroupedCall:
     """A prepared grouped forward: descriptors and workspace built once, so
-    repeated calls only enqueue the two kernels."""
+    repeated calls only enqueue the kernels.  Optional per projection: a
+    bf16 bias [N] and a bf16 residual [M, N] (may be that projection's
+    output, for an in-place add)."""
 
-    def __init__(self, xs, packeds, w_scales, outs=None, workspace=None):
+    def __init__(self, xs, packeds, w_scales, outs=None, workspace=None, biases=None,
+                 residuals=None):
         if not (len(xs) == len(packeds) == len(w_scales)) or not xs:
             raise ValueError("xs, packeds and w_scales must be non-empty lists of one length")
         m = xs[0].shape[0]
@@ -287,10 +341,19 @@ class GroupedCall:
         for x, p, y in zip(xs, packeds, outs):
             _require(y, torch.bfloat16, 2, "out", shape=(m, weight_layout(p, x.shape[1])[0]),
                      device=dev)
+        for lst, what in ((biases, "biases"), (residuals, "residuals")):
+            if lst is not None and len(lst) != len(xs):
+                raise ValueError(f"{what}: one entry (or None) per projection")
+        for i, (x, p) in enumerate(zip(xs, packeds)):
+            n = weight_layout(p, x.shape[1])[0]
+            if biases is not None and biases[i] is not None:
+                _require(biases[i], torch.bfloat16, 1, "bias", shape=(n,), device=dev)
+            if residuals is not None and residuals[i] is not None:
+                _require(residuals[i], torch.bfloat16, 2, "residual", shape=(m, n), device=dev)
         self.m = m
         self.outs = outs
-        self._keep = (list(xs), list(packeds), list(w_scales), outs)
-        self._arr = _projections(xs, packeds, w_scales, outs)
+        self._keep = (list(xs), list(packeds), list(w_scales), outs, biases, residuals)
+        self._arr = _projections(xs, packeds, w_scales, outs, biases, residuals)
         need = int(_lib.bitlinear_forward_grouped_workspace_bytes(len(xs), self._arr, m))
         self.workspace = _workspace(need, xs[0].device, workspace)
         self._dev = xs[0]
@@ -351,18 +414,25 @@ def forward_acc(q: torch.Tensor, packed: torch.Tensor, out: torch.Tensor | None 
 
 
 class BitLinear:
-    """Inference-time BitLinear layer (no bias): packs fp32 latent weights
-    once, then runs the forward pass on bf16 activations.  The weights are
-    kept in the tiled layout when the shape allows it (N % 16 == 0,
-    K % 256 == 0) unless tiled=False; `packed` holds them in that layout."""
+    """Inference-time BitLinear layer: packs fp32 latent weights once, then
+    runs the forward pass on bf16 activations, adding the bf16 bias if one is
+    given (as nn.Linear's).  The weights are kept in the tiled layout when the
+    shape allows it (N % 16 == 0, K % 256 == 0) unless tiled=False; `packed`
+    holds them in that layout."""
 
-    def __init__(self, weight: torch.Tensor, tiled: bool = True):
+    def __init__(self, weight: torch.Tensor, bias: torch.Tensor | None = None,
+                 tiled: bool = True):
         self.out_features, self.in_features = weight.shape
         self.packed, self.w_scale = pack_weights(weight.contiguous())
         if tiled and self.out_features % 16 == 0 and self.in_features % 256 == 0:
             self.packed = tile_weights(self.packed)
+        self.bias = None if bias is None else bias.to(torch.bfloat16).contiguous()
 
-    def __call__(self, x: torch.Tensor) -> torch.Tensor:
+    def __call__(self, x: torch.Tensor, residual: torch.Tensor | None = None) -> torch.Tensor:
+        """y = BitLinear(x) (+ bias); with `residual` (same shape as y), y +
+        residual, added in the same pass."""
         lead = x.shape[:-1]
-        y = forward(x.reshape(-1, self.in_features).contiguous(), self.packed, self.w_scale)
+        res = None if residual is None else residual.reshape(-1, self.out_features).contiguous()
+        y = forward(x.reshape(-1, self.in_features).contiguous(), self.packed, self.w_scale,
+                    bias=self.bias, residual=res)
         return y.reshape(*lead, self.out_features)

@@ -153,6 +153,8 @@ struct ProjIO {
   int8_t* ins_q;
   float* ins_xs;
   int32_t* ins_qs;
+  const uint16_t* bias;  // [n] bf16, or nullptr
+  const uint16_t* res;   // [m][n] bf16, or nullptr
 };
 
 // Diagnostics of a call: the decode kernel's wait bound and status word.
@@ -242,6 +244,8 @@ bl_status run_forward(int32_t count, const ProjIO* io, int64_t m, void* workspac
       P.n = (int32_t)ns[i];
       P.k = (int32_t)ks[i];
       P.ldq = (int32_t)round_up(ks[i], kKPad);
+      da.epi[i].bias = io[i].bias;
+      da.epi[i].res = io[i].res;
       P.wk = pl.wk;
       P.tww = pl.tww;
       P.kspw = pl.kspw;
@@ -287,6 +291,8 @@ bl_status run_forward(int32_t count, const ProjIO* io, int64_t m, void* workspac
       P.kspw = L.pf_kspw[i];
       P.part = P.ksplit > 1 ? reinterpret_cast<int32_t*>(ws + L.pf_part_off[i]) : nullptr;
       P.tiled = io[i].tiled;
+      P.bias = io[i].bias;
+      P.res = io[i].res;
     }
     // The last tile columns of the last projection become narrow tiles when
     // that evens out the launch's last round of workgroups.
@@ -308,6 +314,8 @@ bl_status run_forward(int32_t count, const ProjIO* io, int64_t m, void* workspac
         T.packed = W.packed + (int64_t)keep * (W.k / 4);
         T.y = W.y ? W.y + keep : nullptr;
         T.acc_out = W.acc_out ? W.acc_out + keep : nullptr;
+        T.bias = W.bias ? W.bias + keep : nullptr;
+        T.res = W.res ? W.res + keep : nullptr;
         T.n = W.n - keep;
         T.tiles_n = (T.n + kPrefillNarrowBN - 1) / kPrefillNarrowBN;
         T.narrow = 1;
@@ -384,7 +392,7 @@ const char* bitlinear_status_string(bl_status s) {
   return "unknown status";
 }
 
-int bitlinear_abi_version(void) { return 3; }
+int bitlinear_abi_version(void) { return 4; }
 
 size_t bitlinear_pack_workspace_bytes(int64_t n, int64_t k) {
   (void)n;
@@ -404,6 +412,22 @@ bl_status bitlinear_pack_weights(const float* w, int64_t n, int64_t k, uint8_t* 
   if (!aligned16(workspace)) return BL_EALIGN;
   if (launch_pack(w, n, k, packed, w_scale, static_cast<unsigned long long*>(workspace),
                   static_cast<hipStream_t>(stream)) != hipSuccess)
+    return BL_EHIP;
+  return BL_OK;
+}
+
+bl_status bitlinear_export_bf16(const uint8_t* packed, int64_t n, int64_t k, int32_t layout,
+                                const float* w_scale, uint16_t* out, void* stream) {
+  bl_status st;
+  if ((st = check_shape(1, n, k)) != BL_OK) return st;
+  if (n * k >= kMaxElems) return BL_ESHAPE;
+  if (layout != BL_LAYOUT_ROWS && layout != BL_LAYOUT_TILED) return BL_EINVAL;
+  if (layout == BL_LAYOUT_TILED && (st = check_tiled_shape(n, k)) != BL_OK) return st;
+  if ((st = check_ptr(packed)) != BL_OK || (st = check_ptr(w_scale)) != BL_OK ||
+      (st = check_ptr(out)) != BL_OK)
+    return st;
+  if (launch_export_bf16(packed, n, k, layout == BL_LAYOUT_TILED, w_scale, out,
+                         static_cast<hipStream_t>(stream)) != hipSuccess)
     return BL_EHIP;
   return BL_OK;
 }
@@ -470,7 +494,8 @@ static bl_status forward_one(int64_t m, int64_t n, int64_t k, const uint16_t* x,
   if ((st = check_ptr(x)) != BL_OK || (st = check_ptr(packed)) != BL_OK ||
       (st = check_ptr(w_scale)) != BL_OK || (st = check_ptr(y)) != BL_OK)
     return st;
-  ProjIO io = {x, nullptr, packed, w_scale, y, nullptr, n, k, tiled, nullptr, nullptr, nullptr};
+  ProjIO io = {x, nullptr, packed, w_scale, y, nullptr, n, k, tiled,
+               nullptr, nullptr, nullptr, nullptr, nullptr};
   return run_forward(1, &io, m, workspace, workspace_bytes, static_cast<hipStream_t>(stream));
 }
 
@@ -512,9 +537,16 @@ static bl_status grouped_io(int32_t count, const bl_projection* projs, int64_t m
     if ((st = check_ptr(p.x)) != BL_OK || (st = check_ptr(p.packed)) != BL_OK ||
         (st = check_ptr(p.w_scale)) != BL_OK || (st = check_ptr(p.y)) != BL_OK)
       return st;
+    if ((p.bias && !aligned16(p.bias)) || (p.residual && !aligned16(p.residual))) return BL_EALIGN;
+    if (p.residual && p.residual != p.y) {  // in place, or apart
+      const uintptr_t a = reinterpret_cast<uintptr_t>(p.residual);
+      const uintptr_t b = reinterpret_cast<uintptr_t>(p.y);
+      const uintptr_t bytes = (uintptr_t)(m * p.n) * 2;
+      if (a < b + bytes && b < a + bytes) return BL_EINVAL;
+    }
     io[i] = ProjIO{p.x,     nullptr, p.packed, p.w_scale, p.y,    nullptr,
                    p.n,     p.k,     p.layout == BL_LAYOUT_TILED ? 1 : 0,   nullptr, nullptr,
-                   nullptr};
+                   nullptr, p.bias,  p.residual};
   }
   return BL_OK;
 }
@@ -595,6 +627,55 @@ bl_status bitlinear_forward_grouped_inspect(int32_t count, const bl_projection* 
                      diag);
 }
 
+// Workspace of bitlinear_forward_latent: the absmean buckets, the weight
+// scale, the packed weights, then a forward call's workspace.
+struct LatentLayout {
+  size_t scale, packed, fwd, total;
+};
+
+static LatentLayout latent_layout(int64_t m, int64_t n, int64_t k) {
+  LatentLayout L;
+  L.scale = align256(kPackWorkspace);
+  L.packed = align256(L.scale + sizeof(float));
+  L.fwd = align256(L.packed + (size_t)n * (size_t)(k / 4));
+  Layout F;
+  make_layout(1, &n, &k, m, false, F);
+  L.total = L.fwd + F.total;
+  return L;
+}
+
+size_t bitlinear_forward_latent_workspace_bytes(int64_t m, int64_t n, int64_t k) {
+  if (check_shape(m, n, k) != BL_OK || n * k >= kMaxElems) return 0;
+  return latent_layout(m, n, k).total;
+}
+
+bl_status bitlinear_forward_latent(int64_t m, int64_t n, int64_t k, const uint16_t* x,
+                                   const float* w, float* w_scale, uint16_t* y, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  bl_status st;
+  if ((st = check_shape(m, n, k)) != BL_OK) return st;
+  if (n * k >= kMaxElems) return BL_ESHAPE;
+  if ((st = check_ptr(x)) != BL_OK || (st = check_ptr(w)) != BL_OK || (st = check_ptr(y)) != BL_OK)
+    return st;
+  if (w_scale && !aligned16(w_scale)) return BL_EALIGN;
+  const LatentLayout L = latent_layout(m, n, k);
+  if (!workspace) return BL_EWORKSPACE;
+  if (!aligned16(workspace)) return BL_EALIGN;
+  if (workspace_bytes < L.total) return BL_EWORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  float* scale = w_scale ? w_scale : reinterpret_cast<float*>(ws + L.scale);
+  uint8_t* packed = reinterpret_cast<uint8_t*>(ws + L.packed);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  // stage 1: the exact global absmean; stage 2: block-wise ternarization and
+  // packing; then the forward pass on the packed weights
+  if (launch_pack(w, n, k, packed, scale, reinterpret_cast<unsigned long long*>(ws), s) !=
+      hipSuccess)
+    return BL_EHIP;
+  ProjIO io = {x, nullptr, packed, scale, y, nullptr, n, k, 0,
+               nullptr, nullptr, nullptr, nullptr, nullptr};
+  return run_forward(1, &io, m, ws + L.fwd, workspace_bytes - L.fwd, s);
+}
+
 static bl_status forward_acc_one(int64_t m, int64_t n, int64_t k, const int8_t* q,
                                  const uint8_t* packed, int32_t* acc, void* workspace,
                                  size_t workspace_bytes, void* stream, int tiled) {
@@ -604,7 +685,8 @@ static bl_status forward_acc_one(int64_t m, int64_t n, int64_t k, const int8_t* 
   if ((st = check_ptr(q)) != BL_OK || (st = check_ptr(packed)) != BL_OK ||
       (st = check_ptr(acc)) != BL_OK)
     return st;
-  ProjIO io = {nullptr, q, packed, nullptr, nullptr, acc, n, k, tiled, nullptr, nullptr, nullptr};
+  ProjIO io = {nullptr, q, packed, nullptr, nullptr, acc, n, k, tiled,
+               nullptr, nullptr, nullptr, nullptr, nullptr};
   return run_forward(1, &io, m, workspace, workspace_bytes, static_cast<hipStream_t>(stream));
 }
 

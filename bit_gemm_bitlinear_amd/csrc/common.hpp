@@ -138,6 +138,19 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2){lo, hi}, b2));
 }
 
+// bf16 a + b the way a bf16 tensor add rounds (the bias line of
+// BitLinear.forward): both widened to fp32, one fp32 add, the sum rounded to
+// bf16 (round to nearest even).
+__device__ __forceinline__ uint16_t add_bf16(uint16_t a, uint16_t b) {
+  return f32_to_bf16(bf16_to_f32(a) + bf16_to_f32(b));
+}
+
+// The same for two pairs held in dwords (bf16 in bits 0-15 and 16-31).
+__device__ __forceinline__ uint32_t add_bf16x2(uint32_t a, uint32_t b) {
+  return pack_bf16x2(bf16_to_f32(a & 0xFFFFu) + bf16_to_f32(b & 0xFFFFu),
+                     __uint_as_float(a & 0xFFFF0000u) + __uint_as_float(b & 0xFFFF0000u));
+}
+
 // Largest magnitude pattern of four bf16 values held in two dwords; the
 // bit pattern of |x| orders like |x| for finite values.
 __device__ __forceinline__ uint32_t absmax_bits4(uint32_t lo, uint32_t hi) {

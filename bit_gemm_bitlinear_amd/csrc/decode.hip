@@ -85,7 +85,7 @@ __device__ __forceinline__ v4i load_w16(const uint8_t* __restrict__ row, int off
 // descriptor words are broadcast with readlane.  (Indexing the argument
 // struct by a computed projection index would cost a second, dependent
 // round trip before any weight load could be issued.)
-__device__ __forceinline__ DecodeProj select_proj(int count, int* wl) {
+__device__ __forceinline__ DecodeProj select_proj(int count, int* wl, int* proj) {
   const char* kp = (const char*)__builtin_amdgcn_kernarg_segment_ptr();
   const DecodeArgs* ka = reinterpret_cast<const DecodeArgs*>(kp);
   const int j = threadIdx.x & 15;
@@ -109,6 +109,7 @@ __device__ __forceinline__ DecodeProj select_proj(int count, int* wl) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) dst[4 * i + c] = __builtin_amdgcn_readlane(words[i][c], pi);
   *wl = b - __builtin_amdgcn_readlane(beg, pi);
+  *proj = pi;
   return P;
 }
 
@@ -200,17 +201,25 @@ __device__ __forceinline__ void lds_post(int32_t* c) {
   if ((threadIdx.x & 63) == 0) __hip_atomic_fetch_add(c, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
-// Writes one output: bf16, or the int32 accumulator (forward_acc); with INS
-// (inspection) both where both are set.  A workgroup whose wait gave up
+// Writes one output: bf16, or the int32 accumulator (forward_acc).  With EPI
+// (a separate kernel instance for the extra epilogue work) the bf16 output
+// gets the bias and then the residual added (BitLinear.forward's bias line,
+// each add rounded to bf16), and int32 accumulators are written next to it
+// where both are asked for (inspection).  A workgroup whose wait gave up
 // (`bad`) writes NaN / INT32_MIN.
-template <bool INS>
-__device__ __forceinline__ void store_out(const DecodeProj& P, int m, int n, int32_t acc,
-                                          const Shared& sh, bool bad) {
-  if (P.y)
-    *G(P.y + (int64_t)m * P.n + n) =
-        bad ? (uint16_t)0x7FC0u : dequant_bf16_row(acc - sh.qs[m], sh.rd[m]);
-  if ((INS || !P.y) && P.acc_out)
-    *G(P.acc_out + (int64_t)m * P.n + n) = bad ? (int32_t)0x80000000u : acc - sh.qs[m];
+template <bool EPI>
+__device__ __forceinline__ void store_out(const DecodeProj& P, const DecodeEpi& E, int m, int n,
+                                          int32_t acc, const Shared& sh, bool bad) {
+  const int64_t o = (int64_t)m * P.n + n;
+  if (P.y) {
+    uint16_t v = bad ? (uint16_t)0x7FC0u : dequant_bf16_row(acc - sh.qs[m], sh.rd[m]);
+    if constexpr (EPI) {
+      if (E.bias) v = add_bf16(v, *G(E.bias + n));
+      if (E.res) v = add_bf16(v, *G(E.res + o));
+    }
+    *G(P.y + o) = v;
+  }
+  if ((EPI || !P.y) && P.acc_out) *G(P.acc_out + o) = bad ? (int32_t)0x80000000u : acc - sh.qs[m];
 }
 
 // Stores the 16 codes of group g (dword a, byte b = code 4b + a of the group)
@@ -452,10 +461,12 @@ __device__ __forceinline__ void mma_chunk(v4i& acc1, v4i& acc4, const v4i (&a)[4
 
 // EARLY (ring shape, several token rows): the first weight loads go out
 // before the code preparation instead of after it.
-// INS: inspection outputs are written (a separate kernel instance).
-template <int TWW, int MODE, bool FUSED, bool SPLIT, bool EARLY, bool INS>
-__device__ __forceinline__ void decode_body(const DecodeArgs& A, const DecodeProj& P, int wl,
-                                            int8_t* __restrict__ lds, Shared& sh) {
+// EPI: the extra epilogue work (inspection outputs, bias, residual) is
+// compiled in (a separate kernel instance).
+template <int TWW, int MODE, bool FUSED, bool SPLIT, bool EARLY, bool EPI>
+__device__ __forceinline__ void decode_body(const DecodeArgs& A, const DecodeProj& P,
+                                            const DecodeEpi& E, int wl, int8_t* __restrict__ lds,
+                                            Shared& sh) {
   constexpr int NT = SPLIT ? 512 : 256;
   const int M = A.m;
   const int tid = threadIdx.x;
@@ -478,7 +489,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& A, const DecodePro
   const int nw = min(ns, ws0 + nsw) - ws0;  // slabs of this wave (may be 0)
   const int rowbytes = P.k >> 2;
   const int lrow = A.lds_row;
-  const bool inspect = INS && FUSED && wl == 0;  // one workgroup writes the inspection outputs
+  const bool inspect = EPI && FUSED && wl == 0;  // one workgroup writes the inspection outputs
   bool bad = false;                       // split shape: a wait of this wave gave up
 
   // weights: this wave streams its TWW row tiles over its K slabs, slab-major
@@ -626,7 +637,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& A, const DecodePro
 
   // inspection: the code sums of the fused quantization (final once the codes
   // are posted, which every streaming wave has waited for)
-  if (INS && FUSED && inspect && P.qsum && tid < M) *G(P.qsum + tid) = sh.qs[tid];
+  if (EPI && FUSED && inspect && P.qsum && tid < M) *G(P.qsum + tid) = sh.qs[tid];
 
   // epilogue.  Streaming lane (ln, lg) holds rows m = 4*lg + r of output
   // column row0 + 16*t + ln.
@@ -638,7 +649,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& A, const DecodePro
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int m = 4 * lg + r;
-        if (m < M && n < P.n) store_out<INS>(P, m, n, acc[t][r], sh, bad);
+        if (m < M && n < P.n) store_out<EPI>(P, E, m, n, acc[t][r], sh, bad);
       }
     }
     return;
@@ -673,7 +684,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& A, const DecodePro
     for (int q = 0; q < P.wk; ++q) v += red[(((g * P.wk + q) * TWW + t) * M + m) * 16 + c];
     if (n >= P.n) continue;
     if (P.ksplit == 1)
-      store_out<INS>(P, m, n, v, sh, bad);
+      store_out<EPI>(P, E, m, n, v, sh, bad);
     else
       atomicAdd(P.part + (int64_t)m * P.n + n, v);
   }
@@ -709,26 +720,27 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& A, const DecodePro
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      if (base + NT * i < nout && outn[i] < P.n) store_out<INS>(P, outm[i], outn[i], vals[i], sh, bad);
+      if (base + NT * i < nout && outn[i] < P.n)
+        store_out<EPI>(P, E, outm[i], outn[i], vals[i], sh, bad);
   }
 }
 
-template <int TWW, int MODE, bool SPLIT, bool EARLY, bool INS>
-__device__ __forceinline__ void decode_tw(const DecodeArgs& A, const DecodeProj& P, int wl,
-                                          int8_t* lds, Shared& sh) {
+template <int TWW, int MODE, bool SPLIT, bool EARLY, bool EPI>
+__device__ __forceinline__ void decode_tw(const DecodeArgs& A, const DecodeProj& P,
+                                          const DecodeEpi& E, int wl, int8_t* lds, Shared& sh) {
   if constexpr (MODE == 0) {
     if (P.x) {
-      decode_body<TWW, MODE, true, SPLIT, EARLY, INS>(A, P, wl, lds, sh);
+      decode_body<TWW, MODE, true, SPLIT, EARLY, EPI>(A, P, E, wl, lds, sh);
       return;
     }
   }
-  decode_body<TWW, MODE, false, SPLIT, EARLY, INS>(A, P, wl, lds, sh);
+  decode_body<TWW, MODE, false, SPLIT, EARLY, EPI>(A, P, E, wl, lds, sh);
 }
 
 // SPLIT: 8 waves, for launches that fit on the chip in one wave of WGs (the
 // activation work of a WG then overlaps its weight stream instead of
 // preceding it); otherwise 4 waves, so that several WGs share a CU.
-template <int MODE, bool SPLIT, bool EARLY, bool INS>
+template <int MODE, bool SPLIT, bool EARLY, bool EPI>
 __global__ __launch_bounds__(SPLIT ? 512 : 256) void decode_kernel(const DecodeArgs A) {
   extern __shared__ __align__(16) int8_t lds[];
   __shared__ Shared sh;
@@ -739,15 +751,17 @@ __global__ __launch_bounds__(SPLIT ? 512 : 256) void decode_kernel(const DecodeA
       sh.bad = 0;
     }
   }
-  int wl;
-  const DecodeProj P = select_proj(A.count, &wl);
+  int wl, pi;
+  const DecodeProj P = select_proj(A.count, &wl, &pi);
+  DecodeEpi E = {nullptr, nullptr};
+  if constexpr (EPI) E = A.epi[pi];
   switch (P.tww) {
-    case 1: decode_tw<1, MODE, SPLIT, EARLY, INS>(A, P, wl, lds, sh); break;
-    case 2: decode_tw<2, MODE, SPLIT, EARLY, INS>(A, P, wl, lds, sh); break;
+    case 1: decode_tw<1, MODE, SPLIT, EARLY, EPI>(A, P, E, wl, lds, sh); break;
+    case 2: decode_tw<2, MODE, SPLIT, EARLY, EPI>(A, P, E, wl, lds, sh); break;
     case 3:  // split-shape plans only, with the K range unsplit (wk = 1)
-      if constexpr (SPLIT) decode_tw<3, MODE, SPLIT, EARLY, INS>(A, P, wl, lds, sh);
+      if constexpr (SPLIT) decode_tw<3, MODE, SPLIT, EARLY, EPI>(A, P, E, wl, lds, sh);
       break;
-    default: decode_tw<4, MODE, SPLIT, EARLY, INS>(A, P, wl, lds, sh); break;
+    default: decode_tw<4, MODE, SPLIT, EARLY, EPI>(A, P, E, wl, lds, sh); break;
   }
 }
 
@@ -885,38 +899,39 @@ hipError_t allow_lds(size_t bytes) {
   return e;
 }
 
-template <bool INS>
+template <bool EPI>
 hipError_t launch_decode_as(const DecodeArgs& a, int total_wgs, size_t lds_bytes, hipStream_t s) {
   const bool split = a.load_mode == 0 && total_wgs <= device_cu_count();
   const dim3 grid((unsigned)total_wgs);
   hipError_t e = hipSuccess;
   if (split) {
-    e = allow_lds<&decode_kernel<0, true, false, INS>>(lds_bytes);
-    if (e == hipSuccess) decode_kernel<0, true, false, INS><<<grid, 512, lds_bytes, s>>>(a);
+    e = allow_lds<&decode_kernel<0, true, false, EPI>>(lds_bytes);
+    if (e == hipSuccess) decode_kernel<0, true, false, EPI><<<grid, 512, lds_bytes, s>>>(a);
   } else if (a.load_mode == 0 && a.m > 1) {
-    e = allow_lds<&decode_kernel<0, false, true, INS>>(lds_bytes);
-    if (e == hipSuccess) decode_kernel<0, false, true, INS><<<grid, 256, lds_bytes, s>>>(a);
+    e = allow_lds<&decode_kernel<0, false, true, EPI>>(lds_bytes);
+    if (e == hipSuccess) decode_kernel<0, false, true, EPI><<<grid, 256, lds_bytes, s>>>(a);
   } else if (a.load_mode == 0) {
-    e = allow_lds<&decode_kernel<0, false, false, INS>>(lds_bytes);
-    if (e == hipSuccess) decode_kernel<0, false, false, INS><<<grid, 256, lds_bytes, s>>>(a);
+    e = allow_lds<&decode_kernel<0, false, false, EPI>>(lds_bytes);
+    if (e == hipSuccess) decode_kernel<0, false, false, EPI><<<grid, 256, lds_bytes, s>>>(a);
   } else if (a.load_mode == 1) {
-    e = allow_lds<&decode_kernel<1, false, false, INS>>(lds_bytes);
-    if (e == hipSuccess) decode_kernel<1, false, false, INS><<<grid, 256, lds_bytes, s>>>(a);
+    e = allow_lds<&decode_kernel<1, false, false, EPI>>(lds_bytes);
+    if (e == hipSuccess) decode_kernel<1, false, false, EPI><<<grid, 256, lds_bytes, s>>>(a);
   } else {
-    e = allow_lds<&decode_kernel<2, false, false, INS>>(lds_bytes);
-    if (e == hipSuccess) decode_kernel<2, false, false, INS><<<grid, 256, lds_bytes, s>>>(a);
+    e = allow_lds<&decode_kernel<2, false, false, EPI>>(lds_bytes);
+    if (e == hipSuccess) decode_kernel<2, false, false, EPI><<<grid, 256, lds_bytes, s>>>(a);
   }
   if (e != hipSuccess) return e;
   return hipGetLastError();
 }
 
 hipError_t launch_decode(const DecodeArgs& a, int total_wgs, size_t lds_bytes, hipStream_t s) {
-  // inspection: int32 accumulators next to bf16 outputs, or the fused
-  // quantization's codes, scales or code sums asked for
+  // extra epilogue work: int32 accumulators next to bf16 outputs, the fused
+  // quantization's codes, scales or code sums, a bias or a residual
   bool ins = false;
   for (int i = 0; i < a.count; ++i) {
     const DecodeProj& P = a.p[i];
-    ins = ins || (P.y && P.acc_out) || (P.x && (P.q || P.x_scale || P.qsum));
+    ins = ins || (P.y && P.acc_out) || (P.x && (P.q || P.x_scale || P.qsum)) || a.epi[i].bias ||
+          a.epi[i].res;
   }
   return ins ? launch_decode_as<true>(a, total_wgs, lds_bytes, s)
              : launch_decode_as<false>(a, total_wgs, lds_bytes, s);

@@ -95,9 +95,17 @@ struct DecodeProj {
   int32_t tiled;       // 1: weights in the 16-row tiled layout (common.hpp)
 };
 
+// Epilogue additions of a projection, kept apart from DecodeProj so that the
+// descriptor every workgroup fetches first stays at seven 16-byte words.
+struct DecodeEpi {
+  const uint16_t* bias;  // [n] bf16 added to y, or nullptr
+  const uint16_t* res;   // [m][n] bf16 added to y after the bias (may be y itself), or nullptr
+};
+
 struct DecodeArgs {
   int32_t wg_begin[kMaxProj];  // first WG of each projection
   DecodeProj p[kMaxProj];
+  DecodeEpi epi[kMaxProj];
   int32_t count;
   int32_t m;
   int32_t load_mode;  // 0: 16-byte rows, 1: 4-byte rows, 2: byte rows
@@ -155,6 +163,8 @@ struct PrefillProj {
   int32_t ksplit, kspw;
   int32_t* part;
   int32_t tiled;        // 1: weights in the 16-row tiled layout (common.hpp)
+  const uint16_t* bias; // [n] bf16 added to y (this entry's columns), or nullptr
+  const uint16_t* res;  // [m][ldy] bf16 added to y after the bias (may be y), or nullptr
 };
 
 struct PrefillArgs {
@@ -184,6 +194,9 @@ hipError_t launch_prefill_finish(const PrefillArgs& a, int total_pieces, hipStre
 hipError_t launch_pack(const float* w, int64_t n, int64_t k, uint8_t* packed, float* w_scale,
                        unsigned long long* buckets, hipStream_t s);
 hipError_t launch_unpack(const uint8_t* packed, int64_t n, int64_t k, int8_t* u, hipStream_t s);
+// bf16 u / w_scale [n][k] from packed weights in either layout.
+hipError_t launch_export_bf16(const uint8_t* packed, int64_t n, int64_t k, bool tiled,
+                              const float* w_scale, uint16_t* out, hipStream_t s);
 // Row-major packed weights <-> the 16-row tiled layout (n % 16 == 0,
 // k % 256 == 0); `untile` runs the inverse permutation.
 hipError_t launch_tile(const uint8_t* src, int64_t n, int64_t k, uint8_t* dst, bool untile,

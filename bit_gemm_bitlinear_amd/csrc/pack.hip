@@ -119,6 +119,58 @@ __global__ __launch_bounds__(256) void tile_kernel(const uint8_t* __restrict__ s
   }
 }
 
+// The "universal" bf16 export: u / w_scale for every weight (the blog's
+// state_dict loop after _weight_quant), from the packed codes.  The four
+// possible values (codes 0..3, u = -1, 0, 1, 2) are one fp32 division each,
+// rounded to bf16, computed once per thread.  Thread work: one 16-byte chunk
+// of a packed row (64 weights) in either layout -> 128 bytes of row-major
+// bf16 output.
+__global__ __launch_bounds__(256) void export_bf16_kernel(const uint8_t* __restrict__ packed,
+                                                          int64_t chunks, int64_t rowbytes,
+                                                          int tiled, const float* __restrict__ w_scale,
+                                                          uint16_t* __restrict__ out) {
+  const float s = load_f32_vmem(w_scale);
+  uint32_t lut[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) lut[c] = f32_to_bf16((float)(c - 1) / s);
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const int64_t cpr = rowbytes >> 4;  // chunks per row
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < chunks; i += stride) {
+    const int64_t row = i / cpr, o = 16 * (i - row * cpr);
+    const int64_t src = tiled ? tiled_chunk_offset(row, o, rowbytes) : row * rowbytes + o;
+    const v4i p = *G(reinterpret_cast<const v4i*>(packed + src));
+    v4i* dst = reinterpret_cast<v4i*>(out + row * (rowbytes * 4) + 4 * o);
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {  // dword d: weights 16d .. 16d+15
+      const uint32_t w = (uint32_t)p[d];
+      uint32_t h[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t c0 = (w >> (4 * j)) & 3u, c1 = (w >> (4 * j + 2)) & 3u;
+        h[j] = lut[c0] | (lut[c1] << 16);
+      }
+      *G(dst + 2 * d) = v4i{(int32_t)h[0], (int32_t)h[1], (int32_t)h[2], (int32_t)h[3]};
+      *G(dst + 2 * d + 1) = v4i{(int32_t)h[4], (int32_t)h[5], (int32_t)h[6], (int32_t)h[7]};
+    }
+  }
+}
+
+// Rows whose packed length is not a multiple of 16 (K % 64 != 0, row-major
+// only): one packed byte per thread.
+__global__ __launch_bounds__(256) void export_bf16_bytes_kernel(const uint8_t* __restrict__ packed,
+                                                                int64_t nbytes,
+                                                                const float* __restrict__ w_scale,
+                                                                uint16_t* __restrict__ out) {
+  const float s = load_f32_vmem(w_scale);
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nbytes; b += stride) {
+    // row-major: byte b of the flattened [n][k/4] array holds weights 4b..4b+3
+    const uint32_t w = packed[b];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) out[4 * b + j] = f32_to_bf16((float)((int)((w >> (2 * j)) & 3u) - 1) / s);
+  }
+}
+
 int grid_for(int64_t work, int per_block, int cap) {
   int64_t g = (work + per_block - 1) / per_block;
   if (g < 1) g = 1;
@@ -145,6 +197,20 @@ hipError_t launch_tile(const uint8_t* src, int64_t n, int64_t k, uint8_t* dst, b
   const int64_t chunks = n * k / 64;
   tile_kernel<<<grid_for(chunks, 256 * 4, 8192), 256, 0, s>>>(src, chunks, k / 4, dst,
                                                               untile ? 1 : 0);
+  return hipGetLastError();
+}
+
+hipError_t launch_export_bf16(const uint8_t* packed, int64_t n, int64_t k, bool tiled,
+                              const float* w_scale, uint16_t* out, hipStream_t s) {
+  const int64_t rowbytes = k / 4;
+  if (rowbytes % 16 == 0) {  // whole 16-byte chunks (always so in the tiled layout)
+    const int64_t chunks = n * (rowbytes / 16);
+    export_bf16_kernel<<<grid_for(chunks, 256 * 2, 8192), 256, 0, s>>>(packed, chunks, rowbytes,
+                                                                       tiled ? 1 : 0, w_scale, out);
+  } else {  // other row lengths (row-major only): byte by byte
+    export_bf16_bytes_kernel<<<grid_for(n * rowbytes, 256 * 4, 8192), 256, 0, s>>>(
+        packed, n * rowbytes, w_scale, out);
+  }
   return hipGetLastError();
 }
 

@@ -233,7 +233,12 @@ __global__ __launch_bounds__(kThreads) void prefill_reg_kernel(const PrefillArgs
         const int n = ncol0 + 32 * f + lj;
         if (n >= P.n) continue;
         const int32_t v = acc[i][f][r] - qs;
-        if (P.y) *G(P.y + (int64_t)m * P.ldy + n) = dequant_bf16_row(v, rd);
+        if (P.y) {
+          uint16_t yb = dequant_bf16_row(v, rd);
+          if (P.bias) yb = add_bf16(yb, *G(P.bias + n));
+          if (P.res) yb = add_bf16(yb, *G(P.res + (int64_t)m * P.ldy + n));
+          *G(P.y + (int64_t)m * P.ldy + n) = yb;
+        }
         if (P.acc_out) *G(P.acc_out + (int64_t)m * P.ldy + n) = v;
       }
     }
@@ -364,9 +369,11 @@ struct Stager {
 // the tile and its own columns, so every weight column is expanded once per
 // workgroup; with WMI = 2 two waves share (and both expand) each column.
 // One output tile (BM rows x BNT columns) of projection P.
-// INS: int32 accumulators are written next to the bf16 outputs where a
-// projection asks for both (inspection; a separate kernel instance).
-template <int BNT, int NST, int WMI, int NW, int BK, bool INS>
+// EPI: the extra epilogue work (a separate kernel instance) -- the bias and
+// then the residual added to the bf16 outputs (BitLinear.forward's bias
+// line, each add rounded to bf16), and int32 accumulators written next to
+// the bf16 outputs where a projection asks for both (inspection).
+template <int BNT, int NST, int WMI, int NW, int BK, bool EPI>
 __device__ __forceinline__ void prefill_tile(const PrefillArgs& A, const PrefillProj& P, int tm, int tn,
                                              int kp, int8_t* __restrict__ smem) {
   using K = Cfg<BNT, WMI, NW, BK>;
@@ -467,7 +474,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& A, const Prefill
     const bool row_ok = m < A.m;
     // int32 sums: the output (forward_acc, or inspection next to the bf16
     // output), or a K part's partial sums
-    if (!bf || P.ksplit > 1 || (INS && P.acc_out)) {
+    if (!bf || P.ksplit > 1 || (EPI && P.acc_out)) {
       const int ld = P.ksplit > 1 ? P.n : P.ldy;
       const bool wide = (ld & 3) == 0;  // rows are 16-byte aligned
       int32_t* yrow = (P.ksplit > 1 ? P.part + (int64_t)kp * A.m * P.n : P.acc_out) + (int64_t)m * ld;
@@ -484,7 +491,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& A, const Prefill
             for (int e = 0; e < 4 && n + e < P.n; ++e) *G(yrow + n + e) = v[e];
           }
         }
-      if constexpr (INS) {
+      if constexpr (EPI) {
         if (!bf || P.ksplit > 1) continue;
       } else {
         continue;
@@ -524,11 +531,30 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& A, const Prefill
       for (int h = 0; h < 2; ++h) {
         const int n = n0 + wn0 + 32 * f + 16 * h + 8 * lg;
         if (!row_ok || n >= P.n) continue;
-        const uint32_t* w = pk + 4 * h;
+        uint32_t w[4] = {pk[4 * h], pk[4 * h + 1], pk[4 * h + 2], pk[4 * h + 3]};
         if (wide && n + 8 <= P.n) {
+          if constexpr (EPI) {
+            if (P.bias) {
+              const v4i b = *G(reinterpret_cast<const v4i*>(P.bias + n));
+#pragma unroll
+              for (int j = 0; j < 4; ++j) w[j] = add_bf16x2(w[j], (uint32_t)b[j]);
+            }
+            if (P.res) {
+              const v4i r = *G(reinterpret_cast<const v4i*>(P.res + (int64_t)m * P.ldy + n));
+#pragma unroll
+              for (int j = 0; j < 4; ++j) w[j] = add_bf16x2(w[j], (uint32_t)r[j]);
+            }
+          }
           *G(reinterpret_cast<v4i*>(yrow + n)) = v4i{(int32_t)w[0], (int32_t)w[1], (int32_t)w[2], (int32_t)w[3]};
         } else {
-          for (int e = 0; e < 8 && n + e < P.n; ++e) *G(yrow + n + e) = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+          for (int e = 0; e < 8 && n + e < P.n; ++e) {
+            uint16_t v = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+            if constexpr (EPI) {
+              if (P.bias) v = add_bf16(v, *G(P.bias + n + e));
+              if (P.res) v = add_bf16(v, *G(P.res + (int64_t)m * P.ldy + n + e));
+            }
+            *G(yrow + n + e) = v;
+          }
         }
       }
     }
@@ -539,7 +565,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& A, const Prefill
 // entries marked narrow: the host gives the tiles that would otherwise run
 // in a last, partly filled round of workgroups that width, so that the
 // round fills the chip and ends sooner.
-template <int NST, int WMI, int NW, int BK, bool INS>
+template <int NST, int WMI, int NW, int BK, bool EPI>
 __global__ __launch_bounds__(64 * NW)
 __attribute__((amdgpu_waves_per_eu(NW * kPrefillWgsPerCu / 4))) void prefill_kernel(const PrefillArgs A) {
   extern __shared__ __align__(16) int8_t smem[];
@@ -553,9 +579,9 @@ __attribute__((amdgpu_waves_per_eu(NW * kPrefillWgsPerCu / 4))) void prefill_ker
   const int kp = tn / P.tiles_n;
   tn -= kp * P.tiles_n;
   if (P.narrow)
-    prefill_tile<kPrefillNarrowBN, NST, WMI, NW, BK, INS>(A, P, tm, tn, kp, smem);
+    prefill_tile<kPrefillNarrowBN, NST, WMI, NW, BK, EPI>(A, P, tm, tn, kp, smem);
   else
-    prefill_tile<kPrefillBN, NST, WMI, NW, BK, INS>(A, P, tm, tn, kp, smem);
+    prefill_tile<kPrefillBN, NST, WMI, NW, BK, EPI>(A, P, tm, tn, kp, smem);
 }
 
 // Adds the K parts of the split projections.  Piece i of a projection is 8
@@ -607,11 +633,24 @@ __global__ __launch_bounds__(kThreads) void prefill_finish_kernel(const PrefillA
   for (int e = 0; e < 8; ++e) yf[e] = d.fast ? row_div_fast((float)v[e], d.d, d.y) : (float)v[e] / d.d;
   uint16_t* dst = P.y + (int64_t)m * P.ldy + n;
   if ((P.ldy & 7) == 0 && whole) {
-    *G(reinterpret_cast<v4i*>(dst)) =
-        v4i{(int32_t)pack_bf16x2(yf[0], yf[1]), (int32_t)pack_bf16x2(yf[2], yf[3]),
-            (int32_t)pack_bf16x2(yf[4], yf[5]), (int32_t)pack_bf16x2(yf[6], yf[7])};
+    uint32_t w[4] = {pack_bf16x2(yf[0], yf[1]), pack_bf16x2(yf[2], yf[3]),
+                     pack_bf16x2(yf[4], yf[5]), pack_bf16x2(yf[6], yf[7])};
+    if (P.bias) {
+      const v4i b = *G(reinterpret_cast<const v4i*>(P.bias + n));
+      for (int j = 0; j < 4; ++j) w[j] = add_bf16x2(w[j], (uint32_t)b[j]);
+    }
+    if (P.res) {
+      const v4i r = *G(reinterpret_cast<const v4i*>(P.res + (int64_t)m * P.ldy + n));
+      for (int j = 0; j < 4; ++j) w[j] = add_bf16x2(w[j], (uint32_t)r[j]);
+    }
+    *G(reinterpret_cast<v4i*>(dst)) = v4i{(int32_t)w[0], (int32_t)w[1], (int32_t)w[2], (int32_t)w[3]};
   } else {
-    for (int e = 0; e < 8 && n + e < P.n; ++e) *G(dst + e) = f32_to_bf16(yf[e]);
+    for (int e = 0; e < 8 && n + e < P.n; ++e) {
+      uint16_t v = f32_to_bf16(yf[e]);
+      if (P.bias) v = add_bf16(v, *G(P.bias + n + e));
+      if (P.res) v = add_bf16(v, *G(P.res + (int64_t)m * P.ldy + n + e));
+      *G(dst + e) = v;
+    }
   }
 }
 
@@ -641,8 +680,9 @@ hipError_t launch_prefill(const PrefillArgs& a, int total_tiles, hipStream_t s) 
                   NW = BL_PREFILL_NW, BK = BL_PREFILL_BK;
     static_assert(BNT >= kPrefillNarrowBN, "the wide tiles' slab buffers hold the narrow ones'");
     constexpr size_t lds = (size_t)NST * Cfg<BNT, WMI, NW, BK>::kStageBytes;
-    bool ins = false;
-    for (int i = 0; i < a.count; ++i) ins = ins || (a.p[i].y && a.p[i].acc_out);
+    bool ins = false;  // extra epilogue work: inspection, bias or residual
+    for (int i = 0; i < a.count; ++i)
+      ins = ins || (a.p[i].y && a.p[i].acc_out) || a.p[i].bias || a.p[i].res;
     auto go = [&](auto insc) -> hipError_t {
       constexpr bool I = decltype(insc)::value;
       if (lds > 64 * 1024) {  // the attribute is needed above 64 KB; once per device

@@ -79,16 +79,25 @@ typedef enum {
   BL_EHIP = 5        /* a kernel launch failed */
 } bl_status;
 
-/* One projection of a grouped forward call (host-side descriptor). */
+/* One projection of a grouped forward call (host-side descriptor).
+ * Optional epilogue (BitLinear.forward's bias line, and the residual add of
+ * the block around the layer): the bf16 output of the dequantization gets
+ * bias[n] added, then residual[m][n]; each add is one fp32 addition of the
+ * two bf16 values rounded to bf16 (round to nearest even), as a bf16 tensor
+ * add.  NULL skips the step. */
 typedef struct {
-  const uint16_t *x;      /* [M][K] bf16 activations (device) */
-  const uint8_t *packed;  /* [N][K/4] packed ternary weights (device) */
-  const float *w_scale;   /* 1 float, the weight scale (device) */
-  uint16_t *y;            /* [M][N] bf16 output (device) */
-  int64_t n;              /* N, output features */
-  int64_t k;              /* K, input features */
-  int32_t layout;         /* BL_LAYOUT_ROWS (0) or BL_LAYOUT_TILED (1) */
-  int32_t reserved;       /* must be 0 */
+  const uint16_t *x;        /* [M][K] bf16 activations (device) */
+  const uint8_t *packed;    /* [N][K/4] packed ternary weights (device) */
+  const float *w_scale;     /* 1 float, the weight scale (device) */
+  uint16_t *y;              /* [M][N] bf16 output (device) */
+  int64_t n;                /* N, output features */
+  int64_t k;                /* K, input features */
+  int32_t layout;           /* BL_LAYOUT_ROWS (0) or BL_LAYOUT_TILED (1) */
+  int32_t reserved;         /* must be 0 */
+  const uint16_t *bias;     /* [N] bf16 bias (device, 16-byte aligned), or NULL */
+  const uint16_t *residual; /* [M][N] bf16 (device, 16-byte aligned), or NULL; may be
+                               y itself (an in-place residual add), must not
+                               otherwise overlap y */
 } bl_projection;
 
 /* Weight layouts (bl_projection.layout). */
@@ -117,6 +126,15 @@ bl_status bitlinear_pack_weights(const float *w, int64_t n, int64_t k,
                                  uint8_t *packed, float *w_scale,
                                  void *workspace, size_t workspace_bytes,
                                  void *stream);
+
+/* The "universal" bf16 export (the blog's state_dict loop after
+ * _weight_quant): out[n][k] = bf16(u[n][k] / w_scale), one correctly rounded
+ * fp32 division rounded to bf16, from packed weights in either layout
+ * (layout: BL_LAYOUT_ROWS or BL_LAYOUT_TILED; tiled needs N % 16 == 0 and
+ * K % 256 == 0).  out: [N][K] bf16, row-major (written).  One kernel. */
+bl_status bitlinear_export_bf16(const uint8_t *packed, int64_t n, int64_t k,
+                                int32_t layout, const float *w_scale,
+                                uint16_t *out, void *stream);
 
 /* Expand packed weights to int8 values c - 1: [N][K/4] -> [N][K].
  * (The blog's unpack_weights; used to inspect stored weights.) */
@@ -161,6 +179,23 @@ bl_status bitlinear_forward(int64_t m, int64_t n, int64_t k,
                             const float *w_scale, uint16_t *y,
                             void *workspace, size_t workspace_bytes,
                             void *stream);
+
+/* Bytes of workspace bitlinear_forward_latent needs for this shape. */
+size_t bitlinear_forward_latent_workspace_bytes(int64_t m, int64_t n, int64_t k);
+
+/* The forward pass on latent fp32 weights, ternarized on the fly (the
+ * blog's two-stage approach for its training kernels: a global reduction
+ * first, then block-wise quantization): the exact absmean of w [N][K] fp32,
+ * then ternarization and packing into the workspace, then
+ * bitlinear_forward on them.  Results are identical to
+ * bitlinear_pack_weights followed by bitlinear_forward.  w_scale: 1 float
+ * (device, written) or NULL (kept in the workspace).  workspace: at least
+ * bitlinear_forward_latent_workspace_bytes(m, n, k) bytes.  Enqueues the
+ * four packing kernels, then the forward's. */
+bl_status bitlinear_forward_latent(int64_t m, int64_t n, int64_t k,
+                                   const uint16_t *x, const float *w,
+                                   float *w_scale, uint16_t *y, void *workspace,
+                                   size_t workspace_bytes, void *stream);
 
 /* bitlinear_forward with the weights in the tiled layout (N % 16 == 0,
  * K % 256 == 0, else BL_ESHAPE).  Workspace:

@@ -45,7 +45,7 @@ def declared_functions():
 
 def test_exports_every_declared_function(bl):
     names = declared_functions()
-    assert len(names) == 18
+    assert len(names) == 21
     lib = bl.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -88,7 +88,7 @@ def test_probe_library_exports_and_validation():
 
 def test_status_strings_and_version(bl):
     lib = bl.lib()
-    assert lib.bitlinear_abi_version() == 3
+    assert lib.bitlinear_abi_version() == 4
     for s in range(6):
         assert lib.bitlinear_status_string(s)
     assert lib.bitlinear_status_string(99) == b"unknown status"
@@ -167,7 +167,7 @@ def test_tiled_layout_validation(bl):
     assert lib.bitlinear_forward_grouped(1, arr, 1, A16[0], 1 << 30, None) == 2  # N % 16
     arr[0].n, arr[0].k = 64, 320
     assert lib.bitlinear_forward_grouped(1, arr, 1, A16[0], 1 << 30, None) == 2  # K % 256
-    assert ctypes.sizeof(Proj) == 56
+    assert ctypes.sizeof(Proj) == 72
 
 
 def test_grouped_validation_and_sizes(bl):

@@ -552,3 +552,127 @@ def test_binding_rejects_bad_outputs_and_scales(bl):
     y = bl.GroupedCall([x], [packed], [ws], workspace=wsp)()
     torch.cuda.synchronize()
     assert y[0].shape == (2, 32)
+
+
+# ------------------------------------------------------------------ bias and residual
+
+def rand_bf16(seed, shape, scale=1.0):
+    rng = np.random.default_rng(seed)
+    return wls.to_bf16_bits(rng.standard_normal(shape).astype(np.float32) * np.float32(scale))
+
+
+# decode: fused quantization (M <= 4), staged codes (M = 8), K split across
+# workgroups (M = 16, K = 9216); prefill: one tile, K split across
+# workgroups (the finishing pass), ragged N; rows not 16-byte aligned
+# (K % 64 != 0: the register-staged prefill kernel and narrow decode loads)
+BIAS_SHAPES = [(1, 2048, 2048), (4, 96, 4096), (8, 300, 1024), (16, 640, 9216), (40, 200, 1024),
+               (256, 301, 16384), (300, 264, 2560), (3, 100, 1036), (70, 136, 1036)]
+
+
+@pytest.mark.parametrize("m,n,k", BIAS_SHAPES)
+def test_forward_bias_residual_parity(bl, m, n, k):
+    """BitLinear.forward's bias line (and a residual add after it) in the
+    epilogue: (bf16(y) + bias) + residual, each add rounded to bf16, exactly
+    as the oracle computes it; also with the residual in place (it is y)."""
+    x, w = wls.random_case(50, m, n, k, scale=2.0)
+    bias = rand_bf16(51 + m, (n,), 0.5)
+    res = rand_bf16(52 + m, (m, n))
+    p_ref, ws_ref = oracle.pack_weights(w)
+    packed, ws = bl.pack_weights(torch.from_numpy(w).to(DEV))
+    dx, db, dr = dev_bf16(x), dev_bf16(bias), dev_bf16(res)
+    y = bl.forward(dx, packed, ws, bias=db)
+    assert_bf16_close(host_bits(y), oracle.forward(x, p_ref, ws_ref, bias=bias), f"bias {m}x{n}x{k}")
+    y = bl.forward(dx, packed, ws, residual=dr)
+    assert_bf16_close(host_bits(y), oracle.forward(x, p_ref, ws_ref, residual=res), f"res {m}x{n}x{k}")
+    want = oracle.forward(x, p_ref, ws_ref, bias=bias, residual=res)
+    y = bl.forward(dx, packed, ws, bias=db, residual=dr)
+    assert_bf16_close(host_bits(y), want, f"bias+res {m}x{n}x{k}")
+    inplace = dr.clone()  # y += BitLinear(x): the residual buffer is the output
+    bl.forward(dx, packed, ws, bias=db, residual=inplace, out=inplace)
+    assert_bf16_close(host_bits(inplace), want, f"in place {m}x{n}x{k}")
+    if n % 16 == 0 and k % 256 == 0:
+        y = bl.forward(dx, bl.tile_weights(packed), ws, bias=db, residual=dr)
+        assert_bf16_close(host_bits(y), want, f"tiled bias+res {m}x{n}x{k}")
+
+
+@pytest.mark.parametrize("name,m", [("decode_1b_m1", 1), ("decode_3b", 16),
+                                    ("prefill_2b_m2048", 2048)])
+def test_grouped_bias_residual_workload(bl, name, m):
+    """Bias and residual on every projection of a workload in one grouped
+    call (the decode kernel's split and ring shapes, the GEMM with its
+    narrow tail)."""
+    wl = wls.WORKLOADS[name]
+    entries = packed_workload(bl, wl)
+    xs = [wls.activations(wl, pi, m) for pi in range(len(wl.projections))]
+    biases = [rand_bf16(60 + pi, (p.n,), 0.25) for pi, p in enumerate(wl.projections)]
+    ress = [rand_bf16(70 + pi, (m, p.n)) for pi, p in enumerate(wl.projections)]
+    call = bl.GroupedCall([dev_bf16(x) for x in xs], [e[4] for e in entries], [e[1] for e in entries],
+                          biases=[dev_bf16(b) for b in biases], residuals=[dev_bf16(r) for r in ress])
+    ys = call()
+    for pi, (x, y, e) in enumerate(zip(xs, ys, entries)):
+        want = oracle.forward(x, e[2], e[3], bias=biases[pi], residual=ress[pi])
+        assert_bf16_close(host_bits(y), want, f"{name} {wl.projections[pi].name} bias+res")
+
+
+def test_grouped_narrow_tail_bias(bl):
+    """A grouped GEMM launch whose last projection runs partly as narrow
+    tiles: the bias and residual of those columns are offset with them."""
+    m, shapes = NARROW_LAYERS[0]
+    xs, ps, ss, bs, rs, refs = [], [], [], [], [], []
+    for i, (n, k) in enumerate(shapes):
+        x, w = wls.random_case(190 + i, m, n, k)
+        p, s = bl.pack_weights(torch.from_numpy(w).to(DEV))
+        b, r = rand_bf16(200 + i, (n,)), rand_bf16(210 + i, (m, n))
+        xs.append(dev_bf16(x))
+        ps.append(p)
+        ss.append(s)
+        bs.append(dev_bf16(b))
+        rs.append(dev_bf16(r))
+        refs.append(oracle.forward(x, *oracle.pack_weights(w), bias=b, residual=r))
+    ys = bl.GroupedCall(xs, ps, ss, biases=bs, residuals=rs)()
+    for (n, k), y, ref in zip(shapes, ys, refs):
+        assert_bf16_close(host_bits(y), ref, f"narrow tail {m}x{n}x{k} bias+res")
+
+
+# ------------------------------------------------------------------ bf16 export
+
+@pytest.mark.parametrize("n,k", [(1, 4), (16, 256), (33, 260), (64, 1088), (2048, 2048), (48, 14336)])
+def test_export_bf16_parity(bl, n, k):
+    """u / w_scale as bf16 from the packed codes (code 3 included), both
+    layouts, against the oracle's export."""
+    rng = np.random.default_rng(n + 3 * k)
+    packed = rng.integers(0, 256, size=(n, k // 4), dtype=np.int16).astype(np.uint8)
+    s = np.float32(rng.random() * 50 + 0.5)
+    ds = torch.tensor([s], dtype=torch.float32, device=DEV)
+    out = bl.export_bf16(torch.from_numpy(packed).to(DEV), ds)
+    want = oracle.export_bf16(packed, s)
+    assert np.array_equal(host_bits(out), want)
+    if n % 16 == 0 and k % 256 == 0:
+        out_t = bl.export_bf16(torch.from_numpy(oracle.tile(packed)).to(DEV), ds, k=k)
+        assert np.array_equal(host_bits(out_t), want)
+
+
+def test_export_bf16_of_a_workload_projection(bl):
+    """The export of GPU-packed workload weights equals the oracle's export of
+    the oracle's packing."""
+    wl = wls.WORKLOADS["layer_8b"]
+    entries = packed_workload(bl, wl)
+    p, s, p_ref, s_ref, t = entries[1]
+    out = bl.export_bf16(t, s, k=wl.projections[1].k)
+    assert np.array_equal(host_bits(out), oracle.export_bf16(p_ref, s_ref))
+
+
+# ------------------------------------------------------------------ on-the-fly ternarization
+
+@pytest.mark.parametrize("m,n,k", [(1, 2048, 2048), (4, 100, 260), (16, 640, 9216), (40, 200, 1024),
+                                   (300, 257, 2560)])
+def test_forward_latent_parity(bl, m, n, k):
+    """The forward pass on latent fp32 weights (exact absmean, then
+    ternarization and packing, then the forward) equals the oracle's
+    pack-then-forward, scale included."""
+    x, w = wls.random_case(80, m, n, k, scale=2.0)
+    w[np.random.default_rng(81).random(w.shape) < 0.3] = 0
+    y, ws = bl.forward_latent(dev_bf16(x), torch.from_numpy(w).to(DEV))
+    p_ref, ws_ref = oracle.pack_weights(w)
+    assert f32_bits(ws.cpu().numpy()[0]) == f32_bits(ws_ref)
+    assert_bf16_close(host_bits(y), oracle.forward(x, p_ref, ws_ref), f"latent {m}x{n}x{k}")
