@@ -717,6 +717,17 @@ def main():
                                    "export of the packed weights) through torch.matmul (vendor "
                                    "BLAS), rotated like the ternary steps; compare ms_per_step "
                                    "with the configs array")
+        # token counts between decode and prefill: the mid-M path (tiles of
+        # 32 / 64 / 128 rows, chosen by M) on the 3B- and 8B-class layers
+        ctx["mid_m"] = []
+        for n in ("decode_3b", "layer_8b"):
+            for mm in (16, 32, 64, 128, 256):
+                r = measure(torch, bl, wls, n, mm, args, dev, 0.1)
+                wl_n = wls.WORKLOADS[n]
+                ctx["mid_m"].append({"workload": n, "m": mm, "us_per_step": r["ms_per_step"] * 1e3,
+                                     "GBs_packed": wl_n.packed_bytes / (r["ms_per_step"] * 1e-3) / 1e9,
+                                     "TOPS": wl_n.ops(mm) / (r["ms_per_step"] * 1e-3) / 1e12,
+                                     "kernel_launches_per_step": r["kernel_launches_per_step"]})
         peaks = measured_ceilings(torch, dev)
         peaks["headline_frac_of_stream_read"] = h["value"] / peaks["stream_read_GBs"]
         for r in rows:

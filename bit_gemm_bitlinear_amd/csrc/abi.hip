@@ -50,6 +50,8 @@ struct Layout {
   bool decode;
   int load_mode;
   int32_t m_pad;
+  int32_t bm;          // prefill: token rows per tile
+  bool all_narrow;     // prefill: every tile of the launch is a narrow one
   size_t q_off[kMaxProj], xs_off[kMaxProj], qs_off[kMaxProj];
   size_t part_off[kMaxProj], cnt_off[kMaxProj];
   DecodePlan plan[kMaxProj];
@@ -73,7 +75,17 @@ void make_layout(int32_t count, const int64_t* ns, const int64_t* ks, int64_t m,
                  Layout& L) {
   L.decode = m <= kDecodeMaxM;
   L.load_mode = load_mode_for(count, ks);
-  L.m_pad = L.decode ? (int32_t)m : (int32_t)round_up(m, kPrefillBM);
+  L.bm = prefill_bm(m, L.load_mode);
+  L.m_pad = L.decode ? (int32_t)m : (int32_t)round_up(m, L.bm);
+  // A launch whose wide tiles would leave most workgroup slots empty (the
+  // mid-M range: few token tiles) runs every tile narrow, twice as many.
+  L.all_narrow = false;
+  if (!L.decode && L.load_mode == 0) {
+    int64_t wide = 0;
+    for (int i = 0; i < count; ++i)
+      wide += (int64_t)(L.m_pad / L.bm) * ((ns[i] + kPrefillBN - 1) / kPrefillBN);
+    L.all_narrow = 2 * wide < kPrefillPlanSlots;
+  }
   // decode: a layer that one workgroup per CU can cover takes the split
   // plan; otherwise each projection is planned on its own
   const bool split =
@@ -117,7 +129,8 @@ void make_layout(int32_t count, const int64_t* ns, const int64_t* ks, int64_t m,
     int64_t slabs[kMaxProj], tiles[kMaxProj];
     for (int i = 0; i < count; ++i) {
       slabs[i] = L.pf_kspw[i];
-      tiles[i] = (int64_t)(L.m_pad / kPrefillBM) * ((ns[i] + kPrefillBN - 1) / kPrefillBN);
+      const int64_t bn = L.all_narrow ? kPrefillNarrowBN : kPrefillBN;
+      tiles[i] = (int64_t)(L.m_pad / L.bm) * ((ns[i] + bn - 1) / bn);
     }
     plan_ksplit(count, slabs, tiles, kPrefillPlanSlots, kPrefillMinPartSlabs, kPrefillMaxSplit,
                 L.pf_ksplit, L.pf_kspw);
@@ -263,8 +276,10 @@ bl_status run_forward(int32_t count, const ProjIO* io, int64_t m, void* workspac
     PrefillArgs pa = {};
     pa.count = count;
     pa.m = (int32_t)m;
-    pa.tiles_m = L.m_pad / kPrefillBM;
+    pa.tiles_m = L.m_pad / L.bm;
     pa.load_mode = load_mode;
+    pa.bm = L.bm;
+    const int32_t bn = L.all_narrow ? kPrefillNarrowBN : prefill_bn(load_mode);
     // Longest K first: the dispatcher hands out workgroups in launch order,
     // so the costliest tiles start first and the short ones fill in.
     int order[kMaxProj];
@@ -284,9 +299,9 @@ bl_status run_forward(int32_t count, const ProjIO* io, int64_t m, void* workspac
       P.n = (int32_t)ns[i];
       P.k = (int32_t)ks[i];
       P.ldq = (int32_t)round_up(ks[i], kKPad);
-      P.tiles_n = (int32_t)((ns[i] + prefill_bn(load_mode) - 1) / prefill_bn(load_mode));
+      P.tiles_n = (int32_t)((ns[i] + bn - 1) / bn);
       P.ldy = (int32_t)ns[i];
-      P.narrow = 0;
+      P.narrow = L.all_narrow ? 1 : 0;
       P.ksplit = L.pf_ksplit[i];
       P.kspw = L.pf_kspw[i];
       P.part = P.ksplit > 1 ? reinterpret_cast<int32_t*>(ws + L.pf_part_off[i]) : nullptr;
@@ -297,7 +312,7 @@ bl_status run_forward(int32_t count, const ProjIO* io, int64_t m, void* workspac
     // The last tile columns of the last projection become narrow tiles when
     // that evens out the launch's last round of workgroups.
     int entries = count;
-    if (load_mode == 0 && count < kMaxProj) {
+    if (load_mode == 0 && !L.all_narrow && count < kMaxProj) {
       int64_t slabs[kMaxProj], cols[kMaxProj];
       int parts[kMaxProj];
       for (int o = 0; o < count; ++o) {

@@ -131,7 +131,14 @@ size_t decode_lds_bytes(int64_t m, int lds_row);
 hipError_t launch_decode(const DecodeArgs& a, int total_wgs, size_t lds_bytes, hipStream_t s);
 
 // ---- prefill contraction (prefill.hip) ----
-constexpr int kPrefillBM = 128;  // token rows per tile
+constexpr int kPrefillBM = 128;  // token rows per tile (register-staged variant; main variant's largest)
+// Token rows per tile of the main variant: tiles of 32 or 64 rows for
+// 16 < M <= 64 (the mid-M range, where 128-row tiles would mostly multiply
+// padding rows), 128 otherwise.
+inline int prefill_bm(int64_t m, int load_mode) {
+  if (load_mode != 0) return kPrefillBM;
+  return m <= 32 ? 32 : (m <= 64 ? 64 : kPrefillBM);
+}
 #ifndef BL_PREFILL_BN
 #define BL_PREFILL_BN 256
 #endif
@@ -175,6 +182,7 @@ struct PrefillArgs {
   int32_t m;
   int32_t tiles_m;
   int32_t load_mode;
+  int32_t bm;  // token rows per tile (prefill_bm)
 };
 
 // MI355X workgroup slots for the K-split plan of the prefill launch (256 CUs,

@@ -250,9 +250,10 @@ __global__ __launch_bounds__(kThreads) void prefill_reg_kernel(const PrefillArgs
 // straight from global memory into LDS (gfx950 global_load_lds, 16 bytes
 // per lane, lane L's bytes landing at dst + 16 L), through a ring of NST
 // slab buffers: while slab s is multiplied, slabs up to s+NST-1 are in
-// flight.  No staging registers, one barrier per slab.  The tile is BM=128
-// tokens x BNT outputs (256, or 128 for the entries the host marks narrow); a
-// slab is BK codes deep (128 or 256).  The expanded weights are the matrix
+// flight.  No staging registers, one barrier per slab.  The tile is TBM
+// tokens (128; 32 or 64 in the mid-M range, prefill_bm) x BNT outputs (256, or
+// 128 for the entries the host marks narrow); a slab is BK codes deep (128 or
+// 256).  The expanded weights are the matrix
 // core's first operand and the activation codes its second, so each lane's
 // sums belong to one token row (see the epilogue).
 //
@@ -272,12 +273,26 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// Waits until at most `ahead` slabs of D loads each are still in flight
+// (ahead <= C; a compile-time count per case, as the wait needs one).
+template <int D, int C>
+__device__ __forceinline__ void wait_slabs(int ahead) {
+  if constexpr (C == 0) {
+    wait_vm<0>();
+  } else {
+    if (ahead >= C)
+      wait_vm<C * D>();
+    else
+      wait_slabs<D, C - 1>(ahead);
+  }
+}
+
 __device__ __forceinline__ void dma16(const void* src, int8_t* lds_dst) {
   __builtin_amdgcn_global_load_lds((const BL_GLOBAL void*)src,
                                    (__attribute__((address_space(3))) void*)lds_dst, 16, 0, 0);
 }
 
-template <int BNT, int WMI, int NW, int BK>
+template <int BNT, int WMI, int NW, int BK, int TBM>
 struct Cfg {
   static_assert(BK == 128 || BK == 256, "a slab is 128 or 256 codes deep");
   static constexpr int kNT = 64 * NW;  // threads
@@ -296,13 +311,13 @@ struct Cfg {
   static __device__ __forceinline__ int bswz(int j, int c) {
     return c ^ ((j / kBColsPerSlot) & (kBCh - 1));
   }
-  static constexpr int kAChunks = BM * kACh;
+  static constexpr int kAChunks = TBM * kACh;
   static constexpr int kBChunks = BNT * kBCh;
   static constexpr int kStageBytes = (kAChunks + kBChunks) * 16;
   static constexpr int kADma = kAChunks / kNT;
   static constexpr int kBDma = kBChunks / kNT;
   static constexpr int kDma = kADma + kBDma;    // DMA instructions per thread per slab
-  static constexpr int kWavesM = BM / (32 * WMI);  // waves along the tile's rows
+  static constexpr int kWavesM = TBM / (32 * WMI);  // waves along the tile's rows
   static constexpr int kWavesN = NW / kWavesM;     // waves along its columns
   static constexpr int WNF = BNT / (32 * kWavesN);  // 32-column tiles per wave
   static_assert(kWavesM * kWavesN == NW && WNF >= 1, "the waves cover the tile");
@@ -313,9 +328,9 @@ struct Cfg {
 // once per tile, so issuing a slab is an add per load.  Weight rows whose
 // packed length is not a multiple of the slab's bytes have their last
 // slab's loads clamped to the row (the codes there meet zero activations).
-template <int BNT, int WMI, int NW, int BK>
+template <int BNT, int WMI, int NW, int BK, int TBM>
 struct Stager {
-  using K = Cfg<BNT, WMI, NW, BK>;
+  using K = Cfg<BNT, WMI, NW, BK, TBM>;
   const int8_t* a[K::kADma];
   const uint8_t* brow[K::kBDma];
   int bc[K::kBDma];  // byte offset of the lane's chunk within a slab of a weight row
@@ -368,20 +383,20 @@ struct Stager {
 // WMI = 32-row tiles per wave.  With WMI = 4 each wave covers all 128 rows of
 // the tile and its own columns, so every weight column is expanded once per
 // workgroup; with WMI = 2 two waves share (and both expand) each column.
-// One output tile (BM rows x BNT columns) of projection P.
+// One output tile (TBM rows x BNT columns) of projection P.
 // EPI: the extra epilogue work (a separate kernel instance) -- the bias and
 // then the residual added to the bf16 outputs (BitLinear.forward's bias
 // line, each add rounded to bf16), and int32 accumulators written next to
 // the bf16 outputs where a projection asks for both (inspection).
-template <int BNT, int NST, int WMI, int NW, int BK, bool EPI>
+template <int BNT, int NST, int WMI, int NW, int BK, bool EPI, int TBM>
 __device__ __forceinline__ void prefill_tile(const PrefillArgs& A, const PrefillProj& P, int tm, int tn,
                                              int kp, int8_t* __restrict__ smem) {
-  using K = Cfg<BNT, WMI, NW, BK>;
+  using K = Cfg<BNT, WMI, NW, BK, TBM>;
   constexpr int WNF = K::WNF;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int lj = lane & 31, lg = lane >> 5;
-  const int m0 = tm * BM;
+  const int m0 = tm * TBM;
   const int n0 = tn * BNT;
   const int wm0 = (wave % K::kWavesM) * 32 * WMI;  // wave's rows within the tile
   const int wn0 = (wave / K::kWavesM) * 32 * WNF;  // wave's columns within the tile
@@ -407,7 +422,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& A, const Prefill
       for (int r = 0; r < 16; ++r) acc[i][f][r] = q0;
   }
 
-  const Stager<BNT, WMI, NW, BK> stager(P, m0, n0);
+  const Stager<BNT, WMI, NW, BK, TBM> stager(P, m0, n0);
 #pragma unroll
   for (int p = 0; p < NST - 1; ++p)
     if (p < nsl) stager.issue(s0 + p, smem + p * K::kStageBytes);
@@ -415,14 +430,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& A, const Prefill
   for (int s = 0; s < nsl; ++s) {
     // wait for slab s: the slabs issued after it (at most NST-2) may still fly
     const int ahead = min(nsl - 1 - s, NST - 2);
-    if constexpr (NST == 3) {
-      if (ahead >= 1)
-        wait_vm<K::kDma>();
-      else
-        wait_vm<0>();
-    } else {
-      wait_vm<0>();
-    }
+    wait_slabs<K::kDma, NST - 2>(ahead);
     __builtin_amdgcn_s_barrier();  // every wave's slab-s data is in LDS, and
                                    // every wave is done with slab s-1's buffer
     if (s + NST - 1 < nsl)
@@ -565,7 +573,9 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& A, const Prefill
 // entries marked narrow: the host gives the tiles that would otherwise run
 // in a last, partly filled round of workgroups that width, so that the
 // round fills the chip and ends sooner.
-template <int NST, int WMI, int NW, int BK, bool EPI>
+// TBM: token rows per tile (the 32-row tiles take one 32-row subtile per
+// wave, WMI = 1).
+template <int NST, int WMI, int NW, int BK, bool EPI, int TBM>
 __global__ __launch_bounds__(64 * NW)
 __attribute__((amdgpu_waves_per_eu(NW * kPrefillWgsPerCu / 4))) void prefill_kernel(const PrefillArgs A) {
   extern __shared__ __align__(16) int8_t smem[];
@@ -578,10 +588,11 @@ __attribute__((amdgpu_waves_per_eu(NW * kPrefillWgsPerCu / 4))) void prefill_ker
   if (!tile_of((int)blockIdx.x - A.tile_begin[pi], A.tiles_m, P.tiles_n * P.ksplit, &tm, &tn)) return;
   const int kp = tn / P.tiles_n;
   tn -= kp * P.tiles_n;
+  constexpr int W = TBM < 128 ? 1 : WMI;  // 32-row subtiles per wave
   if (P.narrow)
-    prefill_tile<kPrefillNarrowBN, NST, WMI, NW, BK, EPI>(A, P, tm, tn, kp, smem);
+    prefill_tile<kPrefillNarrowBN, NST, W, NW, BK, EPI, TBM>(A, P, tm, tn, kp, smem);
   else
-    prefill_tile<kPrefillBN, NST, WMI, NW, BK, EPI>(A, P, tm, tn, kp, smem);
+    prefill_tile<kPrefillBN, NST, W, NW, BK, EPI, TBM>(A, P, tm, tn, kp, smem);
 }
 
 // Adds the K parts of the split projections.  Piece i of a projection is 8
@@ -679,27 +690,37 @@ hipError_t launch_prefill(const PrefillArgs& a, int total_tiles, hipStream_t s) 
     constexpr int BNT = BL_PREFILL_BN, NST = BL_PREFILL_NST, WMI = BL_PREFILL_WMI,
                   NW = BL_PREFILL_NW, BK = BL_PREFILL_BK;
     static_assert(BNT >= kPrefillNarrowBN, "the wide tiles' slab buffers hold the narrow ones'");
-    constexpr size_t lds = (size_t)NST * Cfg<BNT, WMI, NW, BK>::kStageBytes;
     bool ins = false;  // extra epilogue work: inspection, bias or residual
     for (int i = 0; i < a.count; ++i)
       ins = ins || (a.p[i].y && a.p[i].acc_out) || a.p[i].bias || a.p[i].res;
-    auto go = [&](auto insc) -> hipError_t {
+    auto go = [&](auto insc, auto bmc) -> hipError_t {
       constexpr bool I = decltype(insc)::value;
+      constexpr int TB = decltype(bmc)::value;
+      constexpr int W = TB < 128 ? 1 : WMI;
+      // Small tiles do little work per slab, so more slabs stay in flight to
+      // cover the memory latency (two workgroups per CU still fit the LDS).
+      constexpr int NS = TB == 32 ? 6 : (TB == 64 ? 4 : NST);
+      constexpr size_t lds = (size_t)NS * Cfg<BNT, W, NW, BK, TB>::kStageBytes;
       if (lds > 64 * 1024) {  // the attribute is needed above 64 KB; once per device
         static std::atomic<bool> done[kMaxDevices];
         const int dev = current_device_index();
         if (!done[dev].load(std::memory_order_acquire)) {
           const hipError_t attr = hipFuncSetAttribute(
-              reinterpret_cast<const void*>(&prefill_kernel<NST, WMI, NW, BK, I>),
+              reinterpret_cast<const void*>(&prefill_kernel<NS, WMI, NW, BK, I, TB>),
               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
           if (attr != hipSuccess) return attr;
           done[dev].store(true, std::memory_order_release);
         }
       }
-      prefill_kernel<NST, WMI, NW, BK, I><<<(unsigned)total_tiles, 64 * NW, lds, s>>>(a);
+      prefill_kernel<NS, WMI, NW, BK, I, TB><<<(unsigned)total_tiles, 64 * NW, lds, s>>>(a);
       return hipSuccess;
     };
-    const hipError_t e = ins ? go(std::true_type{}) : go(std::false_type{});
+    auto by_bm = [&](auto insc) -> hipError_t {
+      if (a.bm == 32) return go(insc, std::integral_constant<int, 32>{});
+      if (a.bm == 64) return go(insc, std::integral_constant<int, 64>{});
+      return go(insc, std::integral_constant<int, kPrefillBM>{});
+    };
+    const hipError_t e = ins ? by_bm(std::true_type{}) : by_bm(std::false_type{});
     if (e != hipSuccess) return e;
   } else if (a.load_mode == 1) {
     prefill_reg_kernel<1><<<(unsigned)total_tiles, kThreads, 0, s>>>(a);

@@ -676,3 +676,44 @@ def test_forward_latent_parity(bl, m, n, k):
     p_ref, ws_ref = oracle.pack_weights(w)
     assert f32_bits(ws.cpu().numpy()[0]) == f32_bits(ws_ref)
     assert_bf16_close(host_bits(y), oracle.forward(x, p_ref, ws_ref), f"latent {m}x{n}x{k}")
+
+
+# ------------------------------------------------------------------ mid-M (16 < M < 256)
+
+MID_ACC_SHAPES = [
+    # 32-row tiles (17..32 tokens), 64-row tiles (33..64), 128-row tiles
+    # (65..); every launch with few tiles runs them all narrow; K split across
+    # workgroups where one projection's K dominates; ragged N, K % 128 == 64
+    (17, 16, 256), (32, 300, 1024), (33, 130, 2112), (48, 257, 4096), (64, 200, 16384),
+    (65, 136, 2048), (100, 257, 1088), (128, 640, 4096), (20, 4096, 14336),
+]
+
+
+@pytest.mark.parametrize("m,n,k", MID_ACC_SHAPES)
+def test_mid_m_forward_acc_parity(bl, m, n, k):
+    rng = np.random.default_rng(m * 7919 + n * 31 + k)
+    q = rng.integers(-128, 128, size=(m, k), dtype=np.int16).astype(np.int8)
+    packed = rng.integers(0, 256, size=(n, k // 4), dtype=np.int16).astype(np.uint8)  # incl. code 3
+    ref = oracle.forward_acc(q, packed)
+    acc = bl.forward_acc(torch.from_numpy(q).to(DEV), torch.from_numpy(packed).to(DEV))
+    assert np.array_equal(acc.cpu().numpy(), ref)
+    if n % 16 == 0 and k % 256 == 0:
+        acc = bl.forward_acc(torch.from_numpy(q).to(DEV), torch.from_numpy(oracle.tile(packed)).to(DEV))
+        assert np.array_equal(acc.cpu().numpy(), ref)
+
+
+@pytest.mark.parametrize("name,m", [(n, m) for n in ("decode_3b", "layer_8b")
+                                    for m in (17, 32, 64, 100, 128)])
+def test_mid_m_workload_parity(bl, name, m):
+    """The 3B- and 8B-class layers at mid-range token counts, one grouped
+    call on tiled weights, with the forward path's codes, scales, code sums
+    and accumulators compared element by element with the oracle."""
+    wl = wls.WORKLOADS[name]
+    entries = packed_workload(bl, wl)
+    xs = [wls.activations(wl, pi, m) for pi in range(len(wl.projections))]
+    ys, inss, status = bl.forward_grouped_inspect([dev_bf16(x) for x in xs],
+                                                  [e[4] for e in entries], [e[1] for e in entries])
+    assert int(status.item()) == 0
+    for pi, (x, y, ins, e) in enumerate(zip(xs, ys, inss, entries)):
+        check_inspection(f"{name} {wl.projections[pi].name} M={m}", x, y, ins, e[2], e[3],
+                         oracle.forward(x, e[2], e[3]))
