@@ -104,6 +104,8 @@ def parse():
     ap.add_argument("--command", default="", help="command line recorded in a summary")
     ap.add_argument("--layout", choices=["tiled", "rows"], default="tiled",
                     help="weight layout: the 16-row tiled layout, or row-major [N][K/4]")
+    ap.add_argument("--lut-eval", action="store_true",
+                    help="the lookup-table contraction against the matrix-core decode, M = 1")
     ap.add_argument("--curve", action="store_true",
                     help="decode GB/s against weight bytes for one projection (1 MiB .. 1 GiB)")
     return ap.parse_args()
@@ -622,6 +624,37 @@ def bandwidth_curve(torch, bl, dev, layout, args, k=4096, sizes_mib=(1, 4, 16, 6
     return rows
 
 
+def lut_eval(torch, bl, dev, args, shapes=((8192, 2048), (2048, 8192), (16384, 4096), (4096, 8192))):
+    """The lookup-table contraction (probe library) against the matrix-core
+    decode on single projections at M = 1, same tiled weights, rotated over
+    copies spanning >= 1 GiB: one launch per step each (the decode path also
+    quantizes the bf16 row and dequantizes, the table path takes ready
+    codes and returns int32)."""
+    from bit_gemm_bitlinear_amd import probes
+
+    rows = []
+    g = torch.Generator(device="cpu").manual_seed(5)
+    for n, k in shapes:
+        nbytes = n * k // 4
+        copies = max(1, (1 << 30) // nbytes)
+        base = bl.tile_weights(torch.randint(0, 3, (n, k // 4), dtype=torch.uint8, device=dev))
+        ws = [base] + [base.clone() for _ in range(copies - 1)]
+        x = torch.randn(1, k, generator=g).to(torch.bfloat16).to(dev)
+        q = torch.randint(-127, 128, (k,), dtype=torch.int8, device=dev)
+        scale = torch.ones(1, dtype=torch.float32, device=dev)
+        acc = torch.empty(n, dtype=torch.int32, device=dev)
+        mfma = [bl.GroupedCall([x], [w], [scale]) for w in ws]
+        lut = [lambda w=w: probes.lut_decode_acc(q, w, acc) for w in ws]
+        t_m, _ = time_config(torch, mfma, 20, 5, 0.2)
+        t_l, _ = time_config(torch, lut, 20, 5, 0.2)
+        um, ul = float(np.median(t_m)) * 1e6, float(np.median(t_l)) * 1e6
+        rows.append({"n": n, "k": k, "packed_bytes": nbytes, "mfma_decode_us": um,
+                     "lut_us": ul, "mfma_decode_GBs": nbytes / um / 1e3, "lut_GBs": nbytes / ul / 1e3})
+        del ws, mfma, lut, base
+        torch.cuda.empty_cache()
+    return rows
+
+
 def main():
     args = parse()
     if args.summarize_stats:
@@ -648,6 +681,10 @@ def main():
     dev = torch.device("cuda:0")
     if args.curve:
         for r in bandwidth_curve(torch, bl, dev, args.layout, args):
+            print(json.dumps(r), flush=True)
+        return
+    if args.lut_eval:
+        for r in lut_eval(torch, bl, dev, args):
             print(json.dumps(r), flush=True)
         return
 

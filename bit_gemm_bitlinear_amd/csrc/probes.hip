@@ -87,6 +87,69 @@ __global__ __launch_bounds__(kThreads) void mfma_loop_kernel(int iters, int patt
   sink[t] = (int32_t)s;
 }
 
+// ---------------------------------------------------------------------------
+// A lookup-table contraction for one token row (the idea of T-MAC, which the
+// GeekNews page on bitnet.cpp names as the basis of its CPU kernels), kept as
+// the alternative the matrix-core decode is measured against.  For every
+// pair of activation codes (q[2j], q[2j+1]) the workgroup tabulates, in LDS,
+// the 16 sums q[2j] (c0 - 1) + q[2j+1] (c1 - 1) over the 2-bit weight codes
+// c0, c1 -- one 4-bit field of a packed byte indexes them.  The weights then
+// cost one table read and one add per pair instead of a multiply-add each.
+// Weights are read in the 16-row tiled layout (common.hpp of the library),
+// the same 1 KB per wave load as the matrix-core decode: lane (r, g) holds
+// packed bytes 16 g .. 16 g + 15 of row r in each 256-weight tile.
+constexpr int kLutMaxK = 8192;  // table: (K/2 + K/64) pairs x 32 bytes <= 135 KB of LDS
+constexpr int kLutRing = 8;     // tiles in flight per lane
+
+// Index (in int16 entries) of entry `nib` of pair j: 16 entries per pair and
+// one pair of padding per 32, so that the four 32-pair runs that the four
+// lane groups of a wave read fall on different LDS banks.
+__device__ __forceinline__ int lut_index(int j, int nib) { return (j + (j >> 5)) * 16 + nib; }
+
+__global__ __launch_bounds__(kThreads) void lut_decode_kernel(const int8_t* __restrict__ q, int k,
+                                                              const uint8_t* __restrict__ tiled,
+                                                              int n, int32_t* __restrict__ acc) {
+  extern __shared__ int16_t tab[];
+  const int pairs = k >> 1;
+  for (int j = threadIdx.x; j < pairs; j += kThreads) {
+    const int32_t a = q[2 * j], b = q[2 * j + 1];
+    int16_t* e = tab + lut_index(j, 0);
+#pragma unroll
+    for (int nib = 0; nib < 16; ++nib) e[nib] = (int16_t)(a * ((nib & 3) - 1) + b * ((nib >> 2) - 1));
+  }
+  __syncthreads();
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int r = lane & 15, g = lane >> 4;
+  const int blocks = n >> 4, tiles = k >> 8;
+  const int64_t rowbytes = k >> 2;
+  for (int blk = (int)blockIdx.x * 4 + wave; blk < blocks; blk += (int)gridDim.x * 4) {
+    const uint8_t* base = tiled + (int64_t)blk * 16 * rowbytes + 16 * lane;
+    int32_t sum = 0;
+    for (int t0 = 0; t0 < tiles; t0 += kLutRing) {
+      v4i w[kLutRing];
+#pragma unroll
+      for (int u = 0; u < kLutRing; ++u)
+        w[u] = __builtin_nontemporal_load(
+            reinterpret_cast<const v4i*>(base + 1024 * (int64_t)min(t0 + u, tiles - 1)));
+#pragma unroll
+      for (int u = 0; u < kLutRing; ++u) {
+        if (t0 + u >= tiles) break;
+        // pair 128 t + 32 g + 8 d + e is nibble e of dword d of this chunk
+        const int jb = 128 * (t0 + u) + 32 * g;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const uint32_t x = (uint32_t)w[u][d];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) sum += tab[lut_index(jb + 8 * d + e, (x >> (4 * e)) & 15u)];
+        }
+      }
+    }
+    sum += __shfl_xor(sum, 16, 64);
+    sum += __shfl_xor(sum, 32, 64);
+    if (g == 0) acc[blk * 16 + r] = sum;
+  }
+}
+
 }  // namespace
 
 extern "C" {
@@ -103,6 +166,33 @@ int blprobe_stream_read(const void* buf, int64_t bytes, int32_t* sink, void* str
   if (grid > need) grid = need;
   stream_read_kernel<<<(unsigned)grid, kThreads, 0, (hipStream_t)stream>>>(
       reinterpret_cast<const v4i*>(buf), n16, sink);
+  return hipGetLastError() == hipSuccess ? 0 : 5;
+}
+
+int blprobe_lut_decode_acc(const int8_t* q, int64_t k, const uint8_t* tiled, int64_t n,
+                           int32_t* acc, void* stream) {
+  if (!q || !tiled || !acc || k < 256 || k > kLutMaxK || k % 256 != 0 || n < 16 || n % 16 != 0 ||
+      n > (int64_t(1) << 26) || ((uintptr_t)q & 15) || ((uintptr_t)tiled & 15) || ((uintptr_t)acc & 15))
+    return 1;
+  const size_t lds = (size_t)(k / 2 + k / 64) * 32;
+  static bool attr_set[64] = {};
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64 ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 5;
+  if (!attr_set[dev]) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&lut_decode_kernel),
+                            hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)((kLutMaxK / 2 + kLutMaxK / 64) * 32)) != hipSuccess)
+      return 5;
+    attr_set[dev] = true;
+  }
+  // one workgroup per CU (the table fills most of its LDS), four 16-row
+  // blocks at a time
+  int64_t grid = (n / 16 + 3) / 4;
+  if (grid > cus) grid = cus;
+  lut_decode_kernel<<<(unsigned)grid, kThreads, lds, (hipStream_t)stream>>>(q, (int)k, tiled,
+                                                                            (int)n, acc);
   return hipGetLastError() == hipSuccess ? 0 : 5;
 }
 

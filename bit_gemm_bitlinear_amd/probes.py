@@ -23,6 +23,8 @@ _lib = ctypes.CDLL(LIB_PATH)
 _i64, _i32, _vp = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p
 _lib.blprobe_stream_read.restype = ctypes.c_int
 _lib.blprobe_stream_read.argtypes = [_vp, _i64, _vp, _vp]
+_lib.blprobe_lut_decode_acc.restype = ctypes.c_int
+_lib.blprobe_lut_decode_acc.argtypes = [_vp, _i64, _vp, _i64, _vp, _vp]
 _lib.blprobe_mfma_i8.restype = ctypes.c_int
 _lib.blprobe_mfma_i8.argtypes = [_i64, _i32, _i32, _vp, _vp]
 
@@ -47,6 +49,24 @@ def stream_read(buf: torch.Tensor, sink: torch.Tensor) -> None:
                                   ctypes.c_void_p(sink.data_ptr()), _stream(buf.device))
     if st != 0:
         raise RuntimeError(f"blprobe_stream_read failed ({st})")
+
+
+def lut_decode_acc(q: torch.Tensor, tiled: torch.Tensor, out: torch.Tensor | None = None):
+    """The lookup-table contraction of one token row: q int8 [K], weights in
+    the tiled layout [N/16, 4K] -> int32 [N]."""
+    assert q.is_cuda and q.dtype == torch.int8 and q.dim() == 1 and q.is_contiguous()
+    assert tiled.is_cuda and tiled.dtype == torch.uint8 and tiled.dim() == 2 and tiled.is_contiguous()
+    k = q.numel()
+    assert tiled.shape[1] == 4 * k
+    n = 16 * tiled.shape[0]
+    if out is None:
+        out = torch.empty(max(n, 4), dtype=torch.int32, device=q.device)[:n]
+    assert out.is_cuda and out.dtype == torch.int32 and out.numel() == n
+    st = _lib.blprobe_lut_decode_acc(ctypes.c_void_p(q.data_ptr()), k, ctypes.c_void_p(tiled.data_ptr()),
+                                     n, ctypes.c_void_p(out.data_ptr()), _stream(q.device))
+    if st != 0:
+        raise RuntimeError(f"blprobe_lut_decode_acc failed ({st})")
+    return out
 
 
 def mfma_i8(workgroups: int, iters: int, pattern: int, sink: torch.Tensor) -> int:

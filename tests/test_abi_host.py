@@ -67,7 +67,7 @@ def test_probe_library_exports_and_validation():
     text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "bitlinear_probes.h")).read(),
                   flags=re.S)
     names = sorted(set(re.findall(r"\b(blprobe_\w+)\s*\(", text)))
-    assert names == ["blprobe_mfma_i8", "blprobe_stream_read"]
+    assert names == ["blprobe_lut_decode_acc", "blprobe_mfma_i8", "blprobe_stream_read"]
     out = subprocess.run(["nm", "-D", "--defined-only", probes.LIB_PATH], capture_output=True,
                          text=True).stdout
     assert set(names) <= set(re.findall(r"\bT (blprobe_\w+)", out))
@@ -84,6 +84,13 @@ def test_probe_library_exports_and_validation():
     assert lib.blprobe_mfma_i8(1, (1 << 16) + 1, 0, sink, None) == 1
     assert lib.blprobe_mfma_i8(1, 1, 2, sink, None) == 1
     assert lib.blprobe_mfma_i8(1, 1, 0, None, None) == 1
+    q, t, a = ctypes.c_void_p(0x30000), ctypes.c_void_p(0x40000), ctypes.c_void_p(0x50000)
+    assert lib.blprobe_lut_decode_acc(None, 256, t, 16, a, None) == 1
+    assert lib.blprobe_lut_decode_acc(q, 128, t, 16, a, None) == 1     # K < 256
+    assert lib.blprobe_lut_decode_acc(q, 8448, t, 16, a, None) == 1    # K > 8192
+    assert lib.blprobe_lut_decode_acc(q, 384, t, 16, a, None) == 1     # K % 256
+    assert lib.blprobe_lut_decode_acc(q, 256, t, 24, a, None) == 1     # N % 16
+    assert lib.blprobe_lut_decode_acc(q, 256, ctypes.c_void_p(0x40008), 16, a, None) == 1
 
 
 def test_status_strings_and_version(bl):

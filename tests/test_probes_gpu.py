@@ -51,3 +51,18 @@ def test_mfma_loop_random_operands_deterministic(probes):
     torch.cuda.synchronize()
     assert torch.equal(s1, s2)
     assert int((s1 != 0).sum()) > wgs * 250  # data-dependent sums, not a constant
+
+
+@pytest.mark.parametrize("n,k", [(16, 256), (2048, 2048), (8192, 4096), (1024, 8192), (48, 768)])
+def test_lut_decode_matches_oracle(n, k):
+    """The lookup-table contraction (the alternative the decode kernel is
+    measured against) gives the oracle's exact accumulators, code 3 and
+    q = -128 included."""
+    import oracle
+    from bit_gemm_bitlinear_amd import probes
+
+    rng = np.random.default_rng(n + k)
+    q = rng.integers(-128, 128, size=k, dtype=np.int16).astype(np.int8)
+    packed = rng.integers(0, 256, size=(n, k // 4), dtype=np.int16).astype(np.uint8)
+    acc = probes.lut_decode_acc(torch.from_numpy(q).cuda(), torch.from_numpy(oracle.tile(packed)).cuda())
+    assert np.array_equal(acc.cpu().numpy(), oracle.forward_acc(q[None, :], packed)[0])
