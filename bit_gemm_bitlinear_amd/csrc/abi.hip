@@ -252,8 +252,8 @@ bl_status run_forward(int32_t count, const ProjIO* io, int64_t m, void* workspac
       P.q = pl.fused ? io[i].ins_q : qptr[i];
       P.x_scale = pl.fused ? io[i].ins_xs : xsptr[i];
       P.qsum = pl.fused ? io[i].ins_qs : qsptr[i];
-      P.part = pl.ksplit > 1 ? reinterpret_cast<int32_t*>(ws + L.part_off[i]) : nullptr;
-      P.count = pl.ksplit > 1 ? reinterpret_cast<uint32_t*>(ws + L.cnt_off[i]) : nullptr;
+      da.epi[i].part = pl.ksplit > 1 ? reinterpret_cast<int32_t*>(ws + L.part_off[i]) : nullptr;
+      da.epi[i].count = pl.ksplit > 1 ? reinterpret_cast<uint32_t*>(ws + L.cnt_off[i]) : nullptr;
       P.n = (int32_t)ns[i];
       P.k = (int32_t)ks[i];
       P.ldq = (int32_t)round_up(ks[i], kKPad);

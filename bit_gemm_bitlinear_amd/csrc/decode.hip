@@ -686,7 +686,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& A, const DecodePro
     if (P.ksplit == 1)
       store_out<EPI>(P, E, m, n, v, sh, bad);
     else
-      atomicAdd(P.part + (int64_t)m * P.n + n, v);
+      atomicAdd(E.part + (int64_t)m * P.n + n, v);
   }
   if (P.ksplit == 1) return;
 
@@ -702,7 +702,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& A, const DecodePro
   if constexpr (FUSED) return;  // fused quantization never splits K across WGs
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (tid == 0) sh.flag = (atomicAdd(P.count + group, 1u) == (uint32_t)(P.ksplit - 1));
+  if (tid == 0) sh.flag = (atomicAdd(E.count + group, 1u) == (uint32_t)(P.ksplit - 1));
   __syncthreads();
   if (!sh.flag) return;
   // read-backs four at a time, all four in flight together
@@ -715,7 +715,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& A, const DecodePro
       outm[i] = idx >> lrw;
       outn[i] = group * rows_wg + (idx & (rows_wg - 1));
       vals[i] = (idx < nout && outn[i] < P.n)
-                    ? atomicAdd(P.part + (int64_t)outm[i] * P.n + outn[i], 0)
+                    ? atomicAdd(E.part + (int64_t)outm[i] * P.n + outn[i], 0)
                     : 0;
     }
 #pragma unroll
@@ -753,8 +753,9 @@ __global__ __launch_bounds__(SPLIT ? 512 : 256) void decode_kernel(const DecodeA
   }
   int wl, pi;
   const DecodeProj P = select_proj(A.count, &wl, &pi);
-  DecodeEpi E = {nullptr, nullptr};
-  if constexpr (EPI) E = A.epi[pi];
+  // the epilogue's fields: read where they are used (bias and residual only
+  // in the EPI instance, the split-K buffers only when K is split)
+  const DecodeEpi& E = A.epi[pi];
   switch (P.tww) {
     case 1: decode_tw<1, MODE, SPLIT, EARLY, EPI>(A, P, E, wl, lds, sh); break;
     case 2: decode_tw<2, MODE, SPLIT, EARLY, EPI>(A, P, E, wl, lds, sh); break;

@@ -85,8 +85,6 @@ struct DecodeProj {
   int8_t* q;
   float* x_scale;
   int32_t* qsum;
-  int32_t* part;       // [m][n] int32 split-K partials (zeroed beforehand)
-  uint32_t* count;     // [ngroups] split-K arrival counters (zeroed beforehand)
   int32_t n, k, ldq;
   int32_t wk;          // waves sharing one row tile along K (1, 2 or 4)
   int32_t tww;         // 16-row tiles per wave
@@ -94,12 +92,16 @@ struct DecodeProj {
   int32_t ksplit;      // WGs sharing one row group along K
   int32_t tiled;       // 1: weights in the 16-row tiled layout (common.hpp)
 };
+static_assert(sizeof(DecodeProj) == 96, "six 16-byte words");
 
-// Epilogue additions of a projection, kept apart from DecodeProj so that the
-// descriptor every workgroup fetches first stays at seven 16-byte words.
+// Fields of a projection that only the epilogue needs, kept apart from
+// DecodeProj: every workgroup fetches its descriptor before its first load,
+// and that fetch is shorter the fewer 16-byte words it has.
 struct DecodeEpi {
   const uint16_t* bias;  // [n] bf16 added to y, or nullptr
   const uint16_t* res;   // [m][n] bf16 added to y after the bias (may be y itself), or nullptr
+  int32_t* part;         // [m][n] int32 split-K partials (zeroed beforehand)
+  uint32_t* count;       // [ngroups] split-K arrival counters (zeroed beforehand)
 };
 
 struct DecodeArgs {
