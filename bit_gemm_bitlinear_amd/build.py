@@ -20,7 +20,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libbitlinear.so")
-SOURCES = ["abi.hip", "act_quant.hip", "decode.hip", "prefill.hip", "pack.hip"]
+SOURCES = ["abi.hip", "act_quant.hip", "decode.hip", "decode_fused.hip", "prefill.hip", "pack.hip"]
 # measurement kernels (include/bitlinear_probes.h), a library of their own
 PROBE_LIB = os.path.join(PKG, "libbitlinear_probes.so")
 PROBE_SOURCES = ["probes.hip"]

@@ -64,13 +64,21 @@ hipError_t launch_act_quant_internal(const ActQuantArgs& a, int total_rows, hipS
 hipError_t launch_act_quant_public(const uint16_t* x, int64_t m, int64_t k, int8_t* q,
                                    float* x_scale, hipStream_t s);
 
-// ---- decode contraction (decode.hip) ----
+// ---- decode contraction (decode.hip, decode_fused.hip, decode_kernels.hpp) ----
 // Fused activation quantization inside the decode kernel: each workgroup
-// reads the whole bf16 rows (at most kFusedMaxElems values, 16-byte chunks
-// held in registers) and quantizes them itself.
+// reads the whole bf16 rows of up to kFusedMaxM tokens (16-byte chunks held
+// in registers, at most fused_max_elems values) and quantizes them itself.
+// (Measured with 8 rows: a 2048 x 2048 projection at M = 8 took 10.4 us
+// fused against 9.8 us with the separate quantization launch, so 5-8 rows
+// stage codes prepared by act_quant.hip.)
 constexpr int kFusedMaxM = 4;
-constexpr int kFusedChunks = 8;  // 16-byte chunks of x per thread
-constexpr int64_t kFusedMaxElems = (int64_t)kFusedChunks * 8 * 256;
+constexpr int kFusedChunks1 = 8;   // 16-byte chunks of x per thread, one token row
+constexpr int kFusedChunksN = 24;  // the same, 2 to 4 token rows
+inline int64_t fused_max_elems(int64_t m) {
+  return (int64_t)(m == 1 ? kFusedChunks1 : kFusedChunksN) * 8 * 256;
+}
+// Row slots of the kernel instance that fuses the quantization of m rows.
+inline int fused_rows(int64_t m) { return m == 1 ? 1 : 4; }
 
 struct DecodeProj {
   const uint8_t* packed;
@@ -131,6 +139,9 @@ bool plan_decode_split(int64_t m, int32_t count, const int64_t* ns, const int64_
 int device_cu_count();  // compute units of the current device (cached per device)
 size_t decode_lds_bytes(int64_t m, int lds_row);
 hipError_t launch_decode(const DecodeArgs& a, int total_wgs, size_t lds_bytes, hipStream_t s);
+// The instances that fuse the quantization of 2 to 4 token rows.
+hipError_t launch_decode_rows(const DecodeArgs& a, int total_wgs, size_t lds_bytes, hipStream_t s,
+                              bool epi);
 
 // ---- prefill contraction (prefill.hip) ----
 constexpr int kPrefillBM = 128;  // token rows per tile (register-staged variant; main variant's largest)
