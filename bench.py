@@ -56,10 +56,12 @@ METRIC = "BitLinear decode GB/s of packed weights (% HBM peak); prefill int8 TOP
 HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, published
 MFMA_I8_PEAK_TOPS = 5000.0  # MI355X dense int8 matrix peak, published (POPS x 1000)
 
-# (workload, M) of every configuration, in the workload list's order; the
-# headline is the largest single-GPU decode configuration.
-CONFIGS = [("single_2048_m8", 8), ("decode_1b_m1", 1), ("decode_3b", 1), ("decode_3b", 4),
-           ("decode_3b", 16), ("prefill_2b_m2048", 2048), ("layer_8b", 1), ("layer_8b", 512)]
+# (workload, M) of every configuration: the headline (the largest single-GPU
+# decode configuration) first, the other decode configurations, then the
+# matrix-core ones, so that no decode measurement follows the heat of a
+# prefill one.
+CONFIGS = [("layer_8b", 1), ("single_2048_m8", 8), ("decode_1b_m1", 1), ("decode_3b", 1),
+           ("decode_3b", 4), ("decode_3b", 16), ("prefill_2b_m2048", 2048), ("layer_8b", 512)]
 HEADLINE = ("layer_8b", 1)
 
 # Per kernel: the name rocprofv3 reports and the sources it is built from (a
@@ -107,6 +109,7 @@ def parse():
                     help="weight layout: the 16-row tiled layout, or row-major [N][K/4]")
     ap.add_argument("--lut-eval", action="store_true",
                     help="the lookup-table contraction against the matrix-core decode, M = 1")
+    ap.add_argument("--lut-shape", default="", help="N,K: one projection shape for --lut-eval")
     ap.add_argument("--curve", action="store_true",
                     help="decode GB/s against weight bytes for one projection (1 MiB .. 1 GiB)")
     return ap.parse_args()
@@ -685,7 +688,9 @@ def main():
             print(json.dumps(r), flush=True)
         return
     if args.lut_eval:
-        for r in lut_eval(torch, bl, dev, args):
+        shapes = ((tuple(int(v) for v in args.lut_shape.split(",")),) if args.lut_shape else
+                  ((8192, 2048), (2048, 8192), (16384, 4096), (4096, 8192)))
+        for r in lut_eval(torch, bl, dev, args, shapes):
             print(json.dumps(r), flush=True)
         return
 

@@ -98,56 +98,76 @@ __global__ __launch_bounds__(kThreads) void mfma_loop_kernel(int iters, int patt
 // Weights are read in the 16-row tiled layout (common.hpp of the library),
 // the same 1 KB per wave load as the matrix-core decode: lane (r, g) holds
 // packed bytes 16 g .. 16 g + 15 of row r in each 256-weight tile.
-constexpr int kLutMaxK = 8192;  // table: (K/2 + K/64) pairs x 32 bytes <= 135 KB of LDS
-constexpr int kLutRing = 8;     // tiles in flight per lane
+constexpr int kLutMaxK = 8192;
+constexpr int kLutPartK = 2048;  // weights of a row per workgroup (table: 33 KB of LDS)
+constexpr int kLutRing = 8;      // tiles in flight per lane
 
 // Index (in int16 entries) of entry `nib` of pair j: 16 entries per pair and
 // one pair of padding per 32, so that the four 32-pair runs that the four
 // lane groups of a wave read fall on different LDS banks.
 __device__ __forceinline__ int lut_index(int j, int nib) { return (j + (j >> 5)) * 16 + nib; }
 
+__global__ __launch_bounds__(kThreads) void lut_zero_kernel(int32_t* __restrict__ acc, int n) {
+  for (int i = (int)(blockIdx.x * kThreads + threadIdx.x); i < n; i += (int)(gridDim.x * kThreads))
+    acc[i] = 0;
+}
+
+// Workgroup (b, p): 16-row blocks 4b .. 4b+3 (one per wave) over K part p
+// (kLutPartK weights); partial sums are added to acc (exact integers, so the
+// parts may land in any order).
 __global__ __launch_bounds__(kThreads) void lut_decode_kernel(const int8_t* __restrict__ q, int k,
                                                               const uint8_t* __restrict__ tiled,
                                                               int n, int32_t* __restrict__ acc) {
-  extern __shared__ int16_t tab[];
-  const int pairs = k >> 1;
-  for (int j = threadIdx.x; j < pairs; j += kThreads) {
-    const int32_t a = q[2 * j], b = q[2 * j + 1];
-    int16_t* e = tab + lut_index(j, 0);
+  __shared__ __align__(16) int16_t tab[(kLutPartK / 2 + kLutPartK / 64) * 16];
+  const int parts = (k + kLutPartK - 1) / kLutPartK;
+  const int part = (int)blockIdx.x % parts, wgb = (int)blockIdx.x / parts;
+  const int k0 = part * kLutPartK, kp = min(kLutPartK, k - k0);
+  // the part's table: thread t builds pairs t, t + 256, ... with two 16-byte stores each
+  for (int j = threadIdx.x; j < kp / 2; j += kThreads) {
+    const int32_t a = q[k0 + 2 * j], b = q[k0 + 2 * j + 1];
+    uint32_t h[8];
 #pragma unroll
-    for (int nib = 0; nib < 16; ++nib) e[nib] = (int16_t)(a * ((nib & 3) - 1) + b * ((nib >> 2) - 1));
+    for (int e = 0; e < 8; ++e) {
+      const int n0 = 2 * e, n1 = 2 * e + 1;
+      const uint32_t lo = (uint16_t)(int16_t)(a * ((n0 & 3) - 1) + b * ((n0 >> 2) - 1));
+      const uint32_t hi = (uint16_t)(int16_t)(a * ((n1 & 3) - 1) + b * ((n1 >> 2) - 1));
+      h[e] = lo | (hi << 16);
+    }
+    v4i* dst = reinterpret_cast<v4i*>(tab + lut_index(j, 0));
+    dst[0] = v4i{(int32_t)h[0], (int32_t)h[1], (int32_t)h[2], (int32_t)h[3]};
+    dst[1] = v4i{(int32_t)h[4], (int32_t)h[5], (int32_t)h[6], (int32_t)h[7]};
   }
   __syncthreads();
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int r = lane & 15, g = lane >> 4;
-  const int blocks = n >> 4, tiles = k >> 8;
+  const int blk = wgb * 4 + wave;
+  if (blk >= (n >> 4)) return;
+  const int tiles = kp >> 8;
   const int64_t rowbytes = k >> 2;
-  for (int blk = (int)blockIdx.x * 4 + wave; blk < blocks; blk += (int)gridDim.x * 4) {
-    const uint8_t* base = tiled + (int64_t)blk * 16 * rowbytes + 16 * lane;
-    int32_t sum = 0;
-    for (int t0 = 0; t0 < tiles; t0 += kLutRing) {
-      v4i w[kLutRing];
+  const uint8_t* base = tiled + (int64_t)blk * 16 * rowbytes + 1024 * (int64_t)(k0 >> 8) + 16 * lane;
+  int32_t sum = 0;
+  for (int t0 = 0; t0 < tiles; t0 += kLutRing) {
+    v4i w[kLutRing];
 #pragma unroll
-      for (int u = 0; u < kLutRing; ++u)
-        w[u] = __builtin_nontemporal_load(
-            reinterpret_cast<const v4i*>(base + 1024 * (int64_t)min(t0 + u, tiles - 1)));
+    for (int u = 0; u < kLutRing; ++u)
+      w[u] = __builtin_nontemporal_load(
+          reinterpret_cast<const v4i*>(base + 1024 * (int64_t)min(t0 + u, tiles - 1)));
 #pragma unroll
-      for (int u = 0; u < kLutRing; ++u) {
-        if (t0 + u >= tiles) break;
-        // pair 128 t + 32 g + 8 d + e is nibble e of dword d of this chunk
-        const int jb = 128 * (t0 + u) + 32 * g;
+    for (int u = 0; u < kLutRing; ++u) {
+      if (t0 + u >= tiles) break;
+      // pair 128 t + 32 g + 8 d + e (of the part) is nibble e of dword d of this chunk
+      const int jb = 128 * (t0 + u) + 32 * g;
 #pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          const uint32_t x = (uint32_t)w[u][d];
+      for (int d = 0; d < 4; ++d) {
+        const uint32_t x = (uint32_t)w[u][d];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) sum += tab[lut_index(jb + 8 * d + e, (x >> (4 * e)) & 15u)];
-        }
+        for (int e = 0; e < 8; ++e) sum += tab[lut_index(jb + 8 * d + e, (x >> (4 * e)) & 15u)];
       }
     }
-    sum += __shfl_xor(sum, 16, 64);
-    sum += __shfl_xor(sum, 32, 64);
-    if (g == 0) acc[blk * 16 + r] = sum;
   }
+  sum += __shfl_xor(sum, 16, 64);
+  sum += __shfl_xor(sum, 32, 64);
+  if (g == 0) atomicAdd(acc + blk * 16 + r, sum);
 }
 
 }  // namespace
@@ -174,25 +194,11 @@ int blprobe_lut_decode_acc(const int8_t* q, int64_t k, const uint8_t* tiled, int
   if (!q || !tiled || !acc || k < 256 || k > kLutMaxK || k % 256 != 0 || n < 16 || n % 16 != 0 ||
       n > (int64_t(1) << 26) || ((uintptr_t)q & 15) || ((uintptr_t)tiled & 15) || ((uintptr_t)acc & 15))
     return 1;
-  const size_t lds = (size_t)(k / 2 + k / 64) * 32;
-  static bool attr_set[64] = {};
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64 ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-    return 5;
-  if (!attr_set[dev]) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&lut_decode_kernel),
-                            hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)((kLutMaxK / 2 + kLutMaxK / 64) * 32)) != hipSuccess)
-      return 5;
-    attr_set[dev] = true;
-  }
-  // one workgroup per CU (the table fills most of its LDS), four 16-row
-  // blocks at a time
-  int64_t grid = (n / 16 + 3) / 4;
-  if (grid > cus) grid = cus;
-  lut_decode_kernel<<<(unsigned)grid, kThreads, lds, (hipStream_t)stream>>>(q, (int)k, tiled,
-                                                                            (int)n, acc);
+  const hipStream_t s = (hipStream_t)stream;
+  lut_zero_kernel<<<(unsigned)((n + kThreads - 1) / kThreads), kThreads, 0, s>>>(acc, (int)n);
+  const int64_t parts = (k + kLutPartK - 1) / kLutPartK;
+  const int64_t grid = (n / 16 + 3) / 4 * parts;
+  lut_decode_kernel<<<(unsigned)grid, kThreads, 0, s>>>(q, (int)k, tiled, (int)n, acc);
   return hipGetLastError() == hipSuccess ? 0 : 5;
 }
 

@@ -53,8 +53,10 @@ int blprobe_mfma_i8(int64_t workgroups, int32_t iters, int32_t pattern, int32_t*
  * (M = 1): acc[n] = sum_k q[k] * u[n][k], like bitlinear_forward_acc, with a
  * per-workgroup LDS table of the 16 partial sums of every pair of activation
  * codes indexed by 4 bits of packed weights (the T-MAC idea the GeekNews
- * page on bitnet.cpp names).  q: [K] int8; tiled: the weights in the 16-row
- * tiled layout of bitlinear.h; acc: [N] int32 (written).  N % 16 == 0,
+ * page on bitnet.cpp names); a workgroup covers 64 rows and 2048 weights of
+ * each, the parts' sums are added atomically.  q: [K] int8; tiled: the
+ * weights in the 16-row tiled layout of bitlinear.h; acc: [N] int32
+ * (written; two kernels: clearing, then the contraction).  N % 16 == 0,
  * 256 <= K <= 8192, K % 256 == 0, pointers 16-byte aligned.  It exists to be
  * measured against the matrix-core decode; the library does not use it. */
 int blprobe_lut_decode_acc(const int8_t* q, int64_t k, const uint8_t* tiled, int64_t n,
