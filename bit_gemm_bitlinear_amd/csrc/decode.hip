@@ -54,16 +54,18 @@ bool plan_decode_split(int64_t m, int32_t count, const int64_t* ns, const int64_
     tiles[i] = (ns[i] + 15) / 16;
     if (m * (S[i] * 256 + 16) > kDecodeLdsA) return false;
   }
-  // (wk, tww) pairs: three tiles per wave only with the K range unsplit
-  // (the in-LDS partial sums index rows by shifts)
-  const int wks[10] = {1, 1, 1, 1, 2, 2, 2, 4, 4, 4};
-  const int twws[10] = {1, 2, 3, 4, 1, 2, 4, 1, 2, 4};
+  // (wk, tww) pairs; seven tiles per wave with two waves per K range lets
+  // the 8B-class layer's longest wave stream 56 chunks on 240 CUs instead of
+  // 64 on 216
+  constexpr int kOpts = 11;
+  const int wks[kOpts] = {1, 1, 1, 1, 2, 2, 2, 2, 4, 4, 4};
+  const int twws[kOpts] = {1, 2, 3, 4, 1, 2, 4, 7, 1, 2, 4};
   for (int x = 1; x <= kMaxChunks; ++x) {
     int64_t total = 0;
     bool ok = true;
     for (int i = 0; i < count && ok; ++i) {
       int64_t best = -1;
-      for (int o = 0; o < 10; ++o) {
+      for (int o = 0; o < kOpts; ++o) {
         const int wk = wks[o], tww = twws[o];
         if (tww * ((S[i] + wk - 1) / wk) > x) continue;
         const int64_t per = (int64_t)(4 / wk) * tww;  // 16-row tiles per workgroup
@@ -119,7 +121,7 @@ int device_cu_count() {
 }
 
 size_t decode_lds_bytes(int64_t m, int lds_row) {
-  return (size_t)m * lds_row + (size_t)4 * kDecodeMaxTww * m * 16 * 4;
+  return (size_t)m * lds_row + (size_t)4 * kDecodeRedTww * m * 16 * 4;
 }
 
 hipError_t launch_decode(const DecodeArgs& a, int total_wgs, size_t lds_bytes, hipStream_t s) {

@@ -560,7 +560,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& A, const DecodePro
       // a ring of NC chunks per lane: every slot is refilled with the chunk
       // NC ahead right after it is read, so NC loads stay in flight until
       // the last round (which refills nothing)
-      constexpr int NC = TWW == 3 ? 24 : kSplitRing;
+      constexpr int NC = TWW == 3 ? 24 : (TWW == 7 ? 14 : kSplitRing);
       static_assert(NC % TWW == 0, "a ring slot always holds the same row tile");
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");  // counters zeroed
       __builtin_amdgcn_s_barrier();
@@ -688,13 +688,26 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& A, const DecodePro
   }
   __syncthreads();
   if constexpr (SPLIT) bad = __builtin_amdgcn_readfirstlane(sh.bad) != 0;
-  // output idx -> row m and local column nl; rows_wg and TWW * 16 are powers
-  // of two, so the split is shifts and masks
+  // output idx -> row m and local column nl; with TWW a power of two,
+  // rows_wg and TWW * 16 are too and the split is shifts and masks (seven
+  // tiles per wave divide by constants)
+  constexpr bool kPow2 = (TWW & (TWW - 1)) == 0;
   const int lrw = 31 - __builtin_clz(rows_wg), ltw = 31 - __builtin_clz(TWW * 16);
-  const int nout = M << lrw;  // outputs of this WG
+  const int nout = kPow2 ? (M << lrw) : M * rows_wg;  // outputs of this WG
+  auto split_idx = [&](int idx, int& m, int& nl) {
+    if constexpr (kPow2) {
+      m = idx >> lrw;
+      nl = idx & (rows_wg - 1);
+    } else {
+      m = idx / rows_wg;
+      nl = idx - m * rows_wg;
+    }
+  };
   for (int idx = tid; idx < nout; idx += NT) {
-    const int m = idx >> lrw, nl = idx & (rows_wg - 1);
-    const int g = nl >> ltw, t = (nl >> 4) & (TWW - 1), c = nl & 15;  // g = row wave
+    int m, nl;
+    split_idx(idx, m, nl);
+    const int g = kPow2 ? nl >> ltw : nl / (TWW * 16);  // g = row wave
+    const int t = kPow2 ? (nl >> 4) & (TWW - 1) : (nl >> 4) % TWW, c = nl & 15;
     const int n = group * rows_wg + nl;
     int32_t v = 0;
     for (int q = 0; q < P.wk; ++q) v += red[(((g * P.wk + q) * TWW + t) * M + m) * 16 + c];
@@ -728,8 +741,9 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& A, const DecodePro
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int idx = base + NT * i;
-      outm[i] = idx >> lrw;
-      outn[i] = group * rows_wg + (idx & (rows_wg - 1));
+      int nl;
+      split_idx(idx, outm[i], nl);
+      outn[i] = group * rows_wg + nl;
       vals[i] = (idx < nout && outn[i] < P.n)
                     ? atomicAdd(E.part + (int64_t)outm[i] * P.n + outn[i], 0)
                     : 0;
@@ -776,8 +790,11 @@ __global__ __launch_bounds__(SPLIT ? 512 : 256) void decode_kernel(const DecodeA
   switch (P.tww) {
     case 1: decode_tw<1, MODE, SPLIT, EARLY, EPI, FR>(A, P, E, wl, lds, sh); break;
     case 2: decode_tw<2, MODE, SPLIT, EARLY, EPI, FR>(A, P, E, wl, lds, sh); break;
-    case 3:  // split-shape plans only, with the K range unsplit (wk = 1)
+    case 3:  // split-shape plans only
       if constexpr (SPLIT) decode_tw<3, MODE, SPLIT, EARLY, EPI, FR>(A, P, E, wl, lds, sh);
+      break;
+    case 7:  // split-shape plans only
+      if constexpr (SPLIT) decode_tw<7, MODE, SPLIT, EARLY, EPI, FR>(A, P, E, wl, lds, sh);
       break;
     default: decode_tw<4, MODE, SPLIT, EARLY, EPI, FR>(A, P, E, wl, lds, sh); break;
   }

@@ -14,7 +14,8 @@ int current_device_index();  // hipGetDevice, clamped to [0, kMaxDevices)
 
 // Decode path (M <= 16) limits.
 constexpr int kDecodeMaxM = 16;
-constexpr int kDecodeMaxTww = 4;      // 16-row tiles per wave
+constexpr int kDecodeMaxTww = 4;      // 16-row tiles per wave (per-projection plans)
+constexpr int kDecodeRedTww = 7;      // the same, any plan (sizes the in-LDS partial sums)
 // 52 KB: 16 token rows of 3072 codes (plus row padding) fit, so the 3B-class
 // layer's 3072-wide projections need no K split across workgroups at M = 16
 // (measured: 26.6 -> 23.4 us per layer); a multiple of 4 KB, so the code
