@@ -219,6 +219,7 @@ bl_status run_forward(int32_t count, const ProjIO* io, int64_t m, void* workspac
     J.m = (int32_t)m;
     J.m_pad = L.m_pad;
     J.row_begin = rows;
+    qa.row_begin[jobs - 1] = rows;
     J.paired = L.decode ? 1 : 0;
     J.ins_q = io[i].ins_q;
     J.ins_xs = io[i].ins_xs;

@@ -44,7 +44,7 @@ struct ActQuantJob {
   float* x_scale;      // [m] (written when x != nullptr)
   int32_t* qsum;       // [m] row sums of the codes (written)
   int32_t k, ldq, m, m_pad;
-  int32_t row_begin;   // first block of this job in the launch
+  int32_t row_begin;   // first block (or row) of this job in the launch
   int32_t paired;      // 1: the decode kernel's order (put_group in act_quant.hip), 0: the GEMM's
   // optional inspection outputs (bf16 input only; nullptr: not written): the
   // codes in the natural layout [m][k], the scales [m] and the code sums [m]
@@ -59,6 +59,9 @@ struct ActQuantArgs {
   int32_t zero_blocks_begin;  // blocks from here on only zero `zero`
   int32_t* zero;              // region cleared by the same launch (split-K partials)
   int64_t zero_words;         // its size in int32 words
+  // the jobs' row_begin again, as one contiguous array: a workgroup finds its
+  // job with one argument load instead of one per job
+  int32_t row_begin[kMaxProj];
 };
 
 hipError_t launch_act_quant_internal(const ActQuantArgs& a, int total_rows, hipStream_t s);
