@@ -297,53 +297,99 @@ __device__ __forceinline__ void quant_row_internal_fast(const uint16_t* __restri
   }
 }
 
-// One wave per row, for launches whose rows all come from bf16 input with
-// k % 8 == 0 and at most 64 * NBW groups of 16 codes: no barriers and no
-// LDS.  Lane l owns groups l + 64 b, two 16-byte loads each, all issued
-// before any is used; the absmax and the code sum are wave reductions.
-// q = rint(x * s) with |x * s| <= 127 * (1 + 2^-24) (s = RN(127 / amax)), so
-// the clamp to [-128, 127] never binds; adding 1.5 * 2^23 to t = RN(x * s)
-// rounds to an integer with ties to even and leaves q in two's complement in
-// the low byte of the sum's bits, which byte permutes gather into the
-// internal order (dword a, byte b = code 4b + a).
-template <int NBW, bool INS>
-__device__ __forceinline__ void quant_row_wave(const uint16_t* __restrict__ xr, int k, int ngroups,
-                                               v4i* __restrict__ qv, int32_t* qsum,
-                                               float* x_scale, int8_t* nat_row, float* ins_xs,
-                                               int32_t* ins_qs) {
-  const int lane = threadIdx.x & 63;
+// Rows of bf16 input with k % 8 == 0, in the GEMM's order: a row of up to
+// 256 groups of 16 codes has one wave, a row of up to 512 or 1024 groups two
+// or four (`J.wpr`), so that one instance of four groups per lane covers
+// every row at full occupancy.  Lane l of a row's wave w owns groups
+// l + 64 (w + wpr b), b < 4, two 16-byte loads each, all issued before any is
+// used.  Absmax and code sum are wave reductions, and a row's waves combine
+// theirs through LDS: one barrier each, taken by the whole workgroup (all of
+// a block's rows belong to one job, so wpr is the same for every wave of
+// it).  q = rint(x * s) with |x * s| <= 127 * (1 + 2^-24) (s = RN(127 /
+// amax)), so the clamp to [-128, 127] never binds; adding 1.5 * 2^23 to
+// t = RN(x * s) rounds to an integer with ties to even and leaves q in two's
+// complement in the low byte of the sum's bits, which byte permutes gather
+// into the internal order (dword a, byte b = code 4b + a).
+constexpr int kRowsNBW = 4;  // groups per lane
+
+// The job that block `r` belongs to.  The jobs' first blocks are one
+// contiguous array at fixed kernel-argument offsets, loaded at once, so the
+// lookup costs one round trip to the argument segment rather than one per
+// job (3B-class layer at M = 16: the quantization kernel 5.3 -> 4.6 us).
+__device__ __forceinline__ int job_of(const ActQuantArgs& a, int r) {
+  int ji = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxProj; ++i) ji += (i < a.count && r >= a.row_begin[i]);
+  return ji;
+}
+
+// INS: some job has inspection outputs (a separate instance, so that the
+// bench path carries none of their registers).
+template <bool INS>
+__global__ __launch_bounds__(kThreads) void act_quant_rows_kernel(const ActQuantArgs a) {
+  constexpr int NBW = kRowsNBW;
+  __shared__ uint32_t red[2][kThreads / 64];
+  const int b = blockIdx.x;
+  if (b >= a.zero_blocks_begin) {
+    const int64_t nzb = (int64_t)(gridDim.x - a.zero_blocks_begin);
+    for (int64_t i = (int64_t)(b - a.zero_blocks_begin) * kThreads + threadIdx.x; i < a.zero_words;
+         i += nzb * kThreads)
+      a.zero[i] = 0;
+    return;
+  }
+  // a.row_begin holds each job's first block here
+  const int ji = job_of(a, b);
+  const ActQuantJob& J = a.j[ji];
+  const int lw = J.wpr == 1 ? 0 : (J.wpr == 2 ? 1 : 2);  // log2 of the waves per row
+  const int wave = (int)(threadIdx.x >> 6), lane = (int)(threadIdx.x & 63);
+  const int sub = wave & ((1 << lw) - 1);  // this wave's part of the row
+  const int m = ((b - a.row_begin[ji]) << (2 - lw)) + (wave >> lw);
+  if (lw == 0 && m >= J.m_pad) return;  // past the job's rows (no barrier follows)
+  const bool data = m < J.m;            // else a padding row (or past the rows): zero codes
+  const int k = J.k, ngroups = J.ldq / 16;
   const int kg = k >> 4;  // groups holding data (a last half group: k % 16 == 8)
+  const uint16_t* xr = J.x + (int64_t)(data ? m : 0) * k;
   v4i lo[NBW], hi[NBW];
 #pragma unroll
-  for (int b = 0; b < NBW; ++b) {
-    const int g = lane + 64 * b;
-    lo[b] = hi[b] = v4i{0, 0, 0, 0};
-    if (16 * g < k) {
-      lo[b] = *reinterpret_cast<const v4i*>(xr + 16 * g);
-      if (16 * g + 8 < k) hi[b] = *reinterpret_cast<const v4i*>(xr + 16 * g + 8);
+  for (int bb = 0; bb < NBW; ++bb) {
+    const int g = lane + 64 * (sub + (bb << lw));
+    lo[bb] = hi[bb] = v4i{0, 0, 0, 0};
+    if (data && 16 * g < k) {
+      lo[bb] = *reinterpret_cast<const v4i*>(xr + 16 * g);
+      if (16 * g + 8 < k) hi[bb] = *reinterpret_cast<const v4i*>(xr + 16 * g + 8);
     }
   }
   uint32_t amax = 0;
 #pragma unroll
-  for (int b = 0; b < NBW; ++b)
-    amax = max(amax, max(max(absmax_bits4((uint32_t)lo[b].x, (uint32_t)lo[b].y),
-                             absmax_bits4((uint32_t)lo[b].z, (uint32_t)lo[b].w)),
-                         max(absmax_bits4((uint32_t)hi[b].x, (uint32_t)hi[b].y),
-                             absmax_bits4((uint32_t)hi[b].z, (uint32_t)hi[b].w))));
+  for (int bb = 0; bb < NBW; ++bb)
+    amax = max(amax, max(max(absmax_bits4((uint32_t)lo[bb].x, (uint32_t)lo[bb].y),
+                             absmax_bits4((uint32_t)lo[bb].z, (uint32_t)lo[bb].w)),
+                         max(absmax_bits4((uint32_t)hi[bb].x, (uint32_t)hi[bb].y),
+                             absmax_bits4((uint32_t)hi[bb].z, (uint32_t)hi[bb].w))));
   amax = wave_reduce(amax, [](uint32_t x, uint32_t y) { return max(x, y); });
+  const int w0 = wave & ~((1 << lw) - 1);  // the row's first wave
+  if (lw > 0) {
+    if (lane == 0) red[0][wave] = amax;
+    __syncthreads();
+    amax = max(red[0][w0], red[0][w0 + 1]);
+    if (lw == 2) amax = max(amax, max(red[0][w0 + 2], red[0][w0 + 3]));
+  }
   const float s = act_scale(bf16_to_f32(amax));
+  const bool active = m < J.m_pad;
+  v4i* qv = reinterpret_cast<v4i*>(J.q + (int64_t)(active ? m : 0) * J.ldq);
+  int8_t* nat_row = (INS && data && J.ins_q) ? J.ins_q + (int64_t)m * k : nullptr;
   int32_t sum = 0;
 #pragma unroll
-  for (int b = 0; b < NBW; ++b) {
-    const int g = lane + 64 * b;
-    if (g >= ngroups) continue;
-    if (g > kg || (g == kg && 16 * g >= k)) {  // padding group: zero codes
+  for (int bb = 0; bb < NBW; ++bb) {
+    const int g = lane + 64 * (sub + (bb << lw));
+    if (!active || g >= ngroups) continue;
+    if (!data || g > kg || (g == kg && 16 * g >= k)) {  // padding: zero codes
       qv[g] = v4i{0, 0, 0, 0};
       continue;
     }
-    const uint32_t w[8] = {(uint32_t)lo[b].x, (uint32_t)lo[b].y, (uint32_t)lo[b].z,
-                           (uint32_t)lo[b].w, (uint32_t)hi[b].x, (uint32_t)hi[b].y,
-                           (uint32_t)hi[b].z, (uint32_t)hi[b].w};
+    const uint32_t w[8] = {(uint32_t)lo[bb].x, (uint32_t)lo[bb].y, (uint32_t)lo[bb].z,
+                           (uint32_t)lo[bb].w, (uint32_t)hi[bb].x, (uint32_t)hi[bb].y,
+                           (uint32_t)hi[bb].z, (uint32_t)hi[bb].w};
     uint32_t r[16];
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
@@ -352,11 +398,11 @@ __device__ __forceinline__ void quant_row_wave(const uint16_t* __restrict__ xr, 
     }
     v4i o;
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      const uint32_t l2 = __builtin_amdgcn_perm(r[a + 4], r[a], 0x0c0c0400u);
-      const uint32_t h2 = __builtin_amdgcn_perm(r[a + 12], r[a + 8], 0x0c0c0400u);
-      o[a] = (int32_t)__builtin_amdgcn_perm(h2, l2, 0x05040100u);
-      sum = __builtin_amdgcn_sdot4(o[a], 0x01010101, sum, false);
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t l2 = __builtin_amdgcn_perm(r[q + 4], r[q], 0x0c0c0400u);
+      const uint32_t h2 = __builtin_amdgcn_perm(r[q + 12], r[q + 8], 0x0c0c0400u);
+      o[q] = (int32_t)__builtin_amdgcn_perm(h2, l2, 0x05040100u);
+      sum = __builtin_amdgcn_sdot4(o[q], 0x01010101, sum, false);
     }
     qv[g] = o;
     if (INS && nat_row) {  // inspection: natural dword j, byte i = byte j of o[i]
@@ -372,52 +418,18 @@ __device__ __forceinline__ void quant_row_wave(const uint16_t* __restrict__ xr, 
     }
   }
   sum = (int32_t)wave_reduce((uint32_t)sum, [](uint32_t x, uint32_t y) { return x + y; });
-  if (lane == 0) {
-    *qsum = sum;
-    *x_scale = s;
-    if (INS && ins_qs) *ins_qs = sum;
-    if (INS && ins_xs) *ins_xs = s;
+  if (lw > 0) {
+    if (lane == 0) red[1][wave] = (uint32_t)sum;
+    __syncthreads();
+    sum = (int32_t)(red[1][w0] + red[1][w0 + 1]);
+    if (lw == 2) sum += (int32_t)(red[1][w0 + 2] + red[1][w0 + 3]);
   }
-}
-
-// The job that block `r` belongs to.  The jobs' first blocks are one
-// contiguous array at fixed kernel-argument offsets, loaded at once, so the
-// lookup costs one round trip to the argument segment rather than one per
-// job (3B-class layer at M = 16: the quantization kernel 5.3 -> 4.6 us).
-__device__ __forceinline__ int job_of(const ActQuantArgs& a, int r) {
-  int ji = 0;
-#pragma unroll
-  for (int i = 1; i < kMaxProj; ++i) ji += (i < a.count && r >= a.row_begin[i]);
-  return ji;
-}
-
-// INS: some job has inspection outputs (a separate instance, so that the
-// bench path carries none of their registers).
-template <int NBW, bool INS>
-__global__ __launch_bounds__(kThreads) void act_quant_rows_kernel(const ActQuantArgs a) {
-  constexpr int kRowsPerBlock = kThreads / 64;
-  const int b = blockIdx.x;
-  if (b >= a.zero_blocks_begin) {
-    const int64_t nzb = (int64_t)(gridDim.x - a.zero_blocks_begin);
-    for (int64_t i = (int64_t)(b - a.zero_blocks_begin) * kThreads + threadIdx.x; i < a.zero_words;
-         i += nzb * kThreads)
-      a.zero[i] = 0;
-    return;
+  if (data && sub == 0 && lane == 0) {
+    J.qsum[m] = sum;
+    J.x_scale[m] = s;
+    if (INS && J.ins_qs) J.ins_qs[m] = sum;
+    if (INS && J.ins_xs) J.ins_xs[m] = s;
   }
-  const int row = b * kRowsPerBlock + (int)(threadIdx.x >> 6);
-  int ji = 0;
-  while (ji + 1 < a.count && row >= a.j[ji + 1].row_begin) ++ji;
-  const ActQuantJob& J = a.j[ji];
-  const int m = row - J.row_begin;
-  if (m >= J.m_pad) return;  // past the last job's rows
-  v4i* qv = reinterpret_cast<v4i*>(J.q + (int64_t)m * J.ldq);
-  if (m >= J.m) {  // padding row: zero codes
-    for (int g = threadIdx.x & 63; g < J.ldq / 16; g += 64) qv[g] = v4i{0, 0, 0, 0};
-    return;
-  }
-  quant_row_wave<NBW, INS>(J.x + (int64_t)m * J.k, J.k, J.ldq / 16, qv, J.qsum + m, J.x_scale + m,
-                      J.ins_q ? J.ins_q + (int64_t)m * J.k : nullptr,
-                      J.ins_xs ? J.ins_xs + m : nullptr, J.ins_qs ? J.ins_qs + m : nullptr);
 }
 
 __global__ __launch_bounds__(kThreads) void act_quant_internal_kernel(const ActQuantArgs a) {
@@ -501,38 +513,34 @@ hipError_t launch_act_quant_internal(const ActQuantArgs& a, int total_rows, hipS
     int64_t zb = (args.zero_words + per - 1) / per;
     zero_blocks = (int)(zb > 1024 ? 1024 : zb);
   }
-  // one wave per row when every job is bf16 input with 16-byte rows that
-  // fit the lanes' registers, and there are rows enough to fill the chip
+  // one to four waves per row when every job is bf16 input with 16-byte
+  // rows of at most 16384 codes, and there are rows enough to fill the chip
   // (a few long decode rows are faster with a workgroup each)
-  int groups = 0;
   bool rows_ok = args.count > 0;
   for (int i = 0; i < args.count; ++i) {
     const ActQuantJob& J = args.j[i];
-    rows_ok = rows_ok && J.x != nullptr && (J.k & 7) == 0 && !J.paired;
-    groups = groups > J.ldq / 16 ? groups : J.ldq / 16;
+    rows_ok = rows_ok && J.x != nullptr && (J.k & 7) == 0 && !J.paired &&
+              J.ldq / 16 <= 64 * kRowsNBW * 4;
   }
-  if (rows_ok && groups <= 64 * 16 && total_rows >= kWaveRowsMin) {
-    const int row_blocks = (total_rows + kThreads / 64 - 1) / (kThreads / 64);
-    args.zero_blocks_begin = row_blocks;
-    const dim3 grid((unsigned)(row_blocks + zero_blocks));
+  if (rows_ok && total_rows >= kWaveRowsMin) {
+    // blocks of 4 / wpr rows; a.row_begin becomes each job's first block
+    int blocks = 0;
+    for (int i = 0; i < args.count; ++i) {
+      ActQuantJob& J = args.j[i];
+      const int g = J.ldq / 16;
+      J.wpr = g <= 64 * kRowsNBW ? 1 : (g <= 2 * 64 * kRowsNBW ? 2 : 4);
+      args.row_begin[i] = blocks;
+      blocks += (J.m_pad * J.wpr + kThreads / 64 - 1) / (kThreads / 64);
+    }
+    args.zero_blocks_begin = blocks;
+    const dim3 grid((unsigned)(blocks + zero_blocks));
     bool ins = false;
     for (int i = 0; i < args.count; ++i)
       ins = ins || args.j[i].ins_q || args.j[i].ins_xs || args.j[i].ins_qs;
-    auto go = [&](auto insc) {
-      constexpr bool I = decltype(insc)::value;
-      if (groups <= 64 * 4)
-        act_quant_rows_kernel<4, I><<<grid, kThreads, 0, s>>>(args);
-      else if (groups <= 64 * 7)
-        act_quant_rows_kernel<7, I><<<grid, kThreads, 0, s>>>(args);
-      else if (groups <= 64 * 8)
-        act_quant_rows_kernel<8, I><<<grid, kThreads, 0, s>>>(args);
-      else
-        act_quant_rows_kernel<16, I><<<grid, kThreads, 0, s>>>(args);
-    };
     if (ins)
-      go(std::true_type{});
+      act_quant_rows_kernel<true><<<grid, kThreads, 0, s>>>(args);
     else
-      go(std::false_type{});
+      act_quant_rows_kernel<false><<<grid, kThreads, 0, s>>>(args);
     return hipGetLastError();
   }
   args.zero_blocks_begin = total_rows;

@@ -46,6 +46,7 @@ struct ActQuantJob {
   int32_t k, ldq, m, m_pad;
   int32_t row_begin;   // first block (or row) of this job in the launch
   int32_t paired;      // 1: the decode kernel's order (put_group in act_quant.hip), 0: the GEMM's
+  int32_t wpr;         // waves per row of the wave-per-row kernel (set at its launch)
   // optional inspection outputs (bf16 input only; nullptr: not written): the
   // codes in the natural layout [m][k], the scales [m] and the code sums [m]
   int8_t* ins_q;

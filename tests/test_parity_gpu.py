@@ -476,10 +476,12 @@ def tie_rows(m, k, seed):
 
 
 # fused decode quantizer (M <= 4); decode rows staged by the activation kernel
-# (M = 8, 16); GEMM rows, a workgroup per row (M = 40) and a wave per row
-# (1100 rows); the general row path (K % 8 != 0; K past the register batch)
+# (M = 8, 16); GEMM rows, a workgroup per row (M = 40) and one, two or four
+# waves per row (1100 or 1030 rows); the general row path (K % 8 != 0; K past
+# the register batch)
 @pytest.mark.parametrize("m,k", [(1, 2048), (4, 2048), (8, 2048), (16, 4096), (40, 1024),
-                                 (1100, 2560), (24, 1036), (20, 16400)])
+                                 (1100, 2560), (1100, 6912), (1030, 14336), (24, 1036),
+                                 (20, 16400)])
 def test_forward_path_ties_round_to_even(bl, m, k):
     """Ties through the forward path's own quantizers: every code, scale and
     code sum equals the oracle's round-half-to-even result."""
@@ -565,6 +567,29 @@ def rand_bf16(seed, shape, scale=1.0):
 # workgroups (M = 16, K = 9216); prefill: one tile, K split across
 # workgroups (the finishing pass), ragged N; rows not 16-byte aligned
 # (K % 64 != 0: the register-staged prefill kernel and narrow decode loads)
+def test_rows_kernel_multi_wave_rows(bl):
+    """The GEMM's activation kernel with one, two and four waves per row (up
+    to 256, 512 and 1024 groups of 16 codes) in one launch of four jobs, with
+    rows that end in half a group (K % 16 == 8) and the padding rows of the
+    128-row tiles (M = 300): codes, scales, code sums, accumulators and
+    outputs against the oracle."""
+    m = 300
+    shapes = [(64, 1032), (64, 4104), (48, 8200), (32, 16384)]
+    xs, ps, ss, refs = [], [], [], []
+    for i, (n, k) in enumerate(shapes):
+        x, w = wls.random_case(300 + i, m, n, k)
+        p, s = bl.pack_weights(torch.from_numpy(w).to(DEV))
+        xs.append(x)
+        ps.append(p)
+        ss.append(s)
+        refs.append(oracle.pack_weights(w))
+    ys, inss, status = bl.forward_grouped_inspect([dev_bf16(x) for x in xs], ps, ss)
+    assert int(status.item()) == 0
+    for (n, k), x, y, ins, (p_ref, ws_ref) in zip(shapes, xs, ys, inss, refs):
+        check_inspection(f"rows kernel {m}x{n}x{k}", x, y, ins, p_ref, ws_ref,
+                         oracle.forward(x, p_ref, ws_ref))
+
+
 BIAS_SHAPES = [(1, 2048, 2048), (4, 96, 4096), (8, 300, 1024), (16, 640, 9216), (40, 200, 1024),
                (256, 301, 16384), (300, 264, 2560), (3, 100, 1036), (70, 136, 1036)]
 
