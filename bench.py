@@ -68,8 +68,8 @@ HEADLINE = ("layer_8b", 1)
 # counter figure measured on other sources is stale and is not reported).
 PMC_KERNELS = {
     "decode": {"name": "decode_kernel",
-               "sources": ["decode.hip", "decode_fused.hip", "decode_kernels.hpp", "common.hpp",
-                           "row_div.hpp", "internal.hpp"]},
+               "sources": ["decode.hip", "decode_fused.hip", "decode_kernels.hpp", "abi.hip",
+                           "common.hpp", "row_div.hpp", "internal.hpp"]},
     "prefill": {"name": "prefill_kernel",
                 "sources": ["prefill.hip", "prefill_plan.hpp", "abi.hip", "common.hpp",
                             "row_div.hpp", "internal.hpp"]},
