@@ -44,10 +44,10 @@
  * Conventions for every entry point:
  *  - All tensor pointers are DEVICE pointers to contiguous row-major data,
  *    owned by the caller.  The library never allocates, frees, or
- *    synchronizes, and keeps no state between calls (apart from the device
- *    address of the no-alloc entry point's scratch array, looked up once per
- *    device); calls are thread-safe, except that no-alloc calls on one GPU
- *    must not overlap.
+ *    synchronizes, and keeps no state between calls apart from per-device
+ *    facts it looks up once (the CU count, kernel LDS limits, and the device
+ *    address of the no-alloc entry point's scratch array); calls are
+ *    thread-safe, except that no-alloc calls on one GPU must not overlap.
  *  - `stream` is a hipStream_t (NULL = the default stream).  Work is only
  *    enqueued; results are ready once the stream has reached that point.
  *  - Arguments are validated on the host before anything is enqueued.  On
@@ -219,9 +219,9 @@ int32_t bitlinear_forward_grouped_launches(int32_t count, const bl_projection *p
                                            int64_t m);
 
 /* Several independent BitLinear forwards with the same token count M (for
- * instance the projections of one decoder layer) in one pass: one
- * activation-quantization launch and one contraction launch for all of
- * them.  projs: HOST array of `count` descriptors (1 <= count <= 16);
+ * instance the projections of one decoder layer) in one pass: at most one
+ * activation-quantization launch, one contraction launch and one pass that
+ * adds K parts, for all of them together.  projs: HOST array of `count` descriptors (1 <= count <= 16);
  * results are identical to calling bitlinear_forward on each.  Each
  * descriptor names its weights' layout; an unknown layout is BL_EINVAL, a
  * tiled one with N % 16 != 0 or K % 256 != 0 is BL_ESHAPE. */
