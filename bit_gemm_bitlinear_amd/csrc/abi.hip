@@ -89,7 +89,8 @@ void make_layout(int32_t count, const int64_t* ns, const int64_t* ks, int64_t m,
   // decode: a layer that one workgroup per CU can cover takes the split
   // plan; otherwise each projection is planned on its own
   const bool split =
-      L.decode && plan_decode_split(m, count, ns, ks, L.load_mode, device_cu_count(), L.plan);
+      L.decode &&
+      plan_decode_split(m, count, ns, ks, L.load_mode, device_cu_count(), have_x, L.plan);
   size_t off = 0;
   for (int i = 0; i < count; ++i) {
     L.q_off[i] = L.xs_off[i] = L.qs_off[i] = 0;

@@ -42,17 +42,21 @@ DecodePlan plan_decode(int64_t m, int64_t n, int64_t k, int mode) {
 // the fewest workgroups each projection needs add up to at most `cus` wins.
 // K is never split across workgroups here, so every row's codes fit LDS.
 bool plan_decode_split(int64_t m, int32_t count, const int64_t* ns, const int64_t* ks, int mode,
-                       int cus, DecodePlan* plans) {
+                       int cus, bool have_x, DecodePlan* plans) {
   constexpr int kMaxChunks = 96;  // per lane: at most six rounds of the ring
   constexpr int kSplitPlanMinChunks = 48;
   constexpr int kSmallLayerCuShare = 4;  // "most CUs idle": a quarter of them or fewer busy
   if (mode != 0 || count < 1 || count > kMaxProj) return false;
   int S[kMaxProj];
   int64_t tiles[kMaxProj];
+  bool fuse[kMaxProj];
   for (int i = 0; i < count; ++i) {
     S[i] = (int)((ks[i] + 255) / 256);
     tiles[i] = (ns[i] + 15) / 16;
-    if (m * (S[i] * 256 + 16) > kDecodeLdsA) return false;
+    // rows the kernel quantizes itself may use the split plan's larger code
+    // budget; staged codes are loaded in at most kDecodeLdsA bytes
+    fuse[i] = have_x && m <= kFusedMaxM && ks[i] % 16 == 0 && m * ks[i] <= fused_max_elems(m, true);
+    if (m * (S[i] * 256 + 16) > (fuse[i] ? kDecodeSplitLdsA : kDecodeLdsA)) return false;
   }
   // (wk, tww) pairs; seven tiles per wave with two waves per K range lets
   // the 8B-class layer's longest wave stream 56 chunks on 240 CUs instead of
@@ -78,7 +82,7 @@ bool plan_decode_split(int64_t m, int32_t count, const int64_t* ns, const int64_
           p.kspw = S[i];
           p.ksplit = 1;
           p.ngroups = (int)wgs;
-          p.fused = m <= kFusedMaxM && ks[i] % 16 == 0 && m * ks[i] <= fused_max_elems(m);
+          p.fused = fuse[i];
         }
       }
       if (best < 0) ok = false;
@@ -133,9 +137,12 @@ hipError_t launch_decode(const DecodeArgs& a, int total_wgs, size_t lds_bytes, h
     ins = ins || (P.y && P.acc_out) || (P.x && (P.q || P.x_scale || P.qsum)) || a.epi[i].bias ||
           a.epi[i].res;
   }
-  bool fused = false;
-  for (int i = 0; i < a.count; ++i) fused = fused || a.p[i].x;
-  if (fused && a.m > 1) return launch_decode_rows(a, total_wgs, lds_bytes, s, ins);
+  bool fused = false, big = false;
+  for (int i = 0; i < a.count; ++i) {
+    fused = fused || a.p[i].x;
+    big = big || (a.p[i].x && (int64_t)a.m * a.p[i].k > fused_max_elems(a.m));
+  }
+  if (fused && a.m > 1) return launch_decode_rows(a, total_wgs, lds_bytes, s, ins, big);
   if (fused)  // one token row
     return ins ? launch_decode_as<true, 1>(a, total_wgs, lds_bytes, s)
                : launch_decode_as<false, 1>(a, total_wgs, lds_bytes, s);

@@ -241,15 +241,17 @@ __device__ __forceinline__ void put_group(int8_t* row, int g, v4i v) {
 // codes act_quant.hip prepared, and w_scale.  FR: 0 for staged codes, else
 // the token-row slots of the fused quantizer (1, 4 or 8), one kernel instance
 // per bucket so that one row does not pay for the loops over eight.
-template <int FR>
-constexpr int kXChunks = FR == 0 ? kStageUnits : (FR == 1 ? kFusedChunks1 : kFusedChunksN);
+template <bool SPLIT, int FR>
+constexpr int kXChunks =
+    FR == 0 ? kStageUnits
+            : (FR == 1 ? kFusedChunks1 : (FR == kFusedBigSlots ? kFusedChunksSplit : kFusedChunksN));
 
-template <int FR>
+template <bool SPLIT, int FR>
 __device__ __forceinline__ void load_codes(const DecodeArgs& A, const DecodeProj& P, int sb, int ns,
-                                           v4i (&xin)[kXChunks<FR>], float& ws) {
+                                           v4i (&xin)[kXChunks<SPLIT, FR>], float& ws) {
   constexpr bool FUSED = FR > 0;
   constexpr int NA = 256;
-  constexpr int NX = kXChunks<FR>;
+  constexpr int NX = kXChunks<SPLIT, FR>;
   const int M = A.m;
   const int xt = threadIdx.x & (NA - 1);
   if constexpr (FUSED) {
@@ -291,11 +293,11 @@ __device__ __forceinline__ void load_codes(const DecodeArgs& A, const DecodeProj
 // in the natural layout and the scales to P.q and P.x_scale when those are set.
 template <bool SPLIT, int FR>
 __device__ __forceinline__ void prepare_codes(const DecodeArgs& A, const DecodeProj& P, int ns,
-                                              const v4i (&xin)[kXChunks<FR>], const float ws,
+                                              const v4i (&xin)[kXChunks<SPLIT, FR>], const float ws,
                                               int8_t* __restrict__ lds, Shared& sh, bool inspect) {
   constexpr bool FUSED = FR > 0;
   constexpr int NA = 256;  // activation threads
-  constexpr int NX = kXChunks<FR>;
+  constexpr int NX = kXChunks<SPLIT, FR>;
   const int M = A.m;
   const int xt = threadIdx.x & (NA - 1);
   const int lane = xt & 63, xw = xt >> 6;
@@ -549,9 +551,9 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& A, const DecodePro
     // the weight loads after it, so that the activations do not queue
     // behind the weights.
     if (!streamer) {
-      v4i xin[kXChunks<FR>];
+      v4i xin[kXChunks<true, FR>];
       float ws;
-      load_codes<FR>(A, P, sb, ns, xin, ws);
+      load_codes<true, FR>(A, P, sb, ns, xin, ws);
       __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");  // counters are zero
@@ -609,9 +611,9 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& A, const DecodePro
       __builtin_amdgcn_sched_barrier(0);
     };
     {
-      v4i xin[kXChunks<FR>];
+      v4i xin[kXChunks<false, FR>];
       float ws;
-      load_codes<FR>(A, P, sb, ns, xin, ws);
+      load_codes<false, FR>(A, P, sb, ns, xin, ws);
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (EARLY) fill();
       prepare_codes<false, FR>(A, P, ns, xin, ws, lds, sh, inspect);
@@ -827,6 +829,8 @@ hipError_t launch_decode_as(const DecodeArgs& a, int total_wgs, size_t lds_bytes
     if (split) {
       e = allow_lds<&decode_kernel<0, true, false, EPI, FR>>(lds_bytes);
       if (e == hipSuccess) decode_kernel<0, true, false, EPI, FR><<<grid, 512, lds_bytes, s>>>(a);
+    } else if constexpr (FR == kFusedBigSlots) {
+      return hipErrorInvalidValue;  // not reached: only split plans fuse that many codes
     } else if (a.m > 1) {
       e = allow_lds<&decode_kernel<0, false, true, EPI, FR>>(lds_bytes);
       if (e == hipSuccess) decode_kernel<0, false, true, EPI, FR><<<grid, 256, lds_bytes, s>>>(a);

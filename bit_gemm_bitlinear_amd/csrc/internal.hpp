@@ -79,9 +79,20 @@ hipError_t launch_act_quant_public(const uint16_t* x, int64_t m, int64_t k, int8
 constexpr int kFusedMaxM = 4;
 constexpr int kFusedChunks1 = 8;   // 16-byte chunks of x per thread, one token row
 constexpr int kFusedChunksN = 24;  // the same, 2 to 4 token rows
-inline int64_t fused_max_elems(int64_t m) {
-  return (int64_t)(m == 1 ? kFusedChunks1 : kFusedChunksN) * 8 * 256;
+// 2 to 4 rows whose codes exceed kFusedChunksN per thread, in the split
+// shape only (its activation waves hold no weight ring): 4 rows of 14336, the
+// 8B-class layer's down projection at M = 4.  A kernel instance of its own
+// (kFusedBigSlots row slots), so that the other fused launches keep the
+// shorter loops.
+constexpr int kFusedChunksSplit = 28;
+constexpr int kFusedBigSlots = 5;
+inline int64_t fused_max_elems(int64_t m, bool split = false) {
+  return (int64_t)(m == 1 ? kFusedChunks1 : (split ? kFusedChunksSplit : kFusedChunksN)) * 8 * 256;
 }
+// Code rows of a workgroup in the layer-level split plan (one workgroup per
+// CU, so more LDS than the per-projection plans' kDecodeLdsA): 4 rows of
+// 14336 codes fit.
+constexpr int kDecodeSplitLdsA = 60 * 1024;
 // Row slots of the kernel instance that fuses the quantization of m rows.
 inline int fused_rows(int64_t m) { return m == 1 ? 1 : 4; }
 
@@ -139,14 +150,16 @@ struct DecodePlan {
   bool fused;
 };
 DecodePlan plan_decode(int64_t m, int64_t n, int64_t k, int mode);
+// have_x: the activations are bf16, so rows that fit may be quantized in the
+// kernel (and may then use the larger LDS budget of the split plan).
 bool plan_decode_split(int64_t m, int32_t count, const int64_t* ns, const int64_t* ks, int mode,
-                       int cus, DecodePlan* plans);
+                       int cus, bool have_x, DecodePlan* plans);
 int device_cu_count();  // compute units of the current device (cached per device)
 size_t decode_lds_bytes(int64_t m, int lds_row);
 hipError_t launch_decode(const DecodeArgs& a, int total_wgs, size_t lds_bytes, hipStream_t s);
 // The instances that fuse the quantization of 2 to 4 token rows.
 hipError_t launch_decode_rows(const DecodeArgs& a, int total_wgs, size_t lds_bytes, hipStream_t s,
-                              bool epi);
+                              bool epi, bool big);
 
 // ---- prefill contraction (prefill.hip) ----
 constexpr int kPrefillBM = 128;  // token rows per tile (register-staged variant; main variant's largest)

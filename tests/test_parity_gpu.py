@@ -813,6 +813,27 @@ def test_mid_m_forward_acc_parity(bl, m, n, k):
         assert np.array_equal(acc.cpu().numpy(), ref)
 
 
+@pytest.mark.parametrize("m", [2, 3, 4, 5])
+def test_layer_8b_few_rows_parity(bl, m):
+    """The 8B-class layer at 2-5 token rows.  Up to 4 rows take the
+    layer-level split plan with every projection quantized inside the
+    kernel, the down projection's 4 x 14336 codes included (the split
+    shape's larger code budget): one launch.  At 5 rows the codes are
+    staged by the activation kernel: two launches.  Codes, scales, code sums,
+    accumulators and outputs against the oracle."""
+    wl = wls.WORKLOADS["layer_8b"]
+    entries = packed_workload(bl, wl)
+    shapes = [(p.n, p.k) for p in wl.projections]
+    assert bl.forward_grouped_launches(m, shapes) == (1 if m <= 4 else 2)
+    xs = [wls.activations(wl, pi, m) for pi in range(len(wl.projections))]
+    ys, inss, status = bl.forward_grouped_inspect([dev_bf16(x) for x in xs],
+                                                  [e[4] for e in entries], [e[1] for e in entries])
+    assert int(status.item()) == 0
+    for pi, (x, y, ins, e) in enumerate(zip(xs, ys, inss, entries)):
+        check_inspection(f"layer_8b {wl.projections[pi].name} M={m}", x, y, ins, e[2], e[3],
+                         oracle.forward(x, e[2], e[3]))
+
+
 @pytest.mark.parametrize("name,m", [(n, m) for n in ("decode_3b", "layer_8b")
                                     for m in (17, 32, 64, 100, 128)])
 def test_mid_m_workload_parity(bl, name, m):
