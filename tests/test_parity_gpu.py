@@ -826,12 +826,14 @@ def test_layer_8b_few_rows_parity(bl, m):
     shapes = [(p.n, p.k) for p in wl.projections]
     assert bl.forward_grouped_launches(m, shapes) == (1 if m <= 4 else 2)
     xs = [wls.activations(wl, pi, m) for pi in range(len(wl.projections))]
-    ys, inss, status = bl.forward_grouped_inspect([dev_bf16(x) for x in xs],
-                                                  [e[4] for e in entries], [e[1] for e in entries])
+    dxs = [dev_bf16(x) for x in xs]
+    ys, inss, status = bl.forward_grouped_inspect(dxs, [e[4] for e in entries], [e[1] for e in entries])
     assert int(status.item()) == 0
-    for pi, (x, y, ins, e) in enumerate(zip(xs, ys, inss, entries)):
+    plain = bl.forward_grouped(dxs, [e[4] for e in entries], [e[1] for e in entries])
+    for pi, (x, y, yp, ins, e) in enumerate(zip(xs, ys, plain, inss, entries)):
         check_inspection(f"layer_8b {wl.projections[pi].name} M={m}", x, y, ins, e[2], e[3],
                          oracle.forward(x, e[2], e[3]))
+        assert torch.equal(yp.view(torch.int16), y.view(torch.int16)), "plain call differs"
 
 
 @pytest.mark.parametrize("name,m", [(n, m) for n in ("decode_3b", "layer_8b")
