@@ -707,11 +707,13 @@ def test_forward_bias_residual_parity(bl, m, n, k):
 
 
 @pytest.mark.parametrize("name,m", [("decode_1b_m1", 1), ("decode_3b", 16),
-                                    ("prefill_2b_m2048", 2048)])
+                                    ("prefill_2b_m2048", 2048), ("layer_8b", 4),
+                                    ("decode_3b", 4)])
 def test_grouped_bias_residual_workload(bl, name, m):
     """Bias and residual on every projection of a workload in one grouped
-    call (the decode kernel's split and ring shapes, the GEMM with its
-    narrow tail)."""
+    call (the decode kernel's split and ring shapes with staged and fused
+    codes, the 4-row split instance with the larger code budget, the GEMM
+    with its narrow tail)."""
     wl = wls.WORKLOADS[name]
     entries = packed_workload(bl, wl)
     xs = [wls.activations(wl, pi, m) for pi in range(len(wl.projections))]
