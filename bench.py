@@ -410,6 +410,32 @@ def _time_native(torch, calls, copies, min_seconds):
 # CPU baseline: the oracle as it stands, on the host cores
 
 
+def latent_context(torch, bl, dev, min_seconds=0.1):
+    """Context for on-the-fly ternarization: bitlinear_forward_latent (exact
+    absmean, ternarization and packing, then the forward) against the
+    forward on weights packed once, one projection at M = 1, the fp32
+    weights rotated over copies spanning >= 1 GiB."""
+    out = []
+    g = torch.Generator(device="cpu").manual_seed(5)
+    for n, k in ((4096, 4096), (14336, 4096)):
+        w0 = (torch.randn(n, k, generator=g) * 0.02).to(dev)
+        copies = max(1, int(math.ceil((1 << 30) / (4 * n * k))))
+        ws = [w0] + [w0.clone() for _ in range(copies - 1)]
+        x = torch.randn(1, k, generator=g).to(torch.bfloat16).to(dev)
+        y = torch.empty(1, n, dtype=torch.bfloat16, device=dev)
+        packs = [bl.pack_weights(w) for w in ws]
+        lat = [lambda w=w: bl.forward_latent(x, w, out=y) for w in ws]
+        pk = [lambda p=p: bl.forward(x, p[0], p[1], out=y) for p in packs]
+        t_lat = float(np.median(time_config(torch, lat, 20, 20, min_seconds)[0]))
+        t_pk = float(np.median(time_config(torch, pk, 20, 20, min_seconds)[0]))
+        out.append({"n": n, "k": k, "m": 1, "rotated_copies": copies,
+                    "latent_us": t_lat * 1e6, "packed_us": t_pk * 1e6,
+                    "latent_GBs_of_fp32_weights": 4 * n * k / t_lat / 1e9})
+        del ws, packs, lat, pk
+        torch.cuda.empty_cache()
+    return out
+
+
 def _threads_info():
     try:
         from threadpoolctl import threadpool_info
@@ -782,6 +808,10 @@ def main():
                                    "(torch.mm, weights [N, K] as nn.Linear stores them and "
                                    "[K, N]; the faster is reported), rotated like the ternary "
                                    "steps; compare ms_per_step with the configs array")
+        ctx["latent_forward"] = latent_context(torch, bl, dev)
+        ctx["latent_forward_note"] = ("bitlinear_forward_latent (exact absmean, packing, then the "
+                                      "forward, from fp32 weights) against the forward on weights "
+                                      "packed once; one projection, M = 1")
         # token counts inside the decode path (up to 16 rows)
         ctx["decode_m"] = []
         for n in ("decode_3b", "layer_8b"):
