@@ -91,11 +91,22 @@ void make_layout(int32_t count, const int64_t* ns, const int64_t* ks, int64_t m,
   const bool split =
       L.decode &&
       plan_decode_split(m, count, ns, ks, L.load_mode, device_cu_count(), have_x, L.plan);
+  // per-projection plans of staged codes (5-16 rows) take the larger chunk
+  // target when the layer then still has a workgroup for every CU
+  int target = kDecodeWaveChunks;
+  if (L.decode && !split && m > kFusedMaxM) {
+    int64_t wgs = 0;
+    for (int i = 0; i < count; ++i) {
+      const DecodePlan q = plan_decode(m, ns[i], ks[i], L.load_mode, kDecodeWaveChunksStaged);
+      wgs += (int64_t)q.ngroups * q.ksplit;
+    }
+    if (wgs >= device_cu_count()) target = kDecodeWaveChunksStaged;
+  }
   size_t off = 0;
   for (int i = 0; i < count; ++i) {
     L.q_off[i] = L.xs_off[i] = L.qs_off[i] = 0;
     if (L.decode) {
-      if (!split) L.plan[i] = plan_decode(m, ns[i], ks[i], L.load_mode);
+      if (!split) L.plan[i] = plan_decode(m, ns[i], ks[i], L.load_mode, target);
       L.plan[i].fused = L.plan[i].fused && have_x;
       if (L.plan[i].fused) continue;
     }
@@ -143,6 +154,7 @@ void make_layout(int32_t count, const int64_t* ns, const int64_t* ks, int64_t m,
   }
   // the size does not depend on which plan the device's CU count picks:
   // room for the per-projection plans' split-K partials is always counted
+  // (at the default chunk target, whose plans have the most row groups)
   size_t ring = L.zero_off;
   for (int i = 0; L.decode && i < count; ++i) {
     const DecodePlan p = plan_decode(m, ns[i], ks[i], L.load_mode);

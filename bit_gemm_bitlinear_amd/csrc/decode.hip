@@ -9,11 +9,11 @@ namespace bl {
 // budget for staged codes (beyond it WGs split K and add partial sums in
 // L2).  Waves of a WG split K as well when its range is long (1, 2 or 4
 // ways, partial sums meet in LDS); otherwise each wave owns its own row
-// tiles.  Tiles per wave bring a wave's stream to about kWaveChunks 16-byte
-// chunks, so a WG moves about 64 KB.  Small M*K with 16-aligned rows takes
+// tiles.  Tiles per wave bring a wave's stream to about `target` 16-byte
+// chunks (a WG moves about 64 KB at the default target).  Small M*K with 16-aligned rows takes
 // the fused path (the WG quantizes the bf16 rows itself), which never
 // splits K across WGs.
-DecodePlan plan_decode(int64_t m, int64_t n, int64_t k, int mode) {
+DecodePlan plan_decode(int64_t m, int64_t n, int64_t k, int mode, int target) {
   DecodePlan p;
   const int S = (int)((k + 255) / 256);
   int cap = (int)((kDecodeLdsA / m - 16) / 256);
@@ -21,11 +21,11 @@ DecodePlan plan_decode(int64_t m, int64_t n, int64_t k, int mode) {
   if (cap > 4 * kWaveMaxChunks) cap = 4 * kWaveMaxChunks;
   p.ksplit = (S + cap - 1) / cap;
   p.kspw = (S + p.ksplit - 1) / p.ksplit;
-  p.wk = p.kspw <= kWaveChunks ? 1 : (p.kspw <= 2 * kWaveMaxChunks ? 2 : 4);
-  if (p.wk == 2 && (p.kspw + 1) / 2 > kWaveChunks && p.kspw > 2 * kWaveChunks) p.wk = 4;
+  p.wk = p.kspw <= target ? 1 : (p.kspw <= 2 * kWaveMaxChunks ? 2 : 4);
+  if (p.wk == 2 && (p.kspw + 1) / 2 > target && p.kspw > 2 * target) p.wk = 4;
   const int nsw = (p.kspw + p.wk - 1) / p.wk;  // <= kWaveMaxChunks
   int tww = 1;
-  while (tww < kDecodeMaxTww && 2 * tww * nsw <= kWaveChunks) tww *= 2;  // 1, 2 or 4
+  while (tww < kDecodeMaxTww && 2 * tww * nsw <= target) tww *= 2;  // 1, 2 or 4
   const int rows_wg = (4 / p.wk) * tww * 16;
   p.tww = tww;
   p.ngroups = (int)((n + rows_wg - 1) / rows_wg);

@@ -48,8 +48,9 @@ namespace {
 static_assert(BL_DECODE_WINDOW % 4 == 0, "ring slots hold whole tile rounds");
 
 constexpr int kWindow = BL_DECODE_WINDOW;  // 16-byte weight chunks in flight per lane
-constexpr int kWaveChunks = 24;            // target chunks streamed per wave (ring shape)
-constexpr int kWaveMaxChunks = 24;         // most chunks one wave streams (ring shape)
+constexpr int kWaveChunks = kDecodeWaveChunks;  // target chunks streamed per wave (ring shape)
+constexpr int kWaveMaxChunks = 24;              // most chunks per wave at that target
+constexpr int kWaveMaxChunksStaged = kDecodeWaveChunksStaged;  // staged-code instances
 constexpr int kSplitRing = 16;             // load ring per lane of the split shape
 constexpr int kStageUnits = kDecodeLdsA / 16 / 256;  // 16-byte code units per activation thread
 
@@ -636,7 +637,13 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& A, const DecodePro
     };
     using Yes = std::true_type;
     using No = std::false_type;
+    // three rounds at most for the fused-quantization instances, four for
+    // the staged-code ones (the larger chunk target of big layers); the
+    // fused instances keep their shorter code (a loop over rounds instead
+    // of this nesting made the 2-4-row instances slower: 3B-class layer at
+    // M = 4 19.4 against 13.1 us)
     static_assert(kWaveMaxChunks <= 3 * W, "at most three rounds");
+    static_assert(kWaveMaxChunksStaged <= 4 * W, "at most four rounds");
     if (NI <= W) {
       round(0, No{});
     } else {
@@ -645,7 +652,16 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& A, const DecodePro
         round(W, No{});
       } else {
         round(W, Yes{});
-        round(2 * W, No{});
+        if constexpr (FR == 0) {
+          if (NI <= 3 * W) {
+            round(2 * W, No{});
+          } else {
+            round(2 * W, Yes{});
+            round(3 * W, No{});
+          }
+        } else {
+          round(2 * W, No{});
+        }
       }
     }
   }

@@ -15,6 +15,15 @@ int current_device_index();  // hipGetDevice, clamped to [0, kMaxDevices)
 // Decode path (M <= 16) limits.
 constexpr int kDecodeMaxM = 16;
 constexpr int kDecodeMaxTww = 4;      // 16-row tiles per wave (per-projection plans)
+// 16-byte weight chunks a streaming wave targets in the per-projection
+// plans.  Layers whose staged-code plans (5-16 token rows) keep at least one
+// workgroup per CU at the larger target take it: each workgroup then streams
+// more weight bytes per staged code byte.  Measured on the 8B-class layer:
+// 21.9 -> 19.2 us at M = 5, 22.4 -> 19.5 us at M = 8, 30.3 -> 27.9 us at
+// M = 16.  (The 3B-class layer at M = 16 would drop to 156 workgroups on 256
+// CUs at 48 chunks, and took 22.7 against 19.3 us.)
+constexpr int kDecodeWaveChunks = 24;
+constexpr int kDecodeWaveChunksStaged = 32;
 constexpr int kDecodeRedTww = 7;      // the same, any plan (sizes the in-LDS partial sums)
 // 52 KB: 16 token rows of 3072 codes (plus row padding) fit, so the 3B-class
 // layer's 3072-wide projections need no K split across workgroups at M = 16
@@ -149,7 +158,8 @@ struct DecodePlan {
   int32_t wk, tww, kspw, ksplit, ngroups;
   bool fused;
 };
-DecodePlan plan_decode(int64_t m, int64_t n, int64_t k, int mode);
+DecodePlan plan_decode(int64_t m, int64_t n, int64_t k, int mode,
+                       int target = kDecodeWaveChunks);
 // have_x: the activations are bf16, so rows that fit may be quantized in the
 // kernel (and may then use the larger LDS budget of the split plan).
 bool plan_decode_split(int64_t m, int32_t count, const int64_t* ns, const int64_t* ks, int mode,

@@ -815,14 +815,16 @@ def test_mid_m_forward_acc_parity(bl, m, n, k):
         assert np.array_equal(acc.cpu().numpy(), ref)
 
 
-@pytest.mark.parametrize("m", [2, 3, 4, 5])
+@pytest.mark.parametrize("m", [2, 3, 4, 5, 8, 16])
 def test_layer_8b_few_rows_parity(bl, m):
-    """The 8B-class layer at 2-5 token rows.  Up to 4 rows take the
+    """The 8B-class layer at 2-16 token rows.  Up to 4 rows take the
     layer-level split plan with every projection quantized inside the
     kernel, the down projection's 4 x 14336 codes included (the split
-    shape's larger code budget): one launch.  At 5 rows the codes are
-    staged by the activation kernel: two launches.  Codes, scales, code sums,
-    accumulators and outputs against the oracle."""
+    shape's larger code budget): one launch.  From 5 rows the codes are
+    staged by the activation kernel (two launches), and the per-projection
+    plans take the larger chunk target, so waves stream 28-32 chunks in
+    four ring rounds (K split across workgroups for the down projection).
+    Codes, scales, code sums, accumulators and outputs against the oracle."""
     wl = wls.WORKLOADS["layer_8b"]
     entries = packed_workload(bl, wl)
     shapes = [(p.n, p.k) for p in wl.projections]
