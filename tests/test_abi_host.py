@@ -493,6 +493,12 @@ int main() {
   { const int64_t sl[1] = {128}, t[1] = {4};
     bl::plan_ksplit(1, sl, t, 512, 16, 16, ks, kw);
     printf("%d %d ", ks[0], kw[0]); }
+  { const int64_t sl[7] = {24, 24, 24, 24, 24, 24, 72}, t[7] = {48, 48, 48, 48, 144, 144, 48};  // 3B, M = 512
+    bl::plan_ksplit(7, sl, t, 512, 16, 16, ks, kw);
+    printf("%d %d ", ks[6], kw[6]); }
+  { const int64_t sl[7] = {24, 24, 24, 24, 24, 24, 72}, t[7] = {24, 24, 24, 24, 72, 72, 24};  // 3B, M = 256
+    bl::plan_ksplit(7, sl, t, 512, 16, 16, ks, kw);
+    printf("%d %d ", ks[6], kw[6]); }
   // every split covers K exactly with no empty part, within the bounds
   std::mt19937 g(3);
   int bad = 0;
@@ -514,17 +520,20 @@ int main() {
 
 
 def test_prefill_ksplit_plan(tmp_path):
-    """The K-split plan leaves the 2B FFN whole, splits the 8B-class layer's
-    down projection at M = 512 (112 slabs) into 3 parts of 38 and a lone
-    128-slab projection into 8 of 16, and every split covers K with no empty
-    part and at most 16 parts."""
+    """The K-split plan leaves the 2B FFN whole.  Launches of more than one
+    round of workgroups take parts of up to twice the average load: the
+    8B-class layer's down projection at M = 512 (112 slabs) in 2 parts of
+    56, the 3B-class layer's (72 slabs) in 2 of 36.  Launches of one round
+    take parts of about the average: a lone 128-slab projection in 8 of 16,
+    the 3B-class down projection at M = 256 in 5 of 15.  Every split covers K
+    with no empty part and at most 16 parts."""
     src = tmp_path / "ksplit_check.cpp"
     exe = tmp_path / "ksplit_check"
     src.write_text(KSPLIT_SRC)
     subprocess.run(["g++", "-O2", "-std=c++17", "-I", CSRC, str(src), "-o", str(exe)], check=True)
     out = list(map(int, subprocess.run([str(exe)], capture_output=True, text=True,
                                        check=True).stdout.split()))
-    assert out == [1, 1, 1, 1, 3, 38, 8, 16, 0]
+    assert out == [1, 1, 1, 1, 2, 56, 8, 16, 2, 36, 5, 15, 0]
 
 
 def test_prefill_plan(tmp_path):
