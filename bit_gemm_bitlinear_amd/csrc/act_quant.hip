@@ -311,15 +311,38 @@ __device__ __forceinline__ void quant_row_internal_fast(const uint16_t* __restri
 // into the internal order (dword a, byte b = code 4b + a).
 constexpr int kRowsNBW = 4;  // groups per lane
 
-// The job that block `r` belongs to.  The jobs' first blocks are one
-// contiguous array at fixed kernel-argument offsets, loaded at once, so the
-// lookup costs one round trip to the argument segment rather than one per
-// job (3B-class layer at M = 16: the quantization kernel 5.3 -> 4.6 us).
-__device__ __forceinline__ int job_of(const ActQuantArgs& a, int r) {
-  int ji = 0;
+// The job of block b in one round trip to the kernel-argument segment: lane
+// j (of each 16) reads job j's first block (row_begin) and descriptor, a
+// ballot picks the job that holds b, and its words are broadcast with
+// readlane (`first`: the job's row_begin entry).  (Looking up
+// the job's index first and then its descriptor is two dependent round trips
+// before the first activation load: 3B-class layer at M = 16 18.93 -> 18.44
+// us per step, 8B-class layer at M = 8 19.5 -> 18.9 us.  A single job needs
+// no lookup and reads its descriptor directly.)
+static_assert(sizeof(ActQuantJob) % 16 == 0, "a job descriptor is read as 16-byte words");
+__device__ __forceinline__ ActQuantJob select_job(int count, int b, int* first = nullptr) {
+  const char* kp = (const char*)__builtin_amdgcn_kernarg_segment_ptr();
+  const ActQuantArgs* ka = reinterpret_cast<const ActQuantArgs*>(kp);
+  const int j = threadIdx.x & 15;
+  constexpr int kWords = sizeof(ActQuantJob) / 16;
+  v4i words[kWords];
+  const v4i* src = reinterpret_cast<const v4i*>(&ka->j[j]);
 #pragma unroll
-  for (int i = 1; i < kMaxProj; ++i) ji += (i < a.count && r >= a.row_begin[i]);
-  return ji;
+  for (int i = 0; i < kWords; ++i) words[i] = src[i];
+  const int beg = ka->row_begin[j];
+  const int nxt = ka->row_begin[j < kMaxProj - 1 ? j + 1 : j];
+  __builtin_amdgcn_sched_barrier(0);
+  const int end = (j + 1 < count) ? nxt : 0x7FFFFFFF;
+  const unsigned long long hit = __ballot(j < count && b >= beg && b < end);
+  const int pi = __builtin_ctzll(hit) & 15;
+  ActQuantJob J;
+  int32_t* dst = reinterpret_cast<int32_t*>(&J);
+#pragma unroll
+  for (int i = 0; i < kWords; ++i)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) dst[4 * i + c] = __builtin_amdgcn_readlane(words[i][c], pi);
+  if (first) *first = __builtin_amdgcn_readlane(beg, pi);
+  return J;
 }
 
 // INS: some job has inspection outputs (a separate instance, so that the
@@ -337,12 +360,12 @@ __global__ __launch_bounds__(kThreads) void act_quant_rows_kernel(const ActQuant
     return;
   }
   // a.row_begin holds each job's first block here
-  const int ji = job_of(a, b);
-  const ActQuantJob& J = a.j[ji];
+  int first = 0;
+  const ActQuantJob J = a.count > 1 ? select_job(a.count, b, &first) : a.j[0];
   const int lw = J.wpr == 1 ? 0 : (J.wpr == 2 ? 1 : 2);  // log2 of the waves per row
   const int wave = (int)(threadIdx.x >> 6), lane = (int)(threadIdx.x & 63);
   const int sub = wave & ((1 << lw) - 1);  // this wave's part of the row
-  const int m = ((b - a.row_begin[ji]) << (2 - lw)) + (wave >> lw);
+  const int m = ((b - first) << (2 - lw)) + (wave >> lw);
   if (lw == 0 && m >= J.m_pad) return;  // past the job's rows (no barrier follows)
   const bool data = m < J.m;            // else a padding row (or past the rows): zero codes
   const int k = J.k, ngroups = J.ldq / 16;
@@ -429,38 +452,6 @@ __global__ __launch_bounds__(kThreads) void act_quant_rows_kernel(const ActQuant
     if (INS && J.ins_qs) J.ins_qs[m] = sum;
     if (INS && J.ins_xs) J.ins_xs[m] = s;
   }
-}
-
-// The job of block b in one round trip to the kernel-argument segment: lane
-// j (of each 16) reads job j's first block and descriptor, a ballot picks the
-// job that holds b, and its words are broadcast with readlane.  (Looking up
-// the job's index first and then its descriptor is two dependent round trips
-// before the first activation load: 3B-class layer at M = 16 18.93 -> 18.44
-// us per step, 8B-class layer at M = 8 19.5 -> 18.9 us.  A single job needs
-// no lookup and reads its descriptor directly.)
-static_assert(sizeof(ActQuantJob) % 16 == 0, "a job descriptor is read as 16-byte words");
-__device__ __forceinline__ ActQuantJob select_job(int count, int b) {
-  const char* kp = (const char*)__builtin_amdgcn_kernarg_segment_ptr();
-  const ActQuantArgs* ka = reinterpret_cast<const ActQuantArgs*>(kp);
-  const int j = threadIdx.x & 15;
-  constexpr int kWords = sizeof(ActQuantJob) / 16;
-  v4i words[kWords];
-  const v4i* src = reinterpret_cast<const v4i*>(&ka->j[j]);
-#pragma unroll
-  for (int i = 0; i < kWords; ++i) words[i] = src[i];
-  const int beg = ka->row_begin[j];
-  const int nxt = ka->row_begin[j < kMaxProj - 1 ? j + 1 : j];
-  __builtin_amdgcn_sched_barrier(0);
-  const int end = (j + 1 < count) ? nxt : 0x7FFFFFFF;
-  const unsigned long long hit = __ballot(j < count && b >= beg && b < end);
-  const int pi = __builtin_ctzll(hit) & 15;
-  ActQuantJob J;
-  int32_t* dst = reinterpret_cast<int32_t*>(&J);
-#pragma unroll
-  for (int i = 0; i < kWords; ++i)
-#pragma unroll
-    for (int c = 0; c < 4; ++c) dst[4 * i + c] = __builtin_amdgcn_readlane(words[i][c], pi);
-  return J;
 }
 
 __global__ __launch_bounds__(kThreads) void act_quant_internal_kernel(const ActQuantArgs a) {
